@@ -1,0 +1,305 @@
+/*
+ * moe_oracle.c -- plain fp64 CPU oracle of one sparse MoE FFN layer forward.
+ * TEST INFRASTRUCTURE ONLY (tests, smoke check, CPU baseline of the bench).
+ * The definitions and their sources are listed in moe_oracle.h.
+ *
+ * Written for a reader to check by eye against the definitions: one loop per
+ * sum, ascending index order, double accumulation, no blocking or fusion.
+ * OpenMP only splits independent tokens (or rows) across threads; no sum is
+ * split or reordered, so results do not depend on the thread count.
+ *
+ * Build: gcc -O2 -std=c99 -ffp-contract=off -fopenmp -shared -fPIC
+ */
+#include "moe_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* exact widening of one stored element to double */
+static double widen(const void* base, int32_t dtype, size_t i) {
+  if (dtype == ORC_F32) return (double)((const float*)base)[i];
+  uint32_t bits = ((uint32_t)((const uint16_t*)base)[i]) << 16;
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return (double)f;
+}
+
+static size_t elem_size(int32_t dtype) { return dtype == ORC_F32 ? 4u : 2u; }
+
+static int check_layer(const orc_layer_t* L) {
+  if (!L || L->H < 1 || L->F < 1 || L->E < 1 || L->k < 1 || L->k > L->E) return -1;
+  if (L->dtype != ORC_F32 && L->dtype != ORC_BF16) return -1;
+  if (!L->router_w || !L->experts) return -1;
+  if (L->stride < 3ull * (uint64_t)L->H * (uint64_t)L->F * elem_size(L->dtype)) return -1;
+  return 0;
+}
+
+/* Round a double to the nearest bfloat16 value (8 significant bits), ties to
+ * even: v = m * 2^ex with 0.5 <= |m| < 1, so m * 2^8 carries exactly the kept
+ * bits in its integer part and rint() rounds the rest half-to-even. */
+double orc_bf16_round(double v) {
+  if (v == 0.0 || !isfinite(v)) return v;
+  int ex;
+  double m = frexp(v, &ex);
+  return ldexp(rint(ldexp(m, 8)), ex - 8);
+}
+
+/* O1: L[t][e] = sum_h x[t][h] * Wr[h][e] (+ b[e]) */
+int orc_logits(const orc_layer_t* L, const void* x, int32_t T, double* logits) {
+  if (check_layer(L) || !x || T < 0 || !logits) return -1;
+  const int32_t H = L->H, E = L->E;
+#pragma omp parallel for schedule(static)
+  for (int32_t t = 0; t < T; ++t) {
+    for (int32_t e = 0; e < E; ++e) {
+      double s = 0.0;
+      for (int32_t h = 0; h < H; ++h)
+        s += widen(x, L->dtype, (size_t)t * H + h) * widen(L->router_w, L->dtype, (size_t)h * E + e);
+      if (L->router_b) s += (double)L->router_b[e];
+      logits[(size_t)t * E + e] = s;
+    }
+  }
+  return 0;
+}
+
+/* O2 + O3 for one token: k rounds of "largest unpicked logit", scanning e
+ * upwards and replacing only on strictly greater, so equal logits go to the
+ * lower index; then w_j = exp(L_j - L_0) / sum_i exp(L_i - L_0). */
+static int topk_one(int32_t E, int32_t k, const double* Lt, int32_t* idx, double* w) {
+  for (int32_t e = 0; e < E; ++e)
+    if (!isfinite(Lt[e])) return -2;
+  for (int32_t j = 0; j < k; ++j) {
+    int32_t best = -1;
+    for (int32_t e = 0; e < E; ++e) {
+      int taken = 0;
+      for (int32_t i = 0; i < j; ++i)
+        if (idx[i] == e) taken = 1;
+      if (taken) continue;
+      if (best < 0 || Lt[e] > Lt[best]) best = e;
+    }
+    idx[j] = best;
+  }
+  double m = Lt[idx[0]];
+  double z = 0.0;
+  for (int32_t j = 0; j < k; ++j) z += exp(Lt[idx[j]] - m);
+  for (int32_t j = 0; j < k; ++j) w[j] = exp(Lt[idx[j]] - m) / z;
+  return 0;
+}
+
+int orc_topk_softmax(int32_t T, int32_t E, int32_t k, const double* logits, int32_t* idx,
+                     double* w) {
+  if (T < 0 || E < 1 || k < 1 || k > E || !logits || !idx || !w) return -1;
+  int rc = 0;
+  for (int32_t t = 0; t < T; ++t) {
+    int r = topk_one(E, k, logits + (size_t)t * E, idx + (size_t)t * k, w + (size_t)t * k);
+    if (r) rc = r;
+  }
+  return rc;
+}
+
+/* O4: counting sort of the T*k (token, slot) pairs by expert.  counts[e];
+ * offsets = exclusive prefix sum of counts (E+1 entries); then pairs are
+ * placed in order of ascending token, then ascending slot, each at the next
+ * free position of its expert: perm[p] = t*k + j and inv[t*k + j] = p. */
+int orc_dispatch(int32_t T, int32_t E, int32_t k, const int32_t* idx, int32_t* counts,
+                 int32_t* offsets, int32_t* perm, int32_t* inv) {
+  if (T < 0 || E < 1 || k < 1 || !idx || !counts || !offsets || !perm || !inv) return -1;
+  for (int32_t e = 0; e < E; ++e) counts[e] = 0;
+  for (int32_t s = 0; s < T * k; ++s) {
+    if (idx[s] < 0 || idx[s] >= E) return -1;
+    counts[idx[s]] += 1;
+  }
+  offsets[0] = 0;
+  for (int32_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int32_t* next = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+  if (!next) return -1;
+  for (int32_t e = 0; e < E; ++e) next[e] = offsets[e];
+  for (int32_t t = 0; t < T; ++t) {
+    for (int32_t j = 0; j < k; ++j) {
+      int32_t s = t * k + j;
+      int32_t p = next[idx[s]]++;
+      perm[p] = s;
+      inv[s] = p;
+    }
+  }
+  free(next);
+  return 0;
+}
+
+/* O5 for one row: g_f = sum_h x_h Wg[f][h], u_f = sum_h x_h Wu[f][h],
+ * a_f = g_f / (1 + exp(-g_f)) * u_f (bf16-rounded in bf16 layers),
+ * y_h = sum_f a_f Wd[h][f]. */
+int orc_expert_ffn(const orc_layer_t* L, int32_t e, const double* xrow, double* yrow) {
+  if (check_layer(L) || e < 0 || e >= L->E || !xrow || !yrow) return -1;
+  const int32_t H = L->H, F = L->F;
+  const size_t es = elem_size(L->dtype);
+  const unsigned char* blk = (const unsigned char*)L->experts + (size_t)e * L->stride;
+  const void* Wg = blk;
+  const void* Wu = blk + (size_t)F * H * es;
+  const void* Wd = blk + 2 * (size_t)F * H * es;
+  double* a = (double*)malloc(sizeof(double) * (size_t)F);
+  if (!a) return -1;
+  for (int32_t f = 0; f < F; ++f) {
+    double g = 0.0, u = 0.0;
+    for (int32_t h = 0; h < H; ++h) g += xrow[h] * widen(Wg, L->dtype, (size_t)f * H + h);
+    for (int32_t h = 0; h < H; ++h) u += xrow[h] * widen(Wu, L->dtype, (size_t)f * H + h);
+    double act = g / (1.0 + exp(-g)) * u;
+    a[f] = (L->dtype == ORC_BF16) ? orc_bf16_round(act) : act;
+  }
+  for (int32_t h = 0; h < H; ++h) {
+    double s = 0.0;
+    for (int32_t f = 0; f < F; ++f) s += a[f] * widen(Wd, L->dtype, (size_t)h * F + f);
+    yrow[h] = s;
+  }
+  free(a);
+  return 0;
+}
+
+/* O5 over the dispatched rows: row p of expert e (offsets[e] <= p <
+ * offsets[e+1]) is token perm[p] / k through expert e. */
+int orc_expert_rows(const orc_layer_t* L, const void* x, int32_t T, const int32_t* offsets,
+                    const int32_t* perm, double* yp) {
+  if (check_layer(L) || !x || T < 0 || !offsets || !perm || !yp) return -1;
+  const int32_t H = L->H, E = L->E, k = L->k;
+  int rc = 0;
+  for (int32_t e = 0; e < E; ++e) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t p = offsets[e]; p < offsets[e + 1]; ++p) {
+      int32_t t = perm[p] / k;
+      double* xr = (double*)malloc(sizeof(double) * (size_t)H);
+      if (!xr) { rc = -1; continue; }
+      for (int32_t h = 0; h < H; ++h) xr[h] = widen(x, L->dtype, (size_t)t * H + h);
+      if (orc_expert_ffn(L, e, xr, yp + (size_t)p * H)) rc = -1;
+      free(xr);
+    }
+  }
+  return rc;
+}
+
+/* O6: y[t][h] = sum_{j=0}^{k-1} w[t][j] * yp[inv[t*k+j]][h], j ascending. */
+int orc_combine(int32_t T, int32_t H, int32_t k, const double* w, const int32_t* inv,
+                const double* yp, double* y) {
+  if (T < 0 || H < 1 || k < 1 || !w || !inv || !yp || !y) return -1;
+  for (int32_t t = 0; t < T; ++t)
+    for (int32_t h = 0; h < H; ++h) {
+      double s = 0.0;
+      for (int32_t j = 0; j < k; ++j)
+        s += w[(size_t)t * k + j] * yp[(size_t)inv[t * k + j] * H + h];
+      y[(size_t)t * H + h] = s;
+    }
+  return 0;
+}
+
+/* O1..O6 for all T tokens.  idx [T*k], w [T*k], counts [E], offsets [E+1],
+ * perm [T*k], inv [T*k] are outputs too. */
+int orc_layer_forward(const orc_layer_t* L, const void* x, int32_t T, double* y, int32_t* idx,
+                      double* w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                      int32_t* inv) {
+  if (check_layer(L) || !x || T < 0 || !y) return -1;
+  const int32_t H = L->H, E = L->E, k = L->k;
+  double* logits = (double*)malloc(sizeof(double) * ((size_t)T * E + 1));
+  double* yp = (double*)malloc(sizeof(double) * ((size_t)T * k * H + 1));
+  int rc = (!logits || !yp) ? -1 : 0;
+  if (!rc) rc = orc_logits(L, x, T, logits);
+  if (!rc) rc = orc_topk_softmax(T, E, k, logits, idx, w);
+  if (!rc) rc = orc_dispatch(T, E, k, idx, counts, offsets, perm, inv);
+  if (!rc) rc = orc_expert_rows(L, x, T, offsets, perm, yp);
+  if (!rc) rc = orc_combine(T, H, k, w, inv, yp, y);
+  free(logits);
+  free(yp);
+  return rc;
+}
+
+/* The layer output of selected tokens only, straight from the per-token
+ * definition y[t] = sum_j w_j * FFN_{idx_j}(x[t]) (the same value that
+ * O1..O6 give row t).  tokens [ntok]; idx_override [ntok*k] or NULL: when
+ * given, those experts (in that slot order) replace the top-k choice and the
+ * weights are the softmax of the oracle's logits at them.  Outputs y
+ * [ntok*H], idx [ntok*k], w [ntok*k], logits [ntok*E]. */
+int orc_layer_tokens(const orc_layer_t* L, const void* x, int32_t T, const int32_t* tokens,
+                     int32_t ntok, const int32_t* idx_override, double* y, int32_t* idx,
+                     double* w, double* logits) {
+  if (check_layer(L) || !x || T < 0 || ntok < 0 || !tokens || !y || !idx || !w || !logits)
+    return -1;
+  const int32_t H = L->H, E = L->E, k = L->k;
+  for (int32_t n = 0; n < ntok; ++n)
+    if (tokens[n] < 0 || tokens[n] >= T) return -1;
+  double* xs = (double*)malloc(sizeof(double) * ((size_t)ntok * H + 1));
+  double* ye = (double*)malloc(sizeof(double) * ((size_t)ntok * k * H + 1));
+  if (!xs || !ye) { free(xs); free(ye); return -1; }
+  int rc = 0;
+  for (int32_t n = 0; n < ntok && !rc; ++n) {
+    const int32_t t = tokens[n];
+    double* xr = xs + (size_t)n * H;
+    for (int32_t h = 0; h < H; ++h) xr[h] = widen(x, L->dtype, (size_t)t * H + h);
+    double* Lt = logits + (size_t)n * E;
+    for (int32_t e = 0; e < E; ++e) {
+      double s = 0.0;
+      for (int32_t h = 0; h < H; ++h) s += xr[h] * widen(L->router_w, L->dtype, (size_t)h * E + e);
+      if (L->router_b) s += (double)L->router_b[e];
+      Lt[e] = s;
+    }
+    int32_t* it = idx + (size_t)n * k;
+    double* wt = w + (size_t)n * k;
+    rc = topk_one(E, k, Lt, it, wt);
+    if (!rc && idx_override) {
+      for (int32_t j = 0; j < k; ++j) {
+        it[j] = idx_override[(size_t)n * k + j];
+        if (it[j] < 0 || it[j] >= E) rc = -1;
+      }
+      if (!rc) {
+        double m = Lt[it[0]], z = 0.0;
+        for (int32_t j = 0; j < k; ++j) z += exp(Lt[it[j]] - m);
+        for (int32_t j = 0; j < k; ++j) wt[j] = exp(Lt[it[j]] - m) / z;
+      }
+    }
+  }
+  if (!rc) {
+    /* every (token, slot) pair through its expert; pairs are independent */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int32_t q = 0; q < ntok * k; ++q) {
+      const int32_t n = q / k;
+      if (orc_expert_ffn(L, idx[q], xs + (size_t)n * H, ye + (size_t)q * H)) rc = -1;
+    }
+  }
+  if (!rc) {
+    for (int32_t n = 0; n < ntok; ++n)
+      for (int32_t h = 0; h < H; ++h) {
+        double s = 0.0;
+        for (int32_t j = 0; j < k; ++j) s += w[(size_t)n * k + j] * ye[((size_t)n * k + j) * H + h];
+        y[(size_t)n * H + h] = s;
+      }
+  }
+  free(xs);
+  free(ye);
+  return rc;
+}
+
+/* Branch input of a stacked layer: xt[t] = bf16( h[t] / sqrt(mean_h h^2 + 1e-6) ). */
+int orc_prenorm_bf16(int32_t T, int32_t H, const float* h, uint16_t* xt) {
+  if (T < 0 || H < 1 || !h || !xt) return -1;
+  for (int32_t t = 0; t < T; ++t) {
+    double ss = 0.0;
+    for (int32_t i = 0; i < H; ++i) ss += (double)h[(size_t)t * H + i] * (double)h[(size_t)t * H + i];
+    double r = sqrt(ss / (double)H + 1e-6);
+    for (int32_t i = 0; i < H; ++i) {
+      float f = (float)orc_bf16_round((double)h[(size_t)t * H + i] / r);
+      uint32_t bits;
+      memcpy(&bits, &f, sizeof bits);
+      xt[(size_t)t * H + i] = (uint16_t)(bits >> 16);
+    }
+  }
+  return 0;
+}

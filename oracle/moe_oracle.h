@@ -1,0 +1,86 @@
+/*
+ * moe_oracle.h -- plain, slow fp64 CPU oracle of one sparse MoE FFN layer's
+ * forward pass.  TEST INFRASTRUCTURE: only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg use it.  It shares no code, header, table or
+ * helper with the GPU library.
+ *
+ * What it computes, and where the pages define it (pages named by address):
+ *   logits   L[t][e] = sum_h x[t][h] * Wr[h][e] (+ b[e])
+ *              router as one linear layer of shape (hidden, experts):
+ *              zskr.cn/news/2275853 "Colibri：面向MoE架构的C语言高效推理引擎解析"
+ *              sec. 3.1 (router weight matrix) and m.nxbn.cn/news/47896 sec. 3.2
+ *              (logits from a matrix-vector product); the bias only for the
+ *              skewed 128-expert workload, added before selection.
+ *   top-k    the k largest logits per token, ties to the lower expert index,
+ *            then a softmax over the k selected logits: www.lmnt.cn/news/246575
+ *            sec. 2.2 (route_tokens: logits, top-k, in-place softmax).
+ *   dispatch the (token, slot) pairs grouped by expert into one batch per
+ *            expert: zskr.cn page sec. 3.3, stage 3.
+ *   expert   SwiGLU without bias, gate/up of shape (intermediate, hidden),
+ *            down of shape (hidden, intermediate): zskr.cn page sec. 3.1 and
+ *            sec. 3.3 stage 4 (gate_proj, up_proj, SiLU, down_proj).
+ *   combine  sum over the k slots of the gate weight times the expert output:
+ *            zskr.cn page sec. 2.2 and sec. 3.3 stage 5; www.pnsm.cn page
+ *            sec. 2.2 (weighted fusion).
+ *   stack    residual inside the forward call: www.pnsm.cn/news/1892388.html
+ *            sec. 2.1; with a parameter-free RMS normalisation of the branch
+ *            input (a reading: the literal residual stack overflows).
+ *
+ * Storage (all row-major):
+ *   x        [T][H]   dtype          Wr  [H][E] dtype       b [E] fp32
+ *   expert e at byte offset e*stride of `experts`:
+ *            Wg [F][H], Wu [F][H], Wd [H][F]   dtype
+ *   dtype ORC_F32: float; ORC_BF16: bfloat16 bit patterns (uint16).
+ * Every stored value is widened exactly to double; all sums are in double,
+ * in ascending index order.  In bf16 layers the SwiGLU activation is rounded
+ * to bf16 (round to nearest even) before the down projection, because the
+ * method stores that activation in bf16.
+ *
+ * Return codes: 0 ok, -1 invalid argument, -2 non-finite logit.
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_F32 = 0, ORC_BF16 = 1 };
+
+typedef struct {
+  int32_t H, F, E, k;
+  int32_t dtype;
+  const void* router_w;
+  const float* router_b;
+  const void* experts;
+  uint64_t stride;
+} orc_layer_t;
+
+int orc_logits(const orc_layer_t* L, const void* x, int32_t T, double* logits);
+int orc_topk_softmax(int32_t T, int32_t E, int32_t k, const double* logits, int32_t* idx,
+                     double* w);
+int orc_dispatch(int32_t T, int32_t E, int32_t k, const int32_t* idx, int32_t* counts,
+                 int32_t* offsets, int32_t* perm, int32_t* inv);
+int orc_expert_ffn(const orc_layer_t* L, int32_t e, const double* xrow, double* yrow);
+int orc_expert_rows(const orc_layer_t* L, const void* x, int32_t T, const int32_t* offsets,
+                    const int32_t* perm, double* yp);
+int orc_combine(int32_t T, int32_t H, int32_t k, const double* w, const int32_t* inv,
+                const double* yp, double* y);
+int orc_layer_forward(const orc_layer_t* L, const void* x, int32_t T, double* y, int32_t* idx,
+                      double* w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                      int32_t* inv);
+int orc_layer_tokens(const orc_layer_t* L, const void* x, int32_t T, const int32_t* tokens,
+                     int32_t ntok, const int32_t* idx_override, double* y, int32_t* idx,
+                     double* w, double* logits);
+int orc_prenorm_bf16(int32_t T, int32_t H, const float* h, uint16_t* xt);
+double orc_bf16_round(double v);
+int orc_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ORACLE_H */
