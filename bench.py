@@ -1,0 +1,172 @@
+"""Benchmark of one sparse MoE FFN layer forward on one MI355X.
+
+Default workload: the Mixtral-8x7B-shaped layer (H=4096, F=14336, E=8, k=2,
+bf16 weights and activations, fp32 accumulation) on a prefill batch of
+T=4096 tokens; one step = one full layer forward (router, top-k + softmax,
+dispatch, gate/up + SiLU, down, combine) over the batch, inputs resident in
+HBM.  The same weights are then timed on decode batches T = 1, 4, 16, 64.
+
+Prints ONE JSON line.  `roofline` describes the dominant kernel (the
+gate/up GEMM of the prefill step), timed with HIP events recorded by the
+library on the launch stream around that kernel in every timed step.
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of tokens of the
+same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s (decode T=1..64, prefill T=4096); % HBM / bf16-MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_prefill",
+                    choices=["mixtral_prefill", "qwen", "deepseek"])
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr, flush=True)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import gen
+    import mixture_experts_amd as moe
+
+    torch.cuda.set_device(0)
+    shape, T = {"mixtral_prefill": (gen.MIXTRAL, 4096), "qwen": (gen.QWEN, 512),
+                "deepseek": (gen.DEEPSEEK, 8192)}[args.workload]
+    print(f"[bench] generating inputs for {shape.name} T={T}", file=sys.stderr, flush=True)
+    x_h = gen.gen_x(shape, T)
+    wr_h, b_h, ex_h = gen.gen_router(shape), gen.gen_bias(shape), gen.gen_experts(shape)
+
+    def dev(a):
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
+
+    x, wr, ex = dev(x_h), dev(wr_h), dev(ex_h)
+    bias = None if b_h is None else dev(b_h)
+    layer = moe.MoELayer(shape.H, shape.F, shape.E, shape.k, T, moe.MOE_BF16, wr, ex,
+                         shape.stride, bias)
+    y = torch.empty((T, shape.H), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    K, W = args.steps, args.warmup
+    nst = moe.MOE_NUM_STAGES
+
+    def run(xx, yy, TT, steps, warm):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(steps)]
+        for row in evs:  # materialise the event handles
+            for e in row:
+                e.record(stream)
+        for _ in range(warm):
+            moe.moe_forward(layer.handle, xx, TT, yy, stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            moe.moe_forward_ev(layer.handle, xx, TT, yy, stream, [e.cuda_event for e in evs[i]])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        stage_ms = [sum(evs[i][s].elapsed_time(evs[i][s + 1]) for i in range(steps)) / steps
+                    for s in range(nst)]
+        dev_ms = sum(evs[i][0].elapsed_time(evs[i][nst]) for i in range(steps)) / steps
+        return wall, stage_ms, dev_ms
+
+    print(f"[bench] prefill: {W} warmup + {K} timed steps", file=sys.stderr, flush=True)
+    wall, stage_ms, dev_ms = run(x, y, T, K, W)
+    tok_s = T * K / wall
+    S = T * shape.k
+    gu_flops = 4.0 * S * shape.H * shape.F
+    dn_flops = 2.0 * S * shape.H * shape.F
+    t_gu = stage_ms[moe.MOE_STAGE_GATE_UP] * 1e-3
+    achieved = gu_flops / t_gu / 1e12
+    step_flops = gu_flops + dn_flops + 2.0 * T * shape.H * shape.E
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) tokens, N(0,0.02) weights (random init)",
+        "config": {"workload": f"{shape.name}_prefill", "tokens": T, "hidden": shape.H,
+                   "ffn": shape.F, "experts": shape.E, "top_k": shape.k,
+                   "router_bias": shape.bias},
+        "roofline": {"bound": "mfma", "kernel": "grouped gate/up GEMM + SiLU",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "stages_ms": {n: round(v, 4) for n, v in zip(moe.STAGE_NAMES, stage_ms)},
+        "step_device_ms": round(dev_ms, 4),
+        "step_tflops": round(step_flops / (dev_ms * 1e-3) / 1e12, 2),
+    }
+
+    if not args.no_decode and args.workload == "mixtral_prefill":
+        dec = {}
+        for Td in (1, 4, 16, 64):
+            xd = x[:Td]
+            yd = y[:Td]
+            r = layer.route(xd, Td)
+            torch.cuda.synchronize()
+            touched = int((r["counts"] > 0).sum().item())
+            wall_d, st_d, dev_d = run(xd, yd, Td, max(K, 50), W)
+            eb = 3 * shape.H * shape.F * 2
+            bytes_step = touched * eb + shape.H * shape.E * 2 + Td * shape.H * (2 + 4)
+            gu_bytes = touched * 2 * shape.H * shape.F * 2
+            dec[f"T{Td}"] = {
+                "tokens_per_s": round(Td * max(K, 50) / wall_d, 1),
+                "ms_per_step": round(wall_d / max(K, 50) * 1e3, 4),
+                "device_ms": round(dev_d, 4),
+                "experts_touched": touched,
+                "hbm_frac_step": round(bytes_step / (dev_d * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "gate_up_GBs": round(gu_bytes / (st_d[moe.MOE_STAGE_GATE_UP] * 1e-3) / 1e9, 1),
+                "stages_ms": {n: round(v, 4) for n, v in zip(moe.STAGE_NAMES, st_d)},
+            }
+        out["decode"] = dec
+
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.layer_from_gen(shape, wr_h, b_h, ex_h)
+        n, el = 2, 0.0
+        while True:
+            toks = np.arange(n, dtype=np.int32) * (T // n)
+            t0 = time.perf_counter()
+            orc.tokens(x_h, toks)
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds / 4 or n >= 1024:
+                break
+            n = min(1024, max(n * 2, int(n * args.cpu_seconds / 2 / max(el, 1e-3))))
+        out["cpu_baseline"] = {"value": round(n / el, 3), "unit": "tokens/s",
+                               "cores": oracle.num_threads(), "kind": "oracle",
+                               "sample": f"{n} of the {T} tokens, full layer per token "
+                                         f"(router, top-k, {shape.k} experts, combine), fp64",
+                               "seconds": round(el, 2)}
+    layer.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

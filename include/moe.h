@@ -1,0 +1,158 @@
+/*
+ * moe.h -- C ABI of libmoe: one sparse Mixture-of-Experts FFN layer's forward
+ * pass on one AMD Instinct MI355X (gfx950), all steps in HIP kernels.
+ *
+ * The layer (pages cited by address and section):
+ *   1. router logits  L = x . Wr (+ b), Wr of shape (hidden, experts)
+ *      [zskr.cn/news/2275853 "Colibri：面向MoE架构的C语言高效推理引擎解析"
+ *      sec. 3.1; m.nxbn.cn/news/47896 sec. 3.2]
+ *   2. per token the top_k largest logits (ties to the lower expert index),
+ *      then a softmax over those k logits [www.lmnt.cn/news/246575 sec. 2.2,
+ *      route_tokens steps 1-3]
+ *   3. dispatch: the (token, slot) pairs grouped into one batch per expert
+ *      [zskr.cn page sec. 3.3, stage 3]
+ *   4. per-expert SwiGLU FFN without bias: gate_proj and up_proj, SiLU, then
+ *      down_proj [zskr.cn page sec. 3.1 and sec. 3.3, stage 4]
+ *   5. combine: y[t] = sum_j w[t][j] * FFN_{idx[t][j]}(x[t]), slots in
+ *      ascending order, no atomics [zskr.cn page sec. 3.3, stage 5;
+ *      www.pnsm.cn/news/1892388.html sec. 2.2]
+ *   Optional: y = h + MoE(rmsnorm(h)), the residual taken inside the forward
+ *   call [www.pnsm.cn page sec. 2.1], with a parameter-free RMS normalisation
+ *   of the branch input (MOE_FLAG_RESIDUAL_PRENORM).
+ *
+ * Life cycle init / forward / free with caller-owned buffers follows the
+ * pages' C API [zskr.cn page sec. 4.2; www.pnsm.cn page sec. 2.1 and 4.4].
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers (hipMalloc or equivalent) on
+ *     the device that was current when the layer was created, 16-byte aligned.
+ *     They are borrowed: the caller owns them and keeps the weights alive
+ *     until moe_layer_free.  The layer owns only its workspace, allocated
+ *     once by moe_layer_create for max_tokens; no call allocates afterwards.
+ *   - Matrices are row-major.  dtype MOE_BF16 means bfloat16 (stored as 16-bit
+ *     patterns), MOE_F32 means IEEE float.
+ *   - Calls validate their arguments synchronously and return MOE_OK or a
+ *     negative MOE_ERR_* code without launching anything on error.  Work is
+ *     queued on `stream` (a hipStream_t; NULL = the null stream) and runs
+ *     asynchronously; a launch failure returns MOE_ERR_DEVICE.
+ *   - One call in flight per layer (calls share the layer's workspace):
+ *     create one layer per concurrent stream.  Results are bitwise
+ *     reproducible for identical inputs (no floating-point atomics).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_layer moe_layer_t; /* opaque */
+
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* bad pointer, size, alignment or descriptor field */
+  MOE_ERR_NO_MEMORY = -2,   /* workspace allocation failed */
+  MOE_ERR_DEVICE = -3,      /* a HIP call or kernel launch failed */
+  MOE_ERR_UNSUPPORTED = -4  /* valid, but outside what the kernels implement */
+};
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+enum {
+  /* Stacked-layer mode: x is the fp32 residual stream h [T][H]; the branch
+   * input is bf16(h[t] / sqrt(mean_h h[t]^2 + 1e-6)) and y = h + MoE(.).
+   * y may alias x.  bf16 layers only. */
+  MOE_FLAG_RESIDUAL_PRENORM = 1u << 0,
+  /* Kernel path for the expert FFN of bf16 layers.  By default a call with
+   * T*k <= 32*E (few rows per expert: decode batches, many small experts)
+   * streams each non-empty expert's weights once; otherwise the rows go
+   * through grouped GEMMs on 256x256 tiles.  These flags pin one path
+   * (results agree within rounding; both are deterministic). */
+  MOE_FLAG_PATH_GROUPED = 1u << 1,
+  MOE_FLAG_PATH_STREAM = 1u << 2
+};
+
+typedef struct {
+  uint32_t struct_size;   /* sizeof(moe_layer_desc) */
+  int32_t hidden;         /* H: model width */
+  int32_t ffn;            /* F: expert FFN width */
+  int32_t num_experts;    /* E: 1..256 */
+  int32_t top_k;          /* k: 1..min(E, 8) */
+  int32_t max_tokens;     /* largest T any call will pass: 1..65536 */
+  int32_t dtype;          /* moe_dtype of x, router_w, the experts and the
+                             stored SwiGLU activation */
+  uint32_t flags;         /* MOE_FLAG_* */
+  const void* router_w;   /* [H][E] dtype: element (h, e) at h*E + e */
+  const float* router_b;  /* [E] fp32 added to the logits, or NULL */
+  const void* expert_base;/* expert e starts at expert_base + e*expert_stride
+                             bytes and holds, contiguously,
+                               Wg [F][H]  gate_proj (row f = output unit f)
+                               Wu [F][H]  up_proj
+                               Wd [H][F]  down_proj
+                             so g_f = sum_h x_h Wg[f][h] and
+                             y_h = sum_f a_f Wd[h][f] */
+  uint64_t expert_stride; /* bytes, >= 3*H*F*sizeof(dtype), multiple of 256 */
+} moe_layer_desc;
+
+/* Validates *d, allocates the workspace for d->max_tokens on the current
+ * device and returns the layer, or NULL with *status (if non-NULL) set to the
+ * error.  Shape limits of the kernels (else MOE_ERR_UNSUPPORTED): bf16 layers
+ * need H % 256 == 0 and F % 128 == 0; fp32 layers H % 4 == 0 and F % 4 == 0;
+ * E <= 256, k <= 8; max_tokens*k*max(H, F), max_tokens*H and 3*H*F below
+ * 2^31.  Nothing is launched. */
+moe_layer_t* moe_layer_create(const moe_layer_desc* d, int* status);
+
+/* Steps 1-3 only, with their results copied out (for inspection and tests).
+ *   x          [T][H] dtype (fp32 h in RESIDUAL_PRENORM mode), 1 <= T <= max_tokens
+ *   logits_in  [T][E] fp32 or NULL: when given, step 1 is skipped and these
+ *              logits are used as they are
+ *   topk_idx   [T][k] int32 out: expert of slot j of token t, slots ordered by
+ *              descending logit, equal logits by ascending expert index
+ *   topk_w     [T][k] fp32 out: softmax of the selected logits
+ *   counts     [E] int32 out or NULL: tokens routed to each expert
+ *   offsets    [E+1] int32 out or NULL: exclusive prefix sum of counts
+ *   perm       [T*k] int32 out or NULL: perm[p] = t*k + j of the p-th pair in
+ *              (expert, token) order
+ *   inv        [T*k] int32 out or NULL: inv[t*k + j] = p, the inverse of perm */
+int moe_route(moe_layer_t* L, const void* x, int32_t T, const float* logits_in,
+              int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+              int32_t* perm, int32_t* inv, void* stream);
+
+/* The whole layer, steps 1-5.
+ *   x  [T][H] dtype; fp32 h in RESIDUAL_PRENORM mode
+ *   y  [T][H] fp32 out; may alias x only in RESIDUAL_PRENORM mode
+ * T in 1..max_tokens. */
+int moe_forward(moe_layer_t* L, const void* x, int32_t T, float* y, void* stream);
+
+/* moe_forward with per-stage timing events.  stage_events is NULL (same as
+ * moe_forward) or an array of MOE_NUM_STAGES + 1 hipEvent_t created by the
+ * caller; event i is recorded on `stream` right before stage i is enqueued
+ * and event MOE_NUM_STAGES after the last stage, so hipEventElapsedTime
+ * between events i and i+1 is the device time of stage i:
+ *   MOE_STAGE_ROUTE    (branch normalisation,) router logits, top-k, softmax
+ *   MOE_STAGE_DISPATCH histogram, scan, scatter
+ *   MOE_STAGE_GATE_UP  gate/up projections + SiLU (one kernel)
+ *   MOE_STAGE_DOWN     down projection (one kernel)
+ *   MOE_STAGE_COMBINE  weighted combine (+ residual) (one kernel) */
+enum {
+  MOE_STAGE_ROUTE = 0,
+  MOE_STAGE_DISPATCH = 1,
+  MOE_STAGE_GATE_UP = 2,
+  MOE_STAGE_DOWN = 3,
+  MOE_STAGE_COMBINE = 4,
+  MOE_NUM_STAGES = 5
+};
+int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* stream,
+                   void* const* stage_events);
+
+/* Releases the workspace (after synchronising the device).  NULL-safe. */
+void moe_layer_free(moe_layer_t* L);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

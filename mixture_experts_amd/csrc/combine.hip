@@ -1,0 +1,50 @@
+// combine.hip -- step 5: y[t] = sum_{j<k} w[t][j] * yp[inv[t*k+j]], slots in
+// ascending order, one fp32 fused multiply-add per slot, no atomics; plus the
+// residual h[t] when the layer runs inside a residual stack.
+//
+// The pages accumulate the K expert outputs weighted by their gate scores
+// [zskr.cn/news/2275853 "Colibri：面向MoE架构的C语言高效推理引擎解析" sec. 3.3
+// stage 5, there with atomicAdd; www.pnsm.cn/news/1892388.html sec. 2.2]; here
+// each output element is owned by one thread, which fixes the order.  The
+// residual is taken inside the forward call as on www.pnsm.cn page sec. 2.1.
+// HBM-bound: 16-byte loads and stores, consecutive threads on consecutive
+// columns.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ yp,
+                                                      const float* __restrict__ w,
+                                                      const int32_t* __restrict__ inv,
+                                                      const float* resid, int T, int H, int k,
+                                                      float* y) {
+  const int h4n = H >> 2;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)T * h4n) return;
+  const int t = (int)(i / h4n), c = (int)(i % h4n) * 4;
+  const int S = T * k;
+  f32x4 acc{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[(size_t)t * k + j];
+    const int p = min(max(inv[(size_t)t * k + j], 0), S - 1);  // in range by construction
+    const f32x4 v = *reinterpret_cast<const f32x4*>(yp + (size_t)p * H + c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = fmaf(wj, v[q], acc[q]);
+  }
+  if (resid) {
+    const f32x4 r = *reinterpret_cast<const f32x4*>(resid + (size_t)t * H + c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = r[q] + acc[q];
+  }
+  *reinterpret_cast<f32x4*>(y + (size_t)t * H + c) = acc;
+}
+
+}  // namespace
+
+int launch_combine(const float* yp, const float* w, const int32_t* inv, const float* resid,
+                   int T, int H, int k, float* y, hipStream_t st) {
+  const int64_t n = (int64_t)T * (H / 4);
+  combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(yp, w, inv, resid, T, H, k, y);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}

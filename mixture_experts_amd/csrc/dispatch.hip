@@ -1,0 +1,130 @@
+// dispatch.hip -- step 3: group the T*k (token, slot) pairs by expert.
+//
+// The pages batch all tokens routed to one expert together before the
+// expert GEMMs [zskr.cn/news/2275853 "Colibri：面向MoE架构的C语言高效推理引擎解析"
+// sec. 3.3, stage 3].  Here that is a stable counting sort of the slots
+// s = t*k + j by expert: counts[e], offsets = exclusive prefix sum,
+// perm[p] = s for the p-th pair in (expert, token) order, inv[s] = p.
+//
+// Three kernels, all deterministic (no ordering depends on atomics):
+//   hist    one wave per run of 512 slots; the rank of a slot among the
+//           earlier slots of the same expert in its run comes from a
+//           bit-sliced ballot match (lanes holding the same expert id) and a
+//           popcount; per-run expert counts go to hist[run][e].
+//   scan    one workgroup: per-expert prefix over runs, offsets, the tile
+//           schedule of the grouped GEMM and the list of non-empty experts.
+//   scatter one thread per slot: p = run base of its expert + its rank.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+__global__ __launch_bounds__(64) void dispatch_hist_kernel(const int32_t* __restrict__ idx,
+                                                           int S, int E, int nbits,
+                                                           int32_t* __restrict__ hist,
+                                                           int32_t* __restrict__ rank) {
+  __shared__ int32_t cnt[MOE_MAX_EXPERTS];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) cnt[e] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * DISPATCH_RUN;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c = 0; c < DISPATCH_RUN / 64; ++c) {
+    const int s = base + c * 64 + lane;
+    const bool valid = s < S;
+    const int e = valid ? idx[s] : 0;
+    uint64_t match = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      match &= bit ? m : ~m;
+    }
+    const uint64_t earlier = match & below;
+    const int c0 = valid ? cnt[e] : 0;
+    __syncthreads();
+    if (valid) {
+      rank[s] = c0 + __popcll(earlier);
+      if (earlier == 0) cnt[e] = c0 + __popcll(match);
+    }
+    __syncthreads();
+  }
+  for (int e = lane; e < E; e += 64) hist[(size_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// One workgroup of MOE_MAX_EXPERTS threads.  base[r][e] = offsets[e] + sum of
+// hist[r'][e] for r' < r.  tile_off[e] = sum over e' < e of ceil(counts[e'] /
+// tile_rows).  active[0..n) = the experts with counts > 0, ascending;
+// active[E] = n.
+__global__ __launch_bounds__(MOE_MAX_EXPERTS) void dispatch_scan_kernel(
+    const int32_t* __restrict__ hist, int nrun, int E, int tile_rows,
+    int32_t* __restrict__ base, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ tile_off, int32_t* __restrict__ active) {
+  __shared__ int32_t sc[MOE_MAX_EXPERTS];
+  __shared__ int32_t so[MOE_MAX_EXPERTS + 1];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+    for (int r = 0; r < nrun; ++r) {
+      const int h = hist[(size_t)r * E + e];
+      base[(size_t)r * E + e] = run;
+      run += h;
+    }
+    counts[e] = run;
+  }
+  sc[e] = (e < E) ? run : 0;
+  __syncthreads();
+  if (e == 0) {
+    int o = 0, t = 0, n = 0;
+    for (int i = 0; i < E; ++i) {
+      so[i] = o;
+      offsets[i] = o;
+      tile_off[i] = t;
+      o += sc[i];
+      t += (sc[i] + tile_rows - 1) / tile_rows;
+      if (sc[i] > 0) active[n++] = i;
+    }
+    so[E] = o;
+    offsets[E] = o;
+    tile_off[E] = t;
+    active[E] = n;
+  }
+  __syncthreads();
+  if (e < E) {
+    const int o = so[e];
+    for (int r = 0; r < nrun; ++r) base[(size_t)r * E + e] += o;
+  }
+}
+
+__global__ __launch_bounds__(256) void dispatch_scatter_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ rank,
+    const int32_t* __restrict__ base, int S, int E, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv) {
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  if (s >= S) return;
+  const int e = idx[s];
+  const int p = base[(size_t)(s / DISPATCH_RUN) * E + e] + rank[s];
+  // p is in [0, S) by construction; the guard keeps a logic error from
+  // turning into an out-of-bounds store (inv then points at a valid row)
+  if (p >= 0 && p < S) {
+    perm[p] = s;
+    inv[s] = p;
+  } else {
+    inv[s] = 0;
+  }
+}
+
+}  // namespace
+
+int launch_dispatch(const DispatchArgs& a, hipStream_t st) {
+  const int S = a.S;
+  const int nrun = (S + DISPATCH_RUN - 1) / DISPATCH_RUN;
+  int nbits = 0;
+  while ((1 << nbits) < a.E) ++nbits;
+  dispatch_hist_kernel<<<nrun, 64, 0, st>>>(a.idx, S, a.E, nbits, a.hist, a.rank);
+  dispatch_scan_kernel<<<1, MOE_MAX_EXPERTS, 0, st>>>(a.hist, nrun, a.E, a.tile_rows, a.base,
+                                                      a.counts, a.offsets, a.tile_off,
+                                                      a.active);
+  dispatch_scatter_kernel<<<(S + 255) / 256, 256, 0, st>>>(a.idx, a.rank, a.base, S, a.E,
+                                                           a.perm, a.inv);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}

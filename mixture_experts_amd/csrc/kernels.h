@@ -1,0 +1,71 @@
+// kernels.h -- internal launchers of libmoe (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_TOPK 8
+#define DISPATCH_RUN 512  // slots per histogram run
+
+// grouped (prefill) GEMM tile: weight rows x token rows x K step
+#define GG_BW 256
+#define GG_BT 256
+#define GG_BK 64
+
+struct RouterArgs {
+  const void* x;          // [T][H] bf16 or fp32
+  int T, H, E, k;
+  int dtype_f32;
+  const void* wr;         // [H][E]
+  const float* bias;      // [E] or null
+  const float* logits_in; // [T][E] or null
+  int32_t* idx;           // [T][k]
+  float* w;               // [T][k]
+};
+
+struct DispatchArgs {
+  const int32_t* idx;  // [S]
+  int S, E;
+  int tile_rows;       // token rows per grouped-GEMM tile
+  int32_t* hist;       // [nrun][E]
+  int32_t* rank;       // [S]
+  int32_t* base;       // [nrun][E]
+  int32_t* counts;     // [E]
+  int32_t* offsets;    // [E+1]
+  int32_t* tile_off;   // [E+1]
+  int32_t* active;     // [E+1]
+  int32_t* perm;       // [S]
+  int32_t* inv;        // [S]
+};
+
+struct ExpertArgs {
+  const void* x;            // [T][H] layer input (bf16 or fp32)
+  const void* experts;      // expert blocks
+  uint64_t stride_elems;    // expert stride in elements
+  int T, H, F, E, k, S;
+  int rows_hint;            // rows per expert one streaming pass should cover
+  const int32_t* perm;      // [S]
+  const int32_t* offsets;   // [E+1]
+  const int32_t* tile_off;  // [E+1]
+  const int32_t* active;    // [E+1]
+  void* act;                // [S][F] bf16 or fp32
+  float* yp;                // [S][H] fp32
+};
+
+int launch_router(const RouterArgs& a, hipStream_t st);
+int launch_prenorm(const float* h, int T, int H, uint16_t* xt, hipStream_t st);
+int launch_dispatch(const DispatchArgs& a, hipStream_t st);
+
+// bf16 expert FFN, grouped MFMA GEMMs (many rows per expert)
+int launch_grouped_gate_up(const ExpertArgs& a, hipStream_t st);
+int launch_grouped_down(const ExpertArgs& a, hipStream_t st);
+// bf16 expert FFN, weight-streaming MFMA kernels (few rows per expert)
+int launch_stream_gate_up(const ExpertArgs& a, hipStream_t st);
+int launch_stream_down(const ExpertArgs& a, hipStream_t st);
+// fp32 expert FFN (plain FMA)
+int launch_f32_gate_up(const ExpertArgs& a, hipStream_t st);
+int launch_f32_down(const ExpertArgs& a, hipStream_t st);
+
+int launch_combine(const float* yp, const float* w, const int32_t* inv, const float* resid,
+                   int T, int H, int k, float* y, hipStream_t st);

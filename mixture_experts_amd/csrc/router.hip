@@ -1,0 +1,227 @@
+// router.hip -- steps 1 and 2 of the layer: router logits, top-k, softmax.
+//
+// Logits L = x . Wr with Wr of shape (hidden, experts) [zskr.cn/news/2275853
+// "Colibri：面向MoE架构的C语言高效推理引擎解析" sec. 3.1; m.nxbn.cn/news/47896
+// sec. 3.2], optional per-expert bias; then per token the k largest logits
+// (equal logits: lower expert index first) and a softmax over those k
+// [www.lmnt.cn/news/246575 sec. 2.2, route_tokens].
+//
+// One workgroup = 4 waves = 64 tokens.  bf16 layers compute the logits with
+// v_mfma_f32_16x16x32_bf16 (tokens as the A operand, the router slice staged
+// transposed in LDS as the B operand, fp32 accumulation); fp32 layers with
+// plain fp32 FMAs.  The logits tile stays in LDS; each wave then selects the
+// top-k of its 16 tokens, one token at a time, with the experts spread over
+// the 64 lanes and a butterfly max-reduction over (value desc, index asc).
+// The softmax over the k picks is evaluated in fp64.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int RT_TOK = 64;  // tokens per workgroup
+constexpr int RT_HC = 64;   // hidden chunk staged per step
+constexpr int RT_PAD = 8;   // bf16 padding of a staged router row
+
+struct Cand {
+  float v;
+  int e;  // INT32_MAX = no candidate
+};
+
+__device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
+  if (a.e == INT32_MAX) return false;
+  if (b.e == INT32_MAX) return true;
+  return a.v > b.v || (a.v == b.v && a.e < b.e);
+}
+
+// Top-k + softmax of the tokens of this wave.  lg: LDS logits [RT_TOK][ldl].
+__device__ void topk_rows(const float* lg, int ldl, int tok0, int ntok, int T, int E, int k,
+                          int32_t* idx_out, float* w_out) {
+  const int lane = threadIdx.x & 63;
+  for (int r = 0; r < ntok; ++r) {
+    const int t = tok0 + r;
+    if (t >= T) break;
+    const float* row = lg + (size_t)(t % RT_TOK) * ldl;
+    float v[4];
+    uint32_t avail = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      int e = lane + 64 * c;
+      v[c] = (e < E) ? row[e] : 0.0f;
+      if (e < E) avail |= 1u << c;
+    }
+    float sel_v[8];
+    int sel_e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      sel_v[j] = 0.0f;
+      sel_e[j] = 0;
+      if (j >= k) continue;
+      Cand best{0.0f, INT32_MAX};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        Cand cand{v[c], (avail >> c & 1u) ? lane + 64 * c : INT32_MAX};
+        if (better(cand, best)) best = cand;
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        Cand o{__shfl_xor(best.v, off), __shfl_xor(best.e, off)};
+        if (better(o, best)) best = o;
+      }
+      sel_v[j] = best.v;
+      sel_e[j] = best.e;
+      if ((best.e & 63) == lane) avail &= ~(1u << (best.e >> 6));
+    }
+    // softmax over the k selected logits, in double
+    const double m = (double)sel_v[0];
+    double z = 0.0;
+    double num = 0.0;
+    int ej = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j >= k) continue;
+      const double ex = exp((double)sel_v[j] - m);
+      z += ex;
+      if (j == lane) { num = ex; ej = sel_e[j]; }
+    }
+    if (lane < k) {
+      idx_out[(size_t)t * k + lane] = ej;
+      w_out[(size_t)t * k + lane] = (float)(num / z);
+    }
+  }
+}
+
+template <int NT>
+__global__ __launch_bounds__(256) void router_bf16_kernel(
+    const uint16_t* __restrict__ x, int T, int H, int E, int k,
+    const uint16_t* __restrict__ wr, const float* __restrict__ bias,
+    const float* __restrict__ logits_in, int32_t* __restrict__ idx_out,
+    float* __restrict__ w_out) {
+  constexpr int EP = NT * 16;
+  constexpr int LDW = RT_HC + RT_PAD;
+  __shared__ __attribute__((aligned(16))) uint16_t wt[EP * LDW];
+  __shared__ float lg[RT_TOK * (EP + 1)];
+  const int ldl = EP + 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tile0 = blockIdx.x * RT_TOK;
+
+  if (logits_in) {
+    for (int i = tid; i < RT_TOK * E; i += 256) {
+      int r = i / E, e = i % E;
+      if (tile0 + r < T) lg[r * ldl + e] = logits_in[(size_t)(tile0 + r) * E + e];
+    }
+  } else {
+    f32x4 acc[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int my_tok = tile0 + wave * 16 + (lane & 15);
+    const bool tok_ok = my_tok < T;
+    const uint16_t* xrow = x + (size_t)(tok_ok ? my_tok : 0) * H;
+    const int kq = (lane >> 4) * 8;
+    for (int h0 = 0; h0 < H; h0 += RT_HC) {
+      __syncthreads();
+      for (int i = tid; i < RT_HC * EP; i += 256) {
+        int r = i / EP, e = i % EP;
+        wt[e * LDW + r] = (e < E) ? wr[(size_t)(h0 + r) * E + e] : (uint16_t)0;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < RT_HC / 32; ++s) {
+        u32x4 av = tok_ok ? ldg16(xrow + h0 + s * 32 + kq) : u32x4{0u, 0u, 0u, 0u};
+        bf16x8 a = as_bf16x8(av);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const uint16_t* bp = wt + (n * 16 + (lane & 15)) * LDW + s * 32 + kq;
+          bf16x8 b = as_bf16x8(*reinterpret_cast<const u32x4*>(bp));
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[n], 0, 0, 0);
+        }
+      }
+    }
+    // C layout: lane holds column (expert) lane%16, rows 4*(lane/16) + j
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int e = n * 16 + (lane & 15);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = wave * 16 + (lane >> 4) * 4 + j;
+        if (e < E) lg[r * ldl + e] = acc[n][j] + (bias ? bias[e] : 0.0f);
+      }
+    }
+  }
+  __syncthreads();
+  topk_rows(lg, ldl, tile0 + wave * 16, 16, T, E, k, idx_out, w_out);
+}
+
+__global__ __launch_bounds__(256) void router_f32_kernel(
+    const float* __restrict__ x, int T, int H, int E, int k, const float* __restrict__ wr,
+    const float* __restrict__ bias, const float* __restrict__ logits_in,
+    int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
+  __shared__ float lg[RT_TOK * 257];
+  const int ldl = E + 1;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tile0 = blockIdx.x * RT_TOK;
+  for (int i = tid; i < RT_TOK * E; i += 256) {
+    const int r = i / E, e = i % E, t = tile0 + r;
+    if (t >= T) continue;
+    float s;
+    if (logits_in) {
+      s = logits_in[(size_t)t * E + e];
+    } else {
+      s = 0.0f;
+      for (int h = 0; h < H; ++h) s = fmaf(x[(size_t)t * H + h], wr[(size_t)h * E + e], s);
+      if (bias) s += bias[e];
+    }
+    lg[r * ldl + e] = s;
+  }
+  __syncthreads();
+  topk_rows(lg, ldl, tile0 + wave * 16, 16, T, E, k, idx_out, w_out);
+}
+
+// Branch input of a stacked layer: xt[t] = bf16(h[t] / sqrt(mean(h[t]^2) + 1e-6)).
+// One workgroup per token; fixed-order reduction.
+__global__ __launch_bounds__(256) void prenorm_kernel(const float* __restrict__ h, int H,
+                                                      uint16_t* __restrict__ xt) {
+  __shared__ float part[256];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const float* row = h + (size_t)t * H;
+  float ss = 0.0f;
+  for (int i = tid; i < H; i += 256) ss = fmaf(row[i], row[i], ss);
+  part[tid] = ss;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) part[tid] += part[tid + s];
+    __syncthreads();
+  }
+  const float r = sqrtf(part[0] / (float)H + 1e-6f);
+  for (int i = tid; i < H; i += 256) xt[(size_t)t * H + i] = f32_to_bf16(row[i] / r);
+}
+
+}  // namespace
+
+int launch_router(const RouterArgs& a, hipStream_t st) {
+  const int grid = (a.T + RT_TOK - 1) / RT_TOK;
+  if (a.dtype_f32) {
+    router_f32_kernel<<<grid, 256, 0, st>>>((const float*)a.x, a.T, a.H, a.E, a.k,
+                                            (const float*)a.wr, a.bias, a.logits_in, a.idx,
+                                            a.w);
+  } else {
+    const int nt = (a.E + 15) / 16;
+    auto* xx = (const uint16_t*)a.x;
+    auto* ww = (const uint16_t*)a.wr;
+    if (nt <= 1)
+      router_bf16_kernel<1><<<grid, 256, 0, st>>>(xx, a.T, a.H, a.E, a.k, ww, a.bias, a.logits_in, a.idx, a.w);
+    else if (nt <= 2)
+      router_bf16_kernel<2><<<grid, 256, 0, st>>>(xx, a.T, a.H, a.E, a.k, ww, a.bias, a.logits_in, a.idx, a.w);
+    else if (nt <= 4)
+      router_bf16_kernel<4><<<grid, 256, 0, st>>>(xx, a.T, a.H, a.E, a.k, ww, a.bias, a.logits_in, a.idx, a.w);
+    else if (nt <= 8)
+      router_bf16_kernel<8><<<grid, 256, 0, st>>>(xx, a.T, a.H, a.E, a.k, ww, a.bias, a.logits_in, a.idx, a.w);
+    else
+      router_bf16_kernel<16><<<grid, 256, 0, st>>>(xx, a.T, a.H, a.E, a.k, ww, a.bias, a.logits_in, a.idx, a.w);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_prenorm(const float* h, int T, int H, uint16_t* xt, hipStream_t st) {
+  prenorm_kernel<<<T, 256, 0, st>>>(h, H, xt);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}

@@ -1,0 +1,116 @@
+"""Helpers shared by the GPU parity tests: build a device layer and its oracle
+twin from the same seeded host inputs, and compare outputs under the rules
+below.
+
+Comparison rules
+  * floating-point outputs: max |y_gpu - y_ref| <= tol * RMS(y_ref), with
+    tol = 1e-5 for fp32 layers and 1e-2 for bf16 layers;
+  * routing: a token whose k-th and (k+1)-th largest oracle logits differ by
+    less than 1e-3 is a near tie.  If the GPU picked a different expert set
+    (or order) for it, the GPU's set must still be a top-k set under a
+    perturbation of at most 1e-3, and that token's reference output is the
+    oracle's output recomputed with the GPU's experts.  Any other routing
+    difference fails.
+"""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+import torch
+
+import gen
+import mixture_experts_amd as moe
+import oracle
+
+NEAR_TIE = 1e-3
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+@functools.lru_cache(maxsize=4)
+def host_inputs(shape: gen.LayerShape, layer: int = 0):
+    """(router_w, bias, experts) of a layer, generated once per process."""
+    return gen.gen_router(shape, layer), gen.gen_bias(shape), gen.gen_experts(shape, layer)
+
+
+class Case:
+    """A device layer and the oracle over the very same host arrays."""
+
+    def __init__(self, shape: gen.LayerShape, max_tokens: int, flags: int = 0, layer: int = 0,
+                 router=None, bias="default", experts=None):
+        wr, b, ex = host_inputs(shape, layer) if router is None or experts is None else (
+            None, None, None)
+        self.router = wr if router is None else router
+        self.bias = b if isinstance(bias, str) else bias
+        self.experts = ex if experts is None else experts
+        self.shape = shape
+        dt = moe.MOE_F32 if shape.dtype == "f32" else moe.MOE_BF16
+        self.d_router = to_dev(self.router)
+        self.d_bias = None if self.bias is None else to_dev(self.bias)
+        self.d_experts = to_dev(self.experts)
+        self.layer = moe.MoELayer(shape.H, shape.F, shape.E, shape.k, max_tokens, dt,
+                                  self.d_router, self.d_experts, shape.stride, self.d_bias, flags)
+        self.orc = oracle.layer_from_gen(shape, self.router, self.bias, self.experts)
+
+    def forward(self, x_np: np.ndarray) -> np.ndarray:
+        x = to_dev(x_np)
+        y = torch.empty((x_np.shape[0], self.shape.H), dtype=torch.float32, device="cuda")
+        self.layer.forward(x, y)
+        torch.cuda.synchronize()
+        return y.cpu().numpy()
+
+    def route(self, x_np: np.ndarray) -> dict:
+        r = self.layer.route(to_dev(x_np), x_np.shape[0])
+        torch.cuda.synchronize()
+        return {k: v.cpu().numpy() for k, v in r.items()}
+
+    def close(self):
+        self.layer.close()
+
+
+def near_tie_gap(logits: np.ndarray, k: int) -> np.ndarray:
+    """k-th minus (k+1)-th largest logit per row (inf when k == E)."""
+    if k >= logits.shape[1]:
+        return np.full(logits.shape[0], np.inf)
+    s = -np.sort(-logits, axis=1)
+    return s[:, k - 1] - s[:, k]
+
+
+def check_rows(case: Case, x_np: np.ndarray, tokens, y_gpu_rows: np.ndarray,
+               gpu_idx_rows: np.ndarray, tol: float | None = None) -> dict:
+    """Compare GPU output rows of `tokens` with the oracle, near-tie rule applied."""
+    k = case.shape.k
+    tol = TOL[case.shape.dtype] if tol is None else tol
+    tokens = np.asarray(tokens, np.int32)
+    ref = case.orc.tokens(x_np, tokens)
+    gap = near_tie_gap(ref["logits"], k)
+    gpu_idx_rows = np.asarray(gpu_idx_rows).reshape(len(tokens), k)
+    differs = np.any(gpu_idx_rows != ref["idx"], axis=1)
+    stats = dict(tokens=len(tokens), near_ties=int((gap < NEAR_TIE).sum()),
+                 routed_differently=int(differs.sum()))
+    y_ref = ref["y"].copy()
+    if differs.any():
+        kth = -np.sort(-ref["logits"], axis=1)[:, k - 1]
+        for n in np.nonzero(differs)[0]:
+            chosen = ref["logits"][n, gpu_idx_rows[n]]
+            # allowed only for near ties, and only as a valid top-k under a
+            # perturbation of at most NEAR_TIE (slot order: adjacent slots
+            # may swap only when their logits are that close)
+            assert len(set(gpu_idx_rows[n].tolist())) == k, (tokens[n], gpu_idx_rows[n])
+            assert np.all(chosen >= kth[n] - NEAR_TIE), (tokens[n], gpu_idx_rows[n], ref["idx"][n])
+            assert np.all(np.diff(chosen) <= NEAR_TIE), (tokens[n], chosen)
+        fix = np.nonzero(differs)[0]
+        r2 = case.orc.tokens(x_np, tokens[fix], idx_override=gpu_idx_rows[fix])
+        y_ref[fix] = r2["y"]
+    rms = float(np.sqrt(np.mean(y_ref ** 2)))
+    err = float(np.abs(y_gpu_rows.astype(np.float64) - y_ref).max()) if len(tokens) else 0.0
+    stats.update(rms=rms, max_err=err, rel=err / rms if rms > 0 else err)
+    assert np.isfinite(y_gpu_rows).all()
+    assert err <= tol * rms, stats
+    return stats
