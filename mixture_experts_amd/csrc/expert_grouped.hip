@@ -15,11 +15,13 @@
 // arrangement, each wave 128x128 with 16 v_mfma_f32_32x32x16_bf16
 // accumulators (256 fp32 per lane).  For gate/up the 256 weight rows are 128
 // gate rows and the same 128 up rows, so SiLU(g)*u pairs accumulators that
-// sit in the same lane.  Tiles are staged in LDS (2 buffers x 128 KB total)
+// sit in the same lane.  Tiles are staged in LDS (2 buffers x 64 KB) by
+// direct global->LDS loads (global_load_lds_dwordx4, no register staging),
 // with the 16-byte chunks of each 128-byte row XOR-swizzled by (row & 7) so
-// that the MFMA operand reads are free of bank conflicts; global loads for
-// tile k+1 are in flight while tile k is multiplied.  Within a K step each
-// lane reads 4 consecutive chunks of its row (a fixed permutation of the
+// that the MFMA operand reads are free of bank conflicts; the loads of K step
+// k+1 are in flight while step k is multiplied, and the operands of MFMA
+// sub-step s+1 are read from LDS while sub-step s runs.  Within a K step
+// lane group g reads chunks 4g..4g+3 of its row (a fixed permutation of the
 // summation index, applied identically to both operands).
 //
 // Tiles are built on the device from the expert offsets (no host sync): the
@@ -68,24 +70,42 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
-  const int lrow = tid >> 3, lc = tid & 7;
 
+  // Global -> LDS: waves 0-1 bring the 256 weight rows, waves 2-3 the 256
+  // token rows of each K step.  One global_load_lds_dwordx4 of a wave fills
+  // 1 KB of LDS = 8 rows; lane l lands in row r0 + l/8 at physical chunk l%8,
+  // so it fetches logical chunk (l%8) ^ (row & 7) of that row (the swizzle).
   const uint16_t* eb = experts + (size_t)e * stride_elems;
-  uint32_t aoff[8], boff[8];
+  const uint16_t* gbase = (wave < 2) ? eb : tok;
+  const int lrow = lane >> 3;
+  const int lchunk = (lane & 7) ^ lrow;  // rows r0 + lrow with r0 % 8 == 0
+  uint32_t roff[16];
 #pragma unroll
-  for (int ri = 0; ri < 8; ++ri) {
-    const int r = ri * 32 + lrow;
-    if (GATED) {
-      const int f0 = mt * 128;
-      aoff[ri] = (r < 128) ? (uint32_t)(f0 + r) * H
-                           : (uint32_t)F * H + (uint32_t)(f0 + r - 128) * H;
-      const int p = p0 + min(r, rows_left - 1);
-      boff[ri] = (uint32_t)min(max(perm[p], 0) / k_top, T - 1) * H;
+  for (int i = 0; i < 16; ++i) {
+    const int r = (wave & 1) * 128 + i * 8 + lrow;  // row within the A or B half
+    if (wave < 2) {
+      if (GATED) {
+        const int f0 = mt * 128;
+        roff[i] = (r < 128) ? (uint32_t)(f0 + r) * H
+                            : (uint32_t)F * H + (uint32_t)(f0 + r - 128) * H;
+      } else {
+        roff[i] = 2u * (uint32_t)F * H + (uint32_t)(mt * 256 + r) * F;
+      }
     } else {
-      aoff[ri] = 2u * (uint32_t)F * H + (uint32_t)(mt * 256 + r) * F;
-      boff[ri] = (uint32_t)(p0 + min(r, rows_left - 1)) * F;
+      const int p = p0 + min(r, rows_left - 1);
+      roff[i] = GATED ? (uint32_t)min(max(perm[p], 0) / k_top, T - 1) * H : (uint32_t)p * F;
     }
+    roff[i] += lchunk * 8;
   }
+  auto issue = [&](int buf, int k0) {
+    __attribute__((address_space(3))) u32x4* dst =
+        (__attribute__((address_space(3))) u32x4*)&lds[buf][wave * 128 * 8];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(gbase + roff[i] + k0),
+                                       (__attribute__((address_space(3))) void*)(dst + i * 64),
+                                       16, 0, 0);
+  };
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -95,53 +115,54 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  u32x4 ra[8], rb[8];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int ri = 0; ri < 8; ++ri) {
-      ra[ri] = ldg16(eb + aoff[ri] + k0 + lc * 8);
-      rb[ri] = ldg16(tok + boff[ri] + k0 + lc * 8);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int ri = 0; ri < 8; ++ri) {
-      const int r = ri * 32 + lrow;
-      lds[buf][lds_chunk(r, lc)] = ra[ri];
-      lds[buf][lds_chunk(GG_BW + r, lc)] = rb[ri];
-    }
-  };
-
   int arow[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    arow[i] = GATED ? ((i < 2) ? wm * 64 + 32 * i : 128 + wm * 64 + 32 * (i - 2))
-                    : wm * 128 + 32 * i;
+    arow[i] = (GATED ? ((i < 2) ? wm * 64 + 32 * i : 128 + wm * 64 + 32 * (i - 2))
+                     : wm * 128 + 32 * i) + (lane & 31);
   const int brow = GG_BW + wn * 128 + (lane & 31);
   const int kg = lane >> 5;
 
+  bf16x8 a[2][4], b[2][4];
+  auto fetch = [&](int buf, int s, int slot) {
+    const int c = kg * 4 + s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[slot][i] = as_bf16x8(lds[buf][lds_chunk(arow[i], c)]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[slot][j] = as_bf16x8(lds[buf][lds_chunk(brow + 32 * j, c)]);
+  };
+
   const int nk = K / GG_BK;
-  gload(0);
-  lstore(0);
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * GG_BK);
+    if (kt + 1 < nk) issue(cur ^ 1, (kt + 1) * GG_BK);
+    fetch(cur, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the 8 reads of sub-step 0
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int c = kg * 4 + s;
-      bf16x8 a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = as_bf16x8(lds[cur][lds_chunk(arow[i] + (lane & 31), c)]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = as_bf16x8(lds[cur][lds_chunk(brow + 32 * j, c)]);
+      if (s < 3) fetch(cur, s + 1, (s + 1) & 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][i], b[s & 1][j],
+                                                              acc[i][j], 0, 0, 0);
+      // interleave the next sub-step's LDS reads with this sub-step's MFMAs
+      if (s < 3) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      }
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's loads have landed
     __syncthreads();
   }
 

@@ -10,9 +10,9 @@
 // Work unit: one non-empty expert x 16 weight rows (gate AND up rows f0..f0+15
 // for the first kernel; down rows h0..h0+15 for the second), all of the
 // expert's token rows in passes of NB*16.  The 4 waves split the K dimension;
-// each lane streams 128 contiguous bytes of its weight row per 8 MFMA steps
-// (16-byte loads), so a row's K slice is read as long contiguous runs, and
-// the token rows (L2-resident) use the same lane -> K mapping.  MFMA:
+// lanes load 16 bytes each, four lanes covering 64 contiguous bytes of a row
+// per instruction, with 8 (gate: 16) loads per lane in flight per batch of 8
+// MFMA steps; the token rows (L2-resident) use the same lane -> K mapping.  MFMA:
 // v_mfma_f32_16x16x32_bf16 with weight rows as A and tokens as B.  The four
 // K partial sums are added in LDS in a fixed order (deterministic), then the
 // gate/up kernel applies SiLU(g)*u and stores the activation in bf16; the
@@ -73,21 +73,25 @@ __global__ __launch_bounds__(256) void stream_kernel(
       const int p = p_beg + (bok[n] ? t : 0);
       brow[n] = GATED ? tok + (size_t)min(max(perm[p], 0) / k_top, T - 1) * H : tok + (size_t)p * F;
     }
+    // MFMA step s covers k in [32 s, 32 s + 32); lane group kg holds
+    // k = 32 s + 8 kg .. +7, so one load instruction reads 64 contiguous
+    // bytes of each of the 16 rows.  Steps go in batches of 8 so that 8 (or
+    // 16) weight loads per lane are in flight before the first MFMA.
     int s = s_beg;
     for (; s + 8 <= s_end; s += 8) {
-      const int kb = s * 32 + kg * 64;
       u32x4 va[8], vu[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        va[q] = ldg16(wa + kb + q * 8);
-        if (GATED) vu[q] = ldg16(wu + kb + q * 8);
+        const int kb = (s + q) * 32 + kg * 8;
+        va[q] = ldg16(wa + kb);
+        if (GATED) vu[q] = ldg16(wu + kb);
       }
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
         u32x4 vb[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q)
-          vb[q] = bok[n] ? ldg16(brow[n] + kb + q * 8) : u32x4{0u, 0u, 0u, 0u};
+          vb[q] = bok[n] ? ldg16(brow[n] + (s + q) * 32 + kg * 8) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           acc[0][n] = mfma16(va[q], vb[q], acc[0][n]);

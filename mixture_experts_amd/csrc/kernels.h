@@ -22,6 +22,7 @@ struct RouterArgs {
   const float* logits_in; // [T][E] or null
   int32_t* idx;           // [T][k]
   float* w;               // [T][k]
+  float* part;            // [router_splits(T, H)][T][E] partial logits (bf16 layers)
 };
 
 struct DispatchArgs {
@@ -53,6 +54,7 @@ struct ExpertArgs {
   float* yp;                // [S][H] fp32
 };
 
+int router_splits(int T, int H);
 int launch_router(const RouterArgs& a, hipStream_t st);
 int launch_prenorm(const float* h, int T, int H, uint16_t* xt, hipStream_t st);
 int launch_dispatch(const DispatchArgs& a, hipStream_t st);

@@ -24,6 +24,7 @@ struct moe_layer {
   uint16_t* xt;       // [maxT][H] bf16 branch input (RESIDUAL_PRENORM)
   int32_t* idx;       // [S]
   float* w;           // [S]
+  float* part;        // partial router logits
   int32_t* counts;    // [E]
   int32_t* offsets;   // [E+1]
   int32_t* tile_off;  // [E+1]
@@ -99,6 +100,15 @@ void carve(moe_layer* L, Arena& A) {
                                         ? (size_t)d.max_tokens * d.hidden * 2 : 0);
   L->idx = (int32_t*)arena_alloc(A, S * 4);
   L->w = (float*)arena_alloc(A, S * 4);
+  size_t part = 0;
+  if (d.dtype == MOE_BF16) {
+    for (int tiles = 1; (tiles - 1) * 64 < d.max_tokens; ++tiles) {
+      const int T = tiles * 64 < d.max_tokens ? tiles * 64 : d.max_tokens;
+      const size_t need = (size_t)router_splits(T, d.hidden) * T * E * 4;
+      if (need > part) part = need;
+    }
+  }
+  L->part = (float*)arena_alloc(A, part);
   L->counts = (int32_t*)arena_alloc(A, E * 4);
   L->offsets = (int32_t*)arena_alloc(A, (E + 1) * 4);
   L->tile_off = (int32_t*)arena_alloc(A, (E + 1) * 4);
@@ -144,7 +154,7 @@ int run_route(moe_layer* L, const void* x_route, int T, const float* logits_in,
               int tile_rows, hipStream_t st) {
   const moe_layer_desc& d = L->d;
   RouterArgs ra{x_route, T, d.hidden, d.num_experts, d.top_k, d.dtype == MOE_F32 ? 1 : 0,
-                d.router_w, d.router_b, logits_in, L->idx, L->w};
+                d.router_w, d.router_b, logits_in, L->idx, L->w, L->part};
   if (launch_router(ra, st)) return MOE_ERR_DEVICE;
   DispatchArgs da{L->idx, T * d.top_k, d.num_experts, tile_rows, L->hist, L->rank, L->base,
                   L->counts, L->offsets, L->tile_off, L->active, L->perm, L->inv};
@@ -259,7 +269,7 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
   {
     const moe_layer_desc& dd = L->d;
     RouterArgs ra{xin, T, dd.hidden, dd.num_experts, dd.top_k, f32 ? 1 : 0, dd.router_w,
-                  dd.router_b, nullptr, L->idx, L->w};
+                  dd.router_b, nullptr, L->idx, L->w, L->part};
     if (launch_router(ra, st)) return MOE_ERR_DEVICE;
     if (!mark(MOE_STAGE_DISPATCH)) return MOE_ERR_DEVICE;
     DispatchArgs da{L->idx, S, dd.num_experts, GG_BT, L->hist, L->rank, L->base, L->counts,

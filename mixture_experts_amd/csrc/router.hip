@@ -6,13 +6,16 @@
 // (equal logits: lower expert index first) and a softmax over those k
 // [www.lmnt.cn/news/246575 sec. 2.2, route_tokens].
 //
-// One workgroup = 4 waves = 64 tokens.  bf16 layers compute the logits with
-// v_mfma_f32_16x16x32_bf16 (tokens as the A operand, the router slice staged
-// transposed in LDS as the B operand, fp32 accumulation); fp32 layers with
-// plain fp32 FMAs.  The logits tile stays in LDS; each wave then selects the
-// top-k of its 16 tokens, one token at a time, with the experts spread over
-// the 64 lanes and a butterfly max-reduction over (value desc, index asc).
-// The softmax over the k picks is evaluated in fp64.
+// bf16 layers: a first kernel computes partial logits of 64-token tiles over
+// slices of the hidden dimension (split so that even one token fills several
+// hundred workgroups) with v_mfma_f32_16x16x32_bf16 (tokens as the A operand,
+// the router slice staged transposed in LDS as the B operand, fp32
+// accumulation); a second kernel adds the slices in a fixed order (+ bias).
+// fp32 layers use one plain-FMA kernel.  The logits tile of 64 tokens sits in
+// LDS; each wave selects the top-k of its 16 tokens, one token at a time,
+// with the experts spread over the 64 lanes and a butterfly max-reduction
+// over (value desc, index asc).  The softmax over the k picks is evaluated in
+// fp64.
 #include "common.h"
 #include "kernels.h"
 
@@ -21,6 +24,7 @@ namespace {
 constexpr int RT_TOK = 64;  // tokens per workgroup
 constexpr int RT_HC = 64;   // hidden chunk staged per step
 constexpr int RT_PAD = 8;   // bf16 padding of a staged router row
+constexpr int RT_MAX_SPLITS = 16;
 
 struct Cand {
   float v;
@@ -33,14 +37,16 @@ __device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
   return a.v > b.v || (a.v == b.v && a.e < b.e);
 }
 
-// Top-k + softmax of the tokens of this wave.  lg: LDS logits [RT_TOK][ldl].
-__device__ void topk_rows(const float* lg, int ldl, int tok0, int ntok, int T, int E, int k,
+// Top-k + softmax of tokens tile0 + wave, tile0 + wave + 4, ... (16 per
+// wave, interleaved so that small batches still spread over the 4 waves).
+// lg: LDS logits [RT_TOK][ldl].
+__device__ void topk_rows(const float* lg, int ldl, int tile0, int T, int E, int k,
                           int32_t* idx_out, float* w_out) {
-  const int lane = threadIdx.x & 63;
-  for (int r = 0; r < ntok; ++r) {
-    const int t = tok0 + r;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int r = wave; r < RT_TOK; r += 4) {
+    const int t = tile0 + r;
     if (t >= T) break;
-    const float* row = lg + (size_t)(t % RT_TOK) * ldl;
+    const float* row = lg + (size_t)r * ldl;
     float v[4];
     uint32_t avail = 0;
 #pragma unroll
@@ -90,65 +96,90 @@ __device__ void topk_rows(const float* lg, int ldl, int tok0, int ntok, int T, i
   }
 }
 
+// Partial logits of a 64-token tile over one slice of the hidden dimension:
+// part[split][t][e] = sum over h in the slice of x[t][h] * Wr[h][e].  The
+// slice is walked in chunks of RT_HC; each chunk of the router is staged in
+// LDS transposed ([e][h]) so that the MFMA B operand is a 16-byte read.
 template <int NT>
-__global__ __launch_bounds__(256) void router_bf16_kernel(
-    const uint16_t* __restrict__ x, int T, int H, int E, int k,
-    const uint16_t* __restrict__ wr, const float* __restrict__ bias,
-    const float* __restrict__ logits_in, int32_t* __restrict__ idx_out,
-    float* __restrict__ w_out) {
+__global__ __launch_bounds__(256) void router_partial_kernel(
+    const uint16_t* __restrict__ x, int T, int H, int E, const uint16_t* __restrict__ wr,
+    int hslice, float* __restrict__ part) {
   constexpr int EP = NT * 16;
   constexpr int LDW = RT_HC + RT_PAD;
   __shared__ __attribute__((aligned(16))) uint16_t wt[EP * LDW];
-  __shared__ float lg[RT_TOK * (EP + 1)];
-  const int ldl = EP + 1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile0 = blockIdx.x * RT_TOK;
-
-  if (logits_in) {
-    for (int i = tid; i < RT_TOK * E; i += 256) {
-      int r = i / E, e = i % E;
-      if (tile0 + r < T) lg[r * ldl + e] = logits_in[(size_t)(tile0 + r) * E + e];
+  const int split = blockIdx.y;
+  const int hb = split * hslice;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int my_tok = tile0 + wave * 16 + (lane & 15);
+  const bool tok_ok = my_tok < T;
+  const uint16_t* xrow = x + (size_t)(tok_ok ? my_tok : 0) * H;
+  const int kq = (lane >> 4) * 8;
+  for (int h0 = hb; h0 < hb + hslice; h0 += RT_HC) {
+    u32x4 av[RT_HC / 32];
+#pragma unroll
+    for (int s = 0; s < RT_HC / 32; ++s)
+      av[s] = tok_ok ? ldg16(xrow + h0 + s * 32 + kq) : u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+    for (int i = tid; i < RT_HC * EP; i += 256) {
+      const int r = i / EP, e = i % EP;
+      wt[e * LDW + r] = (e < E) ? wr[(size_t)(h0 + r) * E + e] : (uint16_t)0;
     }
-  } else {
-    f32x4 acc[NT];
+    __syncthreads();
 #pragma unroll
-    for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int my_tok = tile0 + wave * 16 + (lane & 15);
-    const bool tok_ok = my_tok < T;
-    const uint16_t* xrow = x + (size_t)(tok_ok ? my_tok : 0) * H;
-    const int kq = (lane >> 4) * 8;
-    for (int h0 = 0; h0 < H; h0 += RT_HC) {
-      __syncthreads();
-      for (int i = tid; i < RT_HC * EP; i += 256) {
-        int r = i / EP, e = i % EP;
-        wt[e * LDW + r] = (e < E) ? wr[(size_t)(h0 + r) * E + e] : (uint16_t)0;
-      }
-      __syncthreads();
+    for (int s = 0; s < RT_HC / 32; ++s) {
+      const bf16x8 a = as_bf16x8(av[s]);
 #pragma unroll
-      for (int s = 0; s < RT_HC / 32; ++s) {
-        u32x4 av = tok_ok ? ldg16(xrow + h0 + s * 32 + kq) : u32x4{0u, 0u, 0u, 0u};
-        bf16x8 a = as_bf16x8(av);
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          const uint16_t* bp = wt + (n * 16 + (lane & 15)) * LDW + s * 32 + kq;
-          bf16x8 b = as_bf16x8(*reinterpret_cast<const u32x4*>(bp));
-          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[n], 0, 0, 0);
-        }
-      }
-    }
-    // C layout: lane holds column (expert) lane%16, rows 4*(lane/16) + j
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const int e = n * 16 + (lane & 15);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = wave * 16 + (lane >> 4) * 4 + j;
-        if (e < E) lg[r * ldl + e] = acc[n][j] + (bias ? bias[e] : 0.0f);
+      for (int n = 0; n < NT; ++n) {
+        const uint16_t* bp = wt + (n * 16 + (lane & 15)) * LDW + s * 32 + kq;
+        const bf16x8 b = as_bf16x8(*reinterpret_cast<const u32x4*>(bp));
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[n], 0, 0, 0);
       }
     }
   }
+  // C layout: lane holds column (expert) lane%16, rows 4*(lane/16) + j
+  float* out = part + (size_t)split * T * E;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int e = n * 16 + (lane & 15);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = tile0 + wave * 16 + (lane >> 4) * 4 + j;
+      if (e < E && t < T) out[(size_t)t * E + e] = acc[n][j];
+    }
+  }
+}
+
+// Sum of the partial logits in split order (+ bias), then top-k and softmax.
+// nsplit == 0: `part` holds caller-given logits [T][E], used as they are.
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ part,
+                                                          int nsplit, int T, int E, int k,
+                                                          const float* __restrict__ bias,
+                                                          int32_t* __restrict__ idx_out,
+                                                          float* __restrict__ w_out) {
+  __shared__ float lg[RT_TOK * (MOE_MAX_EXPERTS + 1)];
+  const int ldl = E + 1;
+  const int tid = threadIdx.x;
+  const int tile0 = blockIdx.x * RT_TOK;
+  for (int i = tid; i < RT_TOK * E; i += 256) {
+    const int r = i / E, e = i % E, t = tile0 + r;
+    if (t >= T) continue;
+    float v[RT_MAX_SPLITS];
+#pragma unroll
+    for (int p = 0; p < RT_MAX_SPLITS; ++p)
+      v[p] = (p < nsplit || p == 0) ? part[((size_t)p * T + t) * E + e] : 0.0f;
+    float s = v[0];
+#pragma unroll
+    for (int p = 1; p < RT_MAX_SPLITS; ++p)
+      if (p < nsplit) s += v[p];
+    if (nsplit > 0 && bias) s += bias[e];
+    lg[r * ldl + e] = s;
+  }
   __syncthreads();
-  topk_rows(lg, ldl, tile0 + wave * 16, 16, T, E, k, idx_out, w_out);
+  topk_rows(lg, ldl, tile0, T, E, k, idx_out, w_out);
 }
 
 __global__ __launch_bounds__(256) void router_f32_kernel(
@@ -173,7 +204,7 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
     lg[r * ldl + e] = s;
   }
   __syncthreads();
-  topk_rows(lg, ldl, tile0 + wave * 16, 16, T, E, k, idx_out, w_out);
+  topk_rows(lg, ldl, tile0, T, E, k, idx_out, w_out);
 }
 
 // Branch input of a stacked layer: xt[t] = bf16(h[t] / sqrt(mean(h[t]^2) + 1e-6)).
@@ -197,27 +228,47 @@ __global__ __launch_bounds__(256) void prenorm_kernel(const float* __restrict__ 
 
 }  // namespace
 
+int router_splits(int T, int H) {
+  const int ntt = (T + RT_TOK - 1) / RT_TOK;
+  int ns = (512 + ntt - 1) / ntt;          // aim at >= 512 workgroups
+  int max_ns = H / 256;                    // slices of at least 256
+  if (max_ns > RT_MAX_SPLITS) max_ns = RT_MAX_SPLITS;
+  if (ns > max_ns) ns = max_ns;
+  if (ns < 1) ns = 1;
+  while (H % (ns * RT_HC)) --ns;           // slices made of whole chunks
+  return ns;
+}
+
 int launch_router(const RouterArgs& a, hipStream_t st) {
   const int grid = (a.T + RT_TOK - 1) / RT_TOK;
   if (a.dtype_f32) {
     router_f32_kernel<<<grid, 256, 0, st>>>((const float*)a.x, a.T, a.H, a.E, a.k,
                                             (const float*)a.wr, a.bias, a.logits_in, a.idx,
                                             a.w);
-  } else {
-    const int nt = (a.E + 15) / 16;
-    auto* xx = (const uint16_t*)a.x;
-    auto* ww = (const uint16_t*)a.wr;
-    if (nt <= 1)
-      router_bf16_kernel<1><<<grid, 256, 0, st>>>(xx, a.T, a.H, a.E, a.k, ww, a.bias, a.logits_in, a.idx, a.w);
-    else if (nt <= 2)
-      router_bf16_kernel<2><<<grid, 256, 0, st>>>(xx, a.T, a.H, a.E, a.k, ww, a.bias, a.logits_in, a.idx, a.w);
-    else if (nt <= 4)
-      router_bf16_kernel<4><<<grid, 256, 0, st>>>(xx, a.T, a.H, a.E, a.k, ww, a.bias, a.logits_in, a.idx, a.w);
-    else if (nt <= 8)
-      router_bf16_kernel<8><<<grid, 256, 0, st>>>(xx, a.T, a.H, a.E, a.k, ww, a.bias, a.logits_in, a.idx, a.w);
-    else
-      router_bf16_kernel<16><<<grid, 256, 0, st>>>(xx, a.T, a.H, a.E, a.k, ww, a.bias, a.logits_in, a.idx, a.w);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
   }
+  if (a.logits_in) {
+    router_topk_kernel<<<grid, 256, 0, st>>>(a.logits_in, 0, a.T, a.E, a.k, nullptr, a.idx,
+                                             a.w);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
+  const int ns = router_splits(a.T, a.H);
+  const int hs = a.H / ns;
+  const dim3 g2(grid, ns);
+  const int nt = (a.E + 15) / 16;
+  auto* xx = (const uint16_t*)a.x;
+  auto* ww = (const uint16_t*)a.wr;
+  if (nt <= 1)
+    router_partial_kernel<1><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, ww, hs, a.part);
+  else if (nt <= 2)
+    router_partial_kernel<2><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, ww, hs, a.part);
+  else if (nt <= 4)
+    router_partial_kernel<4><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, ww, hs, a.part);
+  else if (nt <= 8)
+    router_partial_kernel<8><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, ww, hs, a.part);
+  else
+    router_partial_kernel<16><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, ww, hs, a.part);
+  router_topk_kernel<<<grid, 256, 0, st>>>(a.part, ns, a.T, a.E, a.k, a.bias, a.idx, a.w);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
