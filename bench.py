@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (reference "
+                         "for the HBM traffic counters)")
     return ap.parse_args()
 
 
@@ -164,6 +167,14 @@ def main():
                                "sample": f"{n} of the {T} tokens, full layer per token "
                                          f"(router, top-k, {shape.k} experts, combine), fp64",
                                "seconds": round(el, 2)}
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_probe_bytes"] = n
     layer.close()
     print(json.dumps(out), flush=True)
 

@@ -15,6 +15,7 @@
 namespace {
 
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ yp,
+                                                      int nplanes,
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ inv,
                                                       const float* resid, int T, int H, int k,
@@ -28,7 +29,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   for (int j = 0; j < k; ++j) {
     const float wj = w[(size_t)t * k + j];
     const int p = min(max(inv[(size_t)t * k + j], 0), S - 1);  // in range by construction
-    const f32x4 v = *reinterpret_cast<const f32x4*>(yp + (size_t)p * H + c);
+    f32x4 v = *reinterpret_cast<const f32x4*>(yp + (size_t)p * H + c);
+    for (int pl = 1; pl < nplanes; ++pl)  // partial sums of a split K, in plane order
+      v += *reinterpret_cast<const f32x4*>(yp + ((size_t)pl * S + p) * H + c);
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = fmaf(wj, v[q], acc[q]);
   }
@@ -42,9 +45,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 }  // namespace
 
-int launch_combine(const float* yp, const float* w, const int32_t* inv, const float* resid,
-                   int T, int H, int k, float* y, hipStream_t st) {
+int launch_combine(const float* yp, int nplanes, const float* w, const int32_t* inv,
+                   const float* resid, int T, int H, int k, float* y, hipStream_t st) {
   const int64_t n = (int64_t)T * (H / 4);
-  combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(yp, w, inv, resid, T, H, k, y);
+  combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(yp, nplanes, w, inv, resid, T, H,
+                                                              k, y);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -11,7 +11,9 @@
 // grouped (prefill) GEMM tile: weight rows x token rows x K step
 #define GG_BW 256
 #define GG_BT 256
+#ifndef GG_BK
 #define GG_BK 64
+#endif
 
 struct RouterArgs {
   const void* x;          // [T][H] bf16 or fp32
@@ -61,7 +63,10 @@ int launch_dispatch(const DispatchArgs& a, hipStream_t st);
 
 // bf16 expert FFN, grouped MFMA GEMMs (many rows per expert)
 int launch_grouped_gate_up(const ExpertArgs& a, hipStream_t st);
-int launch_grouped_down(const ExpertArgs& a, hipStream_t st);
+// split-K factor the grouped down projection uses for this call (1 or 2);
+// with 2 it writes two partial planes yp[2][S][H]
+int grouped_down_ksplit(const ExpertArgs& a);
+int launch_grouped_down(const ExpertArgs& a, int ksplit, hipStream_t st);
 // bf16 expert FFN, weight-streaming MFMA kernels (few rows per expert)
 int launch_stream_gate_up(const ExpertArgs& a, hipStream_t st);
 int launch_stream_down(const ExpertArgs& a, hipStream_t st);
@@ -69,5 +74,6 @@ int launch_stream_down(const ExpertArgs& a, hipStream_t st);
 int launch_f32_gate_up(const ExpertArgs& a, hipStream_t st);
 int launch_f32_down(const ExpertArgs& a, hipStream_t st);
 
-int launch_combine(const float* yp, const float* w, const int32_t* inv, const float* resid,
-                   int T, int H, int k, float* y, hipStream_t st);
+// y[t] = resid[t] + sum_j w[t][j] * (sum over planes q of yp[q][inv[t*k+j]])
+int launch_combine(const float* yp, int nplanes, const float* w, const int32_t* inv,
+                   const float* resid, int T, int H, int k, float* y, hipStream_t st);

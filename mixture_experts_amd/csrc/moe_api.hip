@@ -119,7 +119,8 @@ void carve(moe_layer* L, Arena& A) {
   L->perm = (int32_t*)arena_alloc(A, S * 4);
   L->inv = (int32_t*)arena_alloc(A, S * 4);
   L->act = arena_alloc(A, S * (size_t)d.ffn * L->esize);
-  L->yp = (float*)arena_alloc(A, S * (size_t)d.hidden * 4);
+  // two planes: the grouped down projection may split its K range in two
+  L->yp = (float*)arena_alloc(A, 2 * S * (size_t)d.hidden * 4);
 }
 
 // Keeps the layer's device current for the duration of a call.
@@ -302,11 +303,12 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
   int r1 = f32 ? launch_f32_gate_up(ea, st)
                : stream_path ? launch_stream_gate_up(ea, st) : launch_grouped_gate_up(ea, st);
   if (r1 || !mark(MOE_STAGE_DOWN)) return MOE_ERR_DEVICE;
+  const int planes = (f32 || stream_path) ? 1 : grouped_down_ksplit(ea);
   int r2 = f32 ? launch_f32_down(ea, st)
-               : stream_path ? launch_stream_down(ea, st) : launch_grouped_down(ea, st);
+               : stream_path ? launch_stream_down(ea, st) : launch_grouped_down(ea, planes, st);
   if (r2 || !mark(MOE_STAGE_COMBINE)) return MOE_ERR_DEVICE;
-  if (launch_combine(L->yp, L->w, L->inv, prenorm ? (const float*)x : nullptr, T, d.hidden,
-                     d.top_k, y, st))
+  if (launch_combine(L->yp, planes, L->w, L->inv, prenorm ? (const float*)x : nullptr, T,
+                     d.hidden, d.top_k, y, st))
     return MOE_ERR_DEVICE;
   if (!mark(MOE_NUM_STAGES)) return MOE_ERR_DEVICE;
   return MOE_OK;
