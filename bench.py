@@ -24,6 +24,27 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s (decode T=1..64, prefill T=4096); % HBM / bf16-MFMA peak"
+PROFILE = os.path.join(ROOT, "profiles", "grouped_gemm_mixtral_prefill_T4096.md")
+KERNEL_SRC = os.path.join(ROOT, "mixture_experts_amd", "csrc", "expert_grouped.hip")
+
+
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed rocprofv3 counter summary,
+    or None when the kernel source changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(PROFILE).read()
+        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    fields = dict(l.split(":", 1) for l in text.splitlines()
+                  if l.startswith(("source_sha256:", "traffic_bytes_per_launch:")))
+    if fields.get("source_sha256", "").strip() != src:
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
@@ -121,7 +142,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "grouped gate/up GEMM + SiLU",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic()},
         "stages_ms": {n: round(v, 4) for n, v in zip(moe.STAGE_NAMES, stage_ms)},
         "step_device_ms": round(dev_ms, 4),
         "step_tflops": round(step_flops / (dev_ms * 1e-3) / 1e12, 2),
