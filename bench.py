@@ -57,12 +57,86 @@ def parse():
     ap.add_argument("--workload", default="mixtral_prefill",
                     choices=["mixtral_prefill", "qwen", "deepseek"])
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the 32-layer stacked decode (90 GB of experts)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (reference "
                          "for the HBM traffic counters)")
     return ap.parse_args()
+
+
+def bench_stack(K, W):
+    """32 Mixtral-shaped layers, experts in one contiguous buffer (layer l,
+    expert e at blob + (l*E + e)*stride), residual stream h <- h + MoE(norm(h));
+    one step = all 32 layers on a decode batch, replayed as one HIP graph."""
+    import numpy as np
+    import torch
+
+    import gen
+    import mixture_experts_amd as moe
+    shape, NL = gen.MIXTRAL, 32
+    st = torch.cuda.current_stream()
+    blob = torch.empty(NL * shape.E * shape.stride, dtype=torch.uint8, device="cuda")
+    layers, keep = [], []
+    for l in range(NL):
+        base = blob.data_ptr() + l * shape.E * shape.stride
+        gen.experts_device(shape, base, layer=l, stream=st.cuda_stream)
+        wr = torch.from_numpy(gen.gen_router(shape, layer=l).view(np.int16)).cuda()
+        keep.append(wr)
+        layers.append(moe.MoELayer(shape.H, shape.F, shape.E, shape.k, 64, moe.MOE_BF16, wr,
+                                   base, shape.stride, flags=moe.MOE_FLAG_RESIDUAL_PRENORM))
+    torch.cuda.synchronize()
+    eb = 3 * shape.H * shape.F * 2
+    res = {"layers": NL, "expert_buffer_GB": round(blob.numel() / 1e9, 2)}
+    for T in (1, 4, 16, 64):
+        x0 = torch.from_numpy(gen.normal(0, 0, gen.T_X, T * shape.H, 1.0, "f32")).cuda()
+        x0 = x0.view(T, shape.H)
+        h = torch.empty_like(x0)
+        h.copy_(x0)
+        touched = 0
+        for L in layers:  # eager pass: experts each layer touches (same routing as the graph)
+            r = L.route(h, T)
+            touched += int((r["counts"] > 0).sum().item())
+            moe.moe_forward(L.handle, h, T, h, st)
+        side = torch.cuda.Stream()
+        side.wait_stream(st)
+        with torch.cuda.stream(side):
+            for _ in range(2):
+                h.copy_(x0)
+                for L in layers:
+                    moe.moe_forward(L.handle, h, T, h, side)
+        st.wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream()
+            h.copy_(x0)
+            for L in layers:
+                moe.moe_forward(L.handle, h, T, h, cs)
+        for _ in range(W):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(st)
+        for _ in range(K):
+            g.replay()
+        e1.record(st)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / K
+        dev_s = e0.elapsed_time(e1) / K * 1e-3
+        byts = touched * eb
+        res[f"T{T}"] = {"tokens_per_s": round(T / wall, 1), "ms_per_step": round(wall * 1e3, 4),
+                        "device_ms": round(dev_s * 1e3, 4),
+                        "experts_touched_per_layer": round(touched / NL, 3),
+                        "hbm_frac": round(byts / dev_s / 1e9 / PEAK_HBM_GBS, 4)}
+        del g
+    for L in layers:
+        L.close()
+    del blob
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -170,6 +244,10 @@ def main():
                 "stages_ms": {n: round(v, 4) for n, v in zip(moe.STAGE_NAMES, st_d)},
             }
         out["decode"] = dec
+
+    if not args.no_stack and args.workload == "mixtral_prefill":
+        print("[bench] 32-layer stacked decode", file=sys.stderr, flush=True)
+        out["stack_decode"] = bench_stack(max(K, 20), W)
 
     if not args.no_cpu_baseline:
         import oracle

@@ -62,6 +62,49 @@ def lib():
     return _LIB
 
 
+_DEV = None
+
+
+def devlib():
+    """The device generator (gen/libgendev.so, HIP); same values as `normal`."""
+    global _DEV
+    if _DEV is None:
+        path = os.path.join(_HERE, "libgendev.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: run __graft_entry__.build() first")
+        L = ctypes.CDLL(path)
+        for name in ("gen_device_normal_bf16", "gen_device_normal_f32"):
+            fn = getattr(L, name)
+            fn.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint64,
+                           ctypes.c_uint64, ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p]
+            fn.restype = ctypes.c_int
+        _DEV = L
+    return _DEV
+
+
+def normal_device(seed: int, layer: int, tensor: int, n: int, sigma: float, dtype: str,
+                  out_ptr: int, idx0: int = 0, stream: int = 0) -> None:
+    """Values idx0 .. idx0+n-1 of stream (seed, layer, tensor) into device
+    memory at out_ptr (bf16 bits or fp32), bit-identical to `normal`."""
+    fn = {"bf16": devlib().gen_device_normal_bf16, "f32": devlib().gen_device_normal_f32}[dtype]
+    rc = fn(seed, layer, tensor, idx0, n, sigma, out_ptr, stream)
+    if rc != 0:
+        raise RuntimeError(f"device generator failed ({rc})")
+
+
+def experts_device(shape: "LayerShape", base_ptr: int, layer: int = 0, seed: int | None = None,
+                   stream: int = 0) -> None:
+    """gen_experts(shape, layer) written straight into device memory at base_ptr
+    (E blocks of shape.stride bytes; padding bytes are left untouched)."""
+    s = shape.seed if seed is None else seed
+    per = shape.H * shape.F
+    for e in range(shape.E):
+        base = base_ptr + e * shape.stride
+        for j, tid in enumerate((T_WG, T_WU, T_WD)):
+            normal_device(s, layer, tid, per, SIGMA_W, shape.dtype,
+                          base + j * per * shape.elem, idx0=e * per, stream=stream)
+
+
 def normal(seed: int, layer: int, tensor: int, n: int, sigma: float, dtype: str,
            idx0: int = 0, out: np.ndarray | None = None) -> np.ndarray:
     """Values idx0 .. idx0+n-1 of stream (seed, layer, tensor).

@@ -59,6 +59,10 @@ struct ExpertArgs {
 int router_splits(int T, int H);
 int launch_router(const RouterArgs& a, hipStream_t st);
 int launch_prenorm(const float* h, int T, int H, uint16_t* xt, hipStream_t st);
+// bf16 routing + dispatch in one launch for T <= 64 (counter: zeroed int32,
+// left zeroed by the kernel)
+int launch_route_small(const RouterArgs& a, const DispatchArgs& d, int32_t* counter,
+                       hipStream_t st);
 int launch_dispatch(const DispatchArgs& a, hipStream_t st);
 
 // bf16 expert FFN, grouped MFMA GEMMs (many rows per expert)

@@ -35,7 +35,8 @@ struct moe_layer {
   int32_t* perm;      // [S]
   int32_t* inv;       // [S]
   void* act;          // [S][F] dtype
-  float* yp;          // [S][H]
+  float* yp;          // [2][S][H]
+  int32_t* sync;      // [1] zeroed completion counter of the fused small-batch router
 };
 
 namespace {
@@ -121,6 +122,7 @@ void carve(moe_layer* L, Arena& A) {
   L->act = arena_alloc(A, S * (size_t)d.ffn * L->esize);
   // two planes: the grouped down projection may split its K range in two
   L->yp = (float*)arena_alloc(A, 2 * S * (size_t)d.hidden * 4);
+  L->sync = (int32_t*)arena_alloc(A, 4);
 }
 
 // Keeps the layer's device current for the duration of a call.
@@ -149,6 +151,11 @@ bool use_stream_path(const moe_layer* L, int T) {
   return (int64_t)T * L->d.top_k <= 32 * (int64_t)L->d.num_experts;
 }
 
+// Routing and dispatch in one launch (bf16 layers, one token tile).
+bool small_route(const moe_layer* L, int T, const float* logits_in) {
+  return L->d.dtype == MOE_BF16 && !logits_in && T <= 64;
+}
+
 // Steps 1-3 into the workspace.  x_route is the routing input (bf16 branch
 // input or the layer input), or nullptr when logits_in is given.
 int run_route(moe_layer* L, const void* x_route, int T, const float* logits_in,
@@ -156,9 +163,10 @@ int run_route(moe_layer* L, const void* x_route, int T, const float* logits_in,
   const moe_layer_desc& d = L->d;
   RouterArgs ra{x_route, T, d.hidden, d.num_experts, d.top_k, d.dtype == MOE_F32 ? 1 : 0,
                 d.router_w, d.router_b, logits_in, L->idx, L->w, L->part};
-  if (launch_router(ra, st)) return MOE_ERR_DEVICE;
   DispatchArgs da{L->idx, T * d.top_k, d.num_experts, tile_rows, L->hist, L->rank, L->base,
                   L->counts, L->offsets, L->tile_off, L->active, L->perm, L->inv};
+  if (small_route(L, T, logits_in)) return launch_route_small(ra, da, L->sync, st) ? MOE_ERR_DEVICE : MOE_OK;
+  if (launch_router(ra, st)) return MOE_ERR_DEVICE;
   if (launch_dispatch(da, st)) return MOE_ERR_DEVICE;
   return MOE_OK;
 }
@@ -196,6 +204,15 @@ moe_layer_t* moe_layer_create(const moe_layer_desc* d, int* status) {
   }
   Arena real{(char*)L->ws, L->ws_bytes, 0};
   carve(L, real);
+  // the fused router's completion counter starts at zero and every launch
+  // leaves it at zero
+  if (hipMemset(L->sync, 0, 4) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(L->ws);
+    free(L);
+    if (status) *status = MOE_ERR_DEVICE;
+    return nullptr;
+  }
   if (status) *status = MOE_OK;
   return L;
 }
@@ -271,11 +288,16 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
     const moe_layer_desc& dd = L->d;
     RouterArgs ra{xin, T, dd.hidden, dd.num_experts, dd.top_k, f32 ? 1 : 0, dd.router_w,
                   dd.router_b, nullptr, L->idx, L->w, L->part};
-    if (launch_router(ra, st)) return MOE_ERR_DEVICE;
-    if (!mark(MOE_STAGE_DISPATCH)) return MOE_ERR_DEVICE;
     DispatchArgs da{L->idx, S, dd.num_experts, GG_BT, L->hist, L->rank, L->base, L->counts,
                     L->offsets, L->tile_off, L->active, L->perm, L->inv};
-    if (launch_dispatch(da, st)) return MOE_ERR_DEVICE;
+    if (small_route(L, T, nullptr)) {  // one launch: the dispatch stage is empty
+      if (launch_route_small(ra, da, L->sync, st)) return MOE_ERR_DEVICE;
+      if (!mark(MOE_STAGE_DISPATCH)) return MOE_ERR_DEVICE;
+    } else {
+      if (launch_router(ra, st)) return MOE_ERR_DEVICE;
+      if (!mark(MOE_STAGE_DISPATCH)) return MOE_ERR_DEVICE;
+      if (launch_dispatch(da, st)) return MOE_ERR_DEVICE;
+    }
   }
   ExpertArgs ea{};
   ea.x = xin;
@@ -303,12 +325,12 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
   int r1 = f32 ? launch_f32_gate_up(ea, st)
                : stream_path ? launch_stream_gate_up(ea, st) : launch_grouped_gate_up(ea, st);
   if (r1 || !mark(MOE_STAGE_DOWN)) return MOE_ERR_DEVICE;
+  const float* resid = prenorm ? (const float*)x : nullptr;
   const int planes = (f32 || stream_path) ? 1 : grouped_down_ksplit(ea);
   int r2 = f32 ? launch_f32_down(ea, st)
                : stream_path ? launch_stream_down(ea, st) : launch_grouped_down(ea, planes, st);
   if (r2 || !mark(MOE_STAGE_COMBINE)) return MOE_ERR_DEVICE;
-  if (launch_combine(L->yp, planes, L->w, L->inv, prenorm ? (const float*)x : nullptr, T,
-                     d.hidden, d.top_k, y, st))
+  if (launch_combine(L->yp, planes, L->w, L->inv, resid, T, d.hidden, d.top_k, y, st))
     return MOE_ERR_DEVICE;
   if (!mark(MOE_NUM_STAGES)) return MOE_ERR_DEVICE;
   return MOE_OK;

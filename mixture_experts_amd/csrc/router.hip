@@ -226,6 +226,148 @@ __global__ __launch_bounds__(256) void prenorm_kernel(const float* __restrict__ 
   for (int i = tid; i < H; i += 256) xt[(size_t)t * H + i] = f32_to_bf16(row[i] / r);
 }
 
+// Small batches (T <= 64, one token tile): routing and dispatch in one
+// launch.  Every workgroup computes the partial logits of its hidden slice;
+// the last one to finish (counted with a device-scope atomic after a
+// release fence) adds the slices in split order, selects the top-k of each
+// token, and builds counts / offsets / tile schedule / non-empty expert list
+// / perm / inv with the same ballot-ranked counting sort as the dispatch
+// kernels.  That workgroup resets the counter for the next launch.  The
+// result does not depend on which workgroup finishes last.
+template <int NT>
+__global__ __launch_bounds__(256) void route_small_kernel(
+    const uint16_t* __restrict__ x, int T, int H, int E, int k,
+    const uint16_t* __restrict__ wr, const float* __restrict__ bias, int hslice,
+    float* __restrict__ part, int32_t* __restrict__ counter, int tile_rows,
+    int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off,
+    int32_t* __restrict__ active, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  constexpr int EP = NT * 16;
+  constexpr int LDW = RT_HC + RT_PAD;
+  __shared__ __attribute__((aligned(16))) uint16_t wt[EP * LDW];
+  __shared__ float lg[RT_TOK * (EP + 1)];
+  __shared__ int32_t cnt[MOE_MAX_EXPERTS];
+  __shared__ int32_t off_l[MOE_MAX_EXPERTS + 1];
+  __shared__ int32_t rank_l[RT_TOK * MOE_MAX_TOPK];
+  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int split = blockIdx.x;
+  const int hb = split * hslice;
+
+  {  // partial logits of all T (<= 64) tokens over this hidden slice
+    f32x4 acc[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int my_tok = wave * 16 + (lane & 15);
+    const bool tok_ok = my_tok < T;
+    const uint16_t* xrow = x + (size_t)(tok_ok ? my_tok : 0) * H;
+    const int kq = (lane >> 4) * 8;
+    for (int h0 = hb; h0 < hb + hslice; h0 += RT_HC) {
+      u32x4 av[RT_HC / 32];
+#pragma unroll
+      for (int q = 0; q < RT_HC / 32; ++q)
+        av[q] = tok_ok ? ldg16(xrow + h0 + q * 32 + kq) : u32x4{0u, 0u, 0u, 0u};
+      __syncthreads();
+      for (int i = tid; i < RT_HC * EP; i += 256) {
+        const int r = i / EP, e = i % EP;
+        wt[e * LDW + r] = (e < E) ? wr[(size_t)(h0 + r) * E + e] : (uint16_t)0;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < RT_HC / 32; ++q) {
+        const bf16x8 a = as_bf16x8(av[q]);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const uint16_t* bp = wt + (n * 16 + (lane & 15)) * LDW + q * 32 + kq;
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              a, as_bf16x8(*reinterpret_cast<const u32x4*>(bp)), acc[n], 0, 0, 0);
+        }
+      }
+    }
+    float* out = part + (size_t)split * T * E;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int e = n * 16 + (lane & 15);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = wave * 16 + (lane >> 4) * 4 + j;
+        if (e < E && t < T) out[(size_t)t * E + e] = acc[n][j];
+      }
+    }
+  }
+  __threadfence();  // release this block's partials
+  __syncthreads();
+  if (tid == 0) s_last = (atomicAdd(counter, 1) == (int)gridDim.x - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();  // acquire every block's partials
+
+  const int ns = gridDim.x;
+  const int ldl = E + 1;
+  for (int i = tid; i < T * E; i += 256) {
+    const int t = i / E, e = i % E;
+    float s = part[(size_t)t * E + e];
+    for (int q = 1; q < ns; ++q) s += part[((size_t)q * T + t) * E + e];
+    if (bias) s += bias[e];
+    lg[t * ldl + e] = s;
+  }
+  __syncthreads();
+  topk_rows(lg, ldl, 0, T, E, k, idx_out, w_out);
+  __syncthreads();  // this block's idx writes are visible to the block
+
+  // dispatch of the S = T*k <= 512 slots (wave 0 ranks, everyone scatters)
+  const int S = T * k;
+  if (wave == 0) {
+    for (int e = lane; e < E; e += 64) cnt[e] = 0;
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int c = 0; c * 64 < S; ++c) {
+      const int sl = c * 64 + lane;
+      const bool valid = sl < S;
+      const int e = valid ? idx_out[sl] : 0;
+      uint64_t match = __ballot(valid);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        match &= bit ? m : ~m;
+      }
+      const uint64_t earlier = match & below;
+      const int c0 = valid ? cnt[e] : 0;
+      __builtin_amdgcn_wave_barrier();
+      if (valid) {
+        rank_l[sl] = c0 + __popcll(earlier);
+        if (earlier == 0) cnt[e] = c0 + __popcll(match);
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int o = 0, tt = 0, n = 0;
+    for (int e = 0; e < E; ++e) {
+      off_l[e] = o;
+      offsets[e] = o;
+      counts[e] = cnt[e];
+      tile_off[e] = tt;
+      o += cnt[e];
+      tt += (cnt[e] + tile_rows - 1) / tile_rows;
+      if (cnt[e] > 0) active[n++] = e;
+    }
+    off_l[E] = o;
+    offsets[E] = o;
+    tile_off[E] = tt;
+    active[E] = n;
+    *counter = 0;  // ready for the next launch
+  }
+  __syncthreads();
+  for (int sl = tid; sl < S; sl += 256) {
+    const int p = off_l[idx_out[sl]] + rank_l[sl];
+    perm[p] = sl;
+    inv[sl] = p;
+  }
+}
+
 }  // namespace
 
 int router_splits(int T, int H) {
@@ -269,6 +411,24 @@ int launch_router(const RouterArgs& a, hipStream_t st) {
   else
     router_partial_kernel<16><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, ww, hs, a.part);
   router_topk_kernel<<<grid, 256, 0, st>>>(a.part, ns, a.T, a.E, a.k, a.bias, a.idx, a.w);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_route_small(const RouterArgs& a, const DispatchArgs& d, int32_t* counter,
+                       hipStream_t st) {
+  const int ns = router_splits(a.T, a.H);
+  const int hs = a.H / ns;
+  const int nt = (a.E + 15) / 16;
+  auto* xx = (const uint16_t*)a.x;
+  auto* ww = (const uint16_t*)a.wr;
+#define RS_ARGS xx, a.T, a.H, a.E, a.k, ww, a.bias, hs, a.part, counter, d.tile_rows, a.idx, a.w, \
+                d.counts, d.offsets, d.tile_off, d.active, d.perm, d.inv
+  if (nt <= 1) route_small_kernel<1><<<ns, 256, 0, st>>>(RS_ARGS);
+  else if (nt <= 2) route_small_kernel<2><<<ns, 256, 0, st>>>(RS_ARGS);
+  else if (nt <= 4) route_small_kernel<4><<<ns, 256, 0, st>>>(RS_ARGS);
+  else if (nt <= 8) route_small_kernel<8><<<ns, 256, 0, st>>>(RS_ARGS);
+  else route_small_kernel<16><<<ns, 256, 0, st>>>(RS_ARGS);
+#undef RS_ARGS
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
