@@ -37,7 +37,10 @@ __device__ __forceinline__ u32x4 ldg16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+// SiLU with the hardware reciprocal (about 1 ulp); -0 for very negative g
+__device__ __forceinline__ float silu_f32(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
 
 // The chip has 8 XCDs, each with its own L2; consecutive workgroup ids are
 // dealt round-robin over them.  Renumber so that blocks sharing data (same

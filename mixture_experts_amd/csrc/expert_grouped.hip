@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const float g = acc[i][j][4 * q + jj];
-            o[jj] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * acc[i + 2][j][4 * q + jj];
+            o[jj] = silu_f32(g) * acc[i + 2][j][4 * q + jj];
           }
           const bf16x2 lo = {(__bf16)o[0], (__bf16)o[1]}, hi = {(__bf16)o[2], (__bf16)o[3]};
           uint2 pk;

@@ -1,168 +1,324 @@
 // expert_stream.hip -- steps 4 and 5 when each expert sees few rows (decode
 // batches, many small experts): the weights of every expert that received at
-// least one row are streamed from HBM exactly once, straight into registers.
+// least one row are streamed from HBM exactly once.
 //
 // Same SwiGLU expert as the grouped path [zskr.cn/news/2275853
 // "Colibri：面向MoE架构的C语言高效推理引擎解析" sec. 3.1, sec. 3.3 stage 4];
 // experts are addressed as base + id * stride inside one contiguous buffer
 // [www.lmnt.cn/news/246575 sec. 2.1].
 //
-// Work unit: one non-empty expert x 16 weight rows (gate AND up rows f0..f0+15
-// for the first kernel; down rows h0..h0+15 for the second), all of the
-// expert's token rows in passes of NB*16.  The 4 waves split the K dimension;
-// lanes load 16 bytes each, four lanes covering 64 contiguous bytes of a row
-// per instruction, with 8 (gate: 16) loads per lane in flight per batch of 8
-// MFMA steps; the token rows (L2-resident) use the same lane -> K mapping.  MFMA:
-// v_mfma_f32_16x16x32_bf16 with weight rows as A and tokens as B.  The four
-// K partial sums are added in LDS in a fixed order (deterministic), then the
-// gate/up kernel applies SiLU(g)*u and stores the activation in bf16; the
-// down kernel stores fp32 rows for the fixed-order combine.
+// Work item: one non-empty expert x 16 output rows (gate AND up rows
+// f0..f0+15 for the first kernel, 32 weight rows; down rows h0..h0+15 for the
+// second), over all of the expert's token rows in passes of TR.  The grid is
+// persistent: workgroup b takes items b, b + G, b + 2G, ... and treats the
+// K chunks of all its items as one sequence.  A chunk is CK (256, or 128
+// when K is not a multiple of 256) K elements: the 2 CK-byte run of every
+// weight row and of every token row of the pass.  It reaches LDS through
+// direct global->LDS loads, weight rows as non-temporal 1 KB loads of
+// 1024 / (2 CK) row runs each; a ring of NS chunk stages keeps NS-1
+// chunks in flight, across item boundaries, so HBM sees long runs and never
+// waits for an item's epilogue.  MFMA v_mfma_f32_16x16x32_bf16 with weight
+// rows as A and token rows as B; each of the 4 waves takes a quarter of the
+// 32-wide K steps of a chunk, and the four partial sums are added in LDS in
+// a fixed order (deterministic) before the gate/up epilogue applies SiLU(g)*u
+// and stores bf16, or the down epilogue stores fp32 rows for the combine.
 #include "common.h"
 #include "kernels.h"
 
 namespace {
 
-__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+#define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0f70)
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <bool GATED, int NB>
+// One LDS row run holds CK/8 chunks of 16 bytes; chunk c of run r sits at
+// slot c ^ (r % 16), so the 16 lanes of an MFMA operand read (16 runs, one
+// chunk) hit 16 distinct bank groups.
+__device__ __forceinline__ int run_slot(int r, int c) { return c ^ (r & 15); }
+
+template <bool GATED, int TR, int NS, int CK>
 __global__ __launch_bounds__(256) void stream_kernel(
     const uint16_t* __restrict__ experts, uint64_t stride_elems,
     const uint16_t* __restrict__ tok, const int32_t* __restrict__ perm, int k_top,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ active, int E, int H,
     int F, int T, void* __restrict__ out) {
-  constexpr int NA = GATED ? 2 : 1;
+  constexpr int NA = GATED ? 2 : 1;   // weight row blocks of 16 (gate, up)
+  constexpr int WR = 16 * NA;         // weight rows per item
+  constexpr int NB = (TR + 15) / 16;  // token column blocks of the MFMA
+  constexpr int RB = 2 * CK;          // bytes per row run
+  constexpr int SPR = CK / 8;         // 16-byte slots per run
+  constexpr int RPI = 64 / SPR;       // runs per 1 KB load
+  constexpr int IW = WR / RPI / 4;    // weight loads per wave per chunk
+  constexpr int IT = TR / RPI / 4;    // token loads per wave per chunk
+  constexpr int KSW = CK / 32 / 4;    // 32-wide K steps per wave per chunk
+  constexpr int STAGE = (WR + TR) * RB;
+  static_assert((CK == 128 || CK == 256) && IT >= 1 && TR % (4 * RPI) == 0,
+                "chunk width and token rows per pass");
+  static_assert(NS >= 2 && NS <= 4, "ring depth");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NS][STAGE];
   __shared__ f32x4 red[4][NA * NB][64];
 
   const int K = GATED ? H : F;
   const int NWT = (GATED ? F : H) / 16;
-  const int slot = blockIdx.x / NWT;
-  const int wt = blockIdx.x - slot * NWT;
-  if (slot >= active[E]) return;
-  const int e = active[slot];
-  const int p_beg = offsets[e];
-  const int n_e = offsets[e + 1] - p_beg;
+  const int NC = K / CK;
+  const int n_items = active[E] * NWT;
+  const int G = gridDim.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // ---- the load cursor: (item j of this workgroup, token pass, chunk) ----
+  int l_j = 0, l_pass = 0, l_c = 0, l_npass = 0;
+  bool l_ok = false;
+  const uint16_t* wsrc[IW];
+  const uint16_t* tsrc[IT];
+  auto l_item = [&]() {  // sets l_ok, l_npass and the weight sources for item l_j
+    const int item = blockIdx.x + l_j * G;
+    l_ok = item < n_items;
+    if (!l_ok) return;
+    const int slot = item / NWT, wt = item - slot * NWT;
+    const int e = active[slot];
+    const int n_e = offsets[e + 1] - offsets[e];
+    l_npass = (n_e + TR - 1) / TR;
+    const uint16_t* eb = experts + (size_t)stride_elems * e;
+#pragma unroll
+    for (int i = 0; i < IW; ++i) {
+      const int r = (wave * IW + i) * RPI + lane / SPR;  // weight row of the item
+      const uint16_t* row;
+      if (GATED)
+        row = eb + (size_t)(r < 16 ? 0 : F) * H + (size_t)(wt * 16 + (r & 15)) * H;
+      else
+        row = eb + 2 * (size_t)F * H + (size_t)(wt * 16 + r) * F;
+      wsrc[i] = row + run_slot(r, lane % SPR) * 8;
+    }
+  };
+  // token sources of pass l_pass of item l_j.  Each load covers RPI token
+  // rows; their indices are read with scalar loads (uniform addresses), so
+  // no vector load the compiler would have to wait for joins the loads in
+  // flight.
+  auto l_pass_rows = [&]() {
+    const int item = blockIdx.x + l_j * G;
+    const int e = active[item / NWT];
+    const int p_beg = offsets[e], n_e = offsets[e + 1] - p_beg;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int r0 = (wave * IT + i) * RPI;  // token rows r0 .. r0 + RPI - 1 of the pass
+      int xr = 0;
+#pragma unroll
+      for (int u = 0; u < RPI; ++u) {
+        const int p = p_beg + min(l_pass * TR + r0 + u, n_e - 1);
+        const int x = GATED ? min(max(perm[p], 0) / k_top, T - 1) : p;
+        if (lane / SPR == u) xr = x;
+      }
+      tsrc[i] = tok + (size_t)xr * K + run_slot(r0 + lane / SPR, lane % SPR) * 8;
+    }
+  };
+  // issue the chunk under the load cursor into stage st, then advance it
+  auto l_issue = [&](int st) {
+    const uint32_t base =
+        (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)&ring[st][0]);
+    const int k0 = l_c * CK;
+#pragma unroll
+    for (int i = 0; i < IW; ++i) {
+      const uint32_t dst = base + (uint32_t)((wave * IW + i) * RPI * RB);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+                   :
+                   : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(wsrc[i] + k0)
+                   : "memory", "m0");
+    }
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const uint32_t dst = base + (uint32_t)((WR + (wave * IT + i) * RPI) * RB);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                   :
+                   : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(tsrc[i] + k0)
+                   : "memory", "m0");
+    }
+    if (++l_c == NC) {
+      l_c = 0;
+      if (++l_pass == l_npass) {
+        l_pass = 0;
+        ++l_j;
+        l_item();
+      }
+      if (l_ok) l_pass_rows();
+    }
+  };
+
+  // ---- the compute cursor ----
+  int c_j = 0, c_pass = 0, c_c = 0;
+  int c_wt = 0, c_pbeg = 0, c_ne = 0, c_npass = 0;
+  bool c_ok = false;
+  auto c_item = [&]() {
+    const int item = blockIdx.x + c_j * G;
+    c_ok = item < n_items;
+    if (!c_ok) return;
+    const int slot = item / NWT;
+    c_wt = item - slot * NWT;
+    const int e = active[slot];
+    c_pbeg = offsets[e];
+    c_ne = offsets[e + 1] - c_pbeg;
+    c_npass = (c_ne + TR - 1) / TR;
+  };
+
+  l_item();
+  if (l_ok) l_pass_rows();
+  c_item();
+  // prologue: chunks 0 .. NS-2 of the sequence
+  int ahead = 0;  // chunks issued and not yet computed
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (l_ok) {
+      l_issue(s);
+      ++ahead;
+    }
+
+  f32x4 acc[NA][NB];
+#pragma unroll
+  for (int i = 0; i < NA; ++i)
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[i][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int r16 = lane & 15, kg = lane >> 4;
-  const uint16_t* eb = experts + (size_t)e * stride_elems;
-  const uint16_t* wa;
-  const uint16_t* wu = nullptr;
-  if (GATED) {
-    wa = eb + (size_t)(wt * 16 + r16) * H;
-    wu = eb + (size_t)F * H + (size_t)(wt * 16 + r16) * H;
-  } else {
-    wa = eb + 2 * (size_t)F * H + (size_t)(wt * 16 + r16) * F;
-  }
-  const int nsteps = K / 32;
-  const int s_beg = wave * nsteps / 4, s_end = (wave + 1) * nsteps / 4;
 
-  for (int pass0 = 0; pass0 < n_e; pass0 += NB * 16) {
-    f32x4 acc[NA][NB];
-#pragma unroll
-    for (int i = 0; i < NA; ++i)
-#pragma unroll
-      for (int n = 0; n < NB; ++n) acc[i][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint16_t* brow[NB];
-    bool bok[NB];
-#pragma unroll
-    for (int n = 0; n < NB; ++n) {
-      const int t = pass0 + n * 16 + r16;
-      bok[n] = t < n_e;
-      const int p = p_beg + (bok[n] ? t : 0);
-      brow[n] = GATED ? tok + (size_t)min(max(perm[p], 0) / k_top, T - 1) * H : tok + (size_t)p * F;
+  int st = 0;  // stage of the chunk being computed
+  while (c_ok) {
+    // this wave's loads of the current chunk have landed once at most the
+    // loads of the (ahead - 1) younger chunks are outstanding
+    constexpr int PER = IW + IT;
+    if (ahead >= 3) WAIT_VMCNT(2 * PER);
+    else if (ahead == 2) WAIT_VMCNT(PER);
+    else WAIT_VMCNT(0);
+    // publishes the chunk, and ends every wave's reads of the previous one
+    asm volatile("s_barrier" ::: "memory");
+    --ahead;
+    if (l_ok) {
+      l_issue(st == 0 ? NS - 1 : st - 1);  // the previous chunk's stage
+      ++ahead;
     }
-    // MFMA step s covers k in [32 s, 32 s + 32); lane group kg holds
-    // k = 32 s + 8 kg .. +7, so one load instruction reads 64 contiguous
-    // bytes of each of the 16 rows.  Steps go in batches of 8 so that 8 (or
-    // 16) weight loads per lane are in flight before the first MFMA.
-    int s = s_beg;
-    for (; s + 8 <= s_end; s += 8) {
-      u32x4 va[8], vu[8];
+    // K steps KSW wave .. KSW wave + KSW - 1 of the chunk
+    const uint8_t* sb = &ring[st][0];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int kb = (s + q) * 32 + kg * 8;
-        va[q] = ldg16(wa + kb);
-        if (GATED) vu[q] = ldg16(wu + kb);
+    for (int s2 = 0; s2 < KSW; ++s2) {
+      const int c = (wave * KSW + s2) * 4 + kg;  // 16-byte chunk of the run
+      bf16x8 a[NA], b[NB];
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        const int r = i * 16 + r16;
+        a[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(sb + r * RB + run_slot(r, c) * 16));
       }
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
-        u32x4 vb[8];
+        // token columns beyond TR read row 0 again; their results are dropped
+        const int r = n * 16 + r16 < TR ? n * 16 + r16 : 0;
+        b[n] = as_bf16x8(
+            *reinterpret_cast<const u32x4*>(sb + (WR + r) * RB + run_slot(r, c) * 16));
+      }
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-          vb[q] = bok[n] ? ldg16(brow[n] + (s + q) * 32 + kg * 8) : u32x4{0u, 0u, 0u, 0u};
+      for (int n = 0; n < NB; ++n)
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          acc[0][n] = mfma16(va[q], vb[q], acc[0][n]);
-          if (GATED) acc[NA - 1][n] = mfma16(vu[q], vb[q], acc[NA - 1][n]);
+        for (int i = 0; i < NA; ++i) acc[i][n] = mfma16(a[i], b[n], acc[i][n]);
+    }
+    st = st == NS - 1 ? 0 : st + 1;
+
+    if (++c_c == NC) {  // end of a token pass: reduce the 4 K partial sums
+      c_c = 0;
+#pragma unroll
+      for (int i = 0; i < NA; ++i)
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          red[wave][i * NB + n][lane] = acc[i][n];
+          acc[i][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      // LDS writes done, then the barrier; no wait on the loads in flight
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      // 16x16 accumulator layout: lane l holds token column l%16 and weight
+      // rows 4*(l/16) + j.  Thread (n, l) sums the waves' partials in order.
+      if (threadIdx.x < NB * 64) {
+        const int n = threadIdx.x >> 6, l = threadIdx.x & 63;
+        const int col = n * 16 + (l & 15);
+        const int t = c_pass * TR + col;
+        if (col < TR && t < c_ne) {
+          const int p = c_pbeg + t;
+          const int r0 = c_wt * 16 + 4 * (l >> 4);
+          f32x4 g = red[0][n][l];
+          g += red[1][n][l];
+          g += red[2][n][l];
+          g += red[3][n][l];
+          if (GATED) {
+            f32x4 u = red[0][NB + n][l];
+            u += red[1][NB + n][l];
+            u += red[2][NB + n][l];
+            u += red[3][NB + n][l];
+            const bf16x2 lo = {(__bf16)(silu_f32(g[0]) * u[0]), (__bf16)(silu_f32(g[1]) * u[1])};
+            const bf16x2 hi = {(__bf16)(silu_f32(g[2]) * u[2]), (__bf16)(silu_f32(g[3]) * u[3])};
+            uint2 pk;
+            pk.x = __builtin_bit_cast(uint32_t, lo);
+            pk.y = __builtin_bit_cast(uint32_t, hi);
+            *reinterpret_cast<uint2*>((uint16_t*)out + (size_t)p * F + r0) = pk;
+          } else {
+            *reinterpret_cast<f32x4*>((float*)out + (size_t)p * H + r0) = g;
+          }
         }
       }
-    }
-    for (; s < s_end; ++s) {
-      const int kb = s * 32 + kg * 8;
-      const u32x4 va = ldg16(wa + kb);
-      u32x4 vu = u32x4{0u, 0u, 0u, 0u};
-      if (GATED) vu = ldg16(wu + kb);
-#pragma unroll
-      for (int n = 0; n < NB; ++n) {
-        const u32x4 vb = bok[n] ? ldg16(brow[n] + kb) : u32x4{0u, 0u, 0u, 0u};
-        acc[0][n] = mfma16(va, vb, acc[0][n]);
-        if (GATED) acc[NA - 1][n] = mfma16(vu, vb, acc[NA - 1][n]);
+      // red is written again only after at least one more chunk barrier
+      if (++c_pass == c_npass) {
+        c_pass = 0;
+        ++c_j;
+        c_item();
       }
     }
-#pragma unroll
-    for (int i = 0; i < NA; ++i)
-#pragma unroll
-      for (int n = 0; n < NB; ++n) red[wave][i * NB + n][lane] = acc[i][n];
-    __syncthreads();
-    // 16x16 accumulator layout: lane l holds token column l%16 and weight
-    // rows 4*(l/16) + j.  Thread (n, l) sums the four K quarters in order.
-    if (tid < NB * 64) {
-      const int n = tid >> 6, l = tid & 63;
-      const int t = pass0 + n * 16 + (l & 15);
-      if (t < n_e) {
-        const int p = p_beg + t;
-        const int r0 = wt * 16 + 4 * (l >> 4);
-        f32x4 g = red[0][n][l];
-        g += red[1][n][l];
-        g += red[2][n][l];
-        g += red[3][n][l];
-        if (GATED) {
-          f32x4 u = red[0][NB + n][l];
-          u += red[1][NB + n][l];
-          u += red[2][NB + n][l];
-          u += red[3][NB + n][l];
-          uint2 pk;
-          pk.x = pack_bf16x2(silu_f32(g[0]) * u[0], silu_f32(g[1]) * u[1]);
-          pk.y = pack_bf16x2(silu_f32(g[2]) * u[2], silu_f32(g[3]) * u[3]);
-          *reinterpret_cast<uint2*>((uint16_t*)out + (size_t)p * F + r0) = pk;
-        } else {
-          *reinterpret_cast<f32x4*>((float*)out + (size_t)p * H + r0) = g;
-        }
-      }
-    }
-    __syncthreads();
   }
+  WAIT_VMCNT(0);
+}
+
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <bool GATED, int TR, int NS, int CK>
+int launch_tr(const ExpertArgs& a, hipStream_t st) {
+  constexpr int NA = GATED ? 2 : 1, NB = (TR + 15) / 16;
+  constexpr int lds = NS * (16 * NA + TR) * 2 * CK + 4 * NA * NB * 64 * 16;
+  const int per_cu = (160 * 1024) / lds;
+  const int nwt = (GATED ? a.F : a.H) / 16;
+  const int slots = a.E < a.S ? a.E : a.S;
+  int grid = cu_count() * (per_cu < 1 ? 1 : per_cu);
+  if (grid > nwt * slots) grid = nwt * slots;
+  const uint16_t* tok = GATED ? (const uint16_t*)a.x : (const uint16_t*)a.act;
+  void* out = GATED ? a.act : (void*)a.yp;
+  stream_kernel<GATED, TR, NS, CK><<<grid, 256, 0, st>>>(
+      (const uint16_t*)a.experts, a.stride_elems, tok, a.perm, a.k, a.offsets, a.active, a.E,
+      a.H, a.F, a.T, out);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 template <bool GATED>
 int launch_stream(const ExpertArgs& a, hipStream_t st) {
-  const int nwt = (GATED ? a.F : a.H) / 16;
-  const int slots = a.E < a.S ? a.E : a.S;
-  const int grid = nwt * slots;
-  // token passes of NB*16 rows; experts with more rows take several passes
+  // token rows per pass (experts with more rows take several passes) and the
+  // chunk width: 256 when K allows it (bf16 layers have H % 256 == 0 and
+  // F % 128 == 0), else 128
   const int rows = a.rows_hint;
-  const uint16_t* tok = GATED ? (const uint16_t*)a.x : (const uint16_t*)a.act;
-  void* out = GATED ? a.act : (void*)a.yp;
-  auto* ex = (const uint16_t*)a.experts;
-  if (rows <= 16)
-    stream_kernel<GATED, 1><<<grid, 256, 0, st>>>(ex, a.stride_elems, tok, a.perm, a.k, a.offsets, a.active, a.E, a.H, a.F, a.T, out);
-  else if (rows <= 32)
-    stream_kernel<GATED, 2><<<grid, 256, 0, st>>>(ex, a.stride_elems, tok, a.perm, a.k, a.offsets, a.active, a.E, a.H, a.F, a.T, out);
-  else
-    stream_kernel<GATED, 4><<<grid, 256, 0, st>>>(ex, a.stride_elems, tok, a.perm, a.k, a.offsets, a.active, a.E, a.H, a.F, a.T, out);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  const int K = GATED ? a.H : a.F;
+  if (K % 256 == 0) {
+    if (rows <= 8) return launch_tr<GATED, 8, GATED ? 3 : 4, 256>(a, st);
+    if (rows <= 16) return launch_tr<GATED, 16, GATED ? 3 : 4, 256>(a, st);
+    return launch_tr<GATED, 32, GATED ? 2 : 3, 256>(a, st);
+  }
+  if (rows <= 16) return launch_tr<GATED, 16, 4, 128>(a, st);
+  return launch_tr<GATED, 32, GATED ? 3 : 4, 128>(a, st);
 }
 
 }  // namespace
