@@ -37,13 +37,15 @@ __device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
   return a.v > b.v || (a.v == b.v && a.e < b.e);
 }
 
-// Top-k + softmax of tokens tile0 + wave, tile0 + wave + 4, ... (16 per
-// wave, interleaved so that small batches still spread over the 4 waves).
-// lg: LDS logits [RT_TOK][ldl].
+// Top-k + softmax of tokens tile0 + wave, tile0 + wave + nwaves, ...
+// (interleaved so that small batches still spread over the waves).
+// lg: LDS logits [RT_TOK][ldl].  idx_lds (optional): an LDS copy of the
+// picks of the tile, [RT_TOK][k].
 __device__ void topk_rows(const float* lg, int ldl, int tile0, int T, int E, int k,
-                          int32_t* idx_out, float* w_out) {
+                          int32_t* idx_out, float* w_out, int nwaves = 4,
+                          int32_t* idx_lds = nullptr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int r = wave; r < RT_TOK; r += 4) {
+  for (int r = wave; r < RT_TOK; r += nwaves) {
     const int t = tile0 + r;
     if (t >= T) break;
     const float* row = lg + (size_t)r * ldl;
@@ -92,7 +94,68 @@ __device__ void topk_rows(const float* lg, int ldl, int tile0, int T, int E, int
     if (lane < k) {
       idx_out[(size_t)t * k + lane] = ej;
       w_out[(size_t)t * k + lane] = (float)(num / z);
+      if (idx_lds) idx_lds[r * k + lane] = ej;
     }
+  }
+}
+
+// Dispatch of S = T*k <= RT_TOK*8 slots whose expert ids are in LDS
+// (idx_lds[S]): wave 0 ranks the slots of each expert with ballot matches
+// in slot order, one thread scans the counts, every thread scatters.  Same
+// stable counting sort as the dispatch kernels.  cnt, off_l, rank_l: LDS.
+__device__ void dispatch_small(const int32_t* idx_lds, int S, int E, int tile_rows,
+                               int32_t* cnt, int32_t* off_l, int32_t* rank_l,
+                               int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                               int32_t* __restrict__ tile_off, int32_t* __restrict__ active,
+                               int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (wave == 0) {
+    for (int e = lane; e < E; e += 64) cnt[e] = 0;
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int c = 0; c * 64 < S; ++c) {
+      const int sl = c * 64 + lane;
+      const bool valid = sl < S;
+      const int e = valid ? idx_lds[sl] : 0;
+      uint64_t match = __ballot(valid);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        match &= bit ? m : ~m;
+      }
+      const uint64_t earlier = match & below;
+      const int c0 = valid ? cnt[e] : 0;
+      __builtin_amdgcn_wave_barrier();
+      if (valid) {
+        rank_l[sl] = c0 + __popcll(earlier);
+        if (earlier == 0) cnt[e] = c0 + __popcll(match);
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int o = 0, tt = 0, n = 0;
+    for (int e = 0; e < E; ++e) {
+      off_l[e] = o;
+      offsets[e] = o;
+      counts[e] = cnt[e];
+      tile_off[e] = tt;
+      o += cnt[e];
+      tt += (cnt[e] + tile_rows - 1) / tile_rows;
+      if (cnt[e] > 0) active[n++] = e;
+    }
+    off_l[E] = o;
+    offsets[E] = o;
+    tile_off[E] = tt;
+    active[E] = n;
+  }
+  __syncthreads();
+  for (int sl = tid; sl < S; sl += blockDim.x) {
+    const int p = off_l[idx_lds[sl]] + rank_l[sl];
+    perm[p] = sl;
+    inv[sl] = p;
   }
 }
 
@@ -249,6 +312,7 @@ __global__ __launch_bounds__(256) void route_small_kernel(
   __shared__ int32_t cnt[MOE_MAX_EXPERTS];
   __shared__ int32_t off_l[MOE_MAX_EXPERTS + 1];
   __shared__ int32_t rank_l[RT_TOK * MOE_MAX_TOPK];
+  __shared__ int32_t idx_l[RT_TOK * MOE_MAX_TOPK];
   __shared__ int s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x;
@@ -312,60 +376,125 @@ __global__ __launch_bounds__(256) void route_small_kernel(
     lg[t * ldl + e] = s;
   }
   __syncthreads();
-  topk_rows(lg, ldl, 0, T, E, k, idx_out, w_out);
-  __syncthreads();  // this block's idx writes are visible to the block
+  topk_rows(lg, ldl, 0, T, E, k, idx_out, w_out, 4, idx_l);
+  __syncthreads();
+  if (tid == 0) *counter = 0;  // ready for the next launch
+  dispatch_small(idx_l, T * k, E, tile_rows, cnt, off_l, rank_l, counts, offsets, tile_off,
+                 active, perm, inv);
+}
 
-  // dispatch of the S = T*k <= 512 slots (wave 0 ranks, everyone scatters)
-  const int S = T * k;
-  if (wave == 0) {
-    for (int e = lane; e < E; e += 64) cnt[e] = 0;
-    int nbits = 0;
-    while ((1 << nbits) < E) ++nbits;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int c = 0; c * 64 < S; ++c) {
-      const int sl = c * 64 + lane;
-      const bool valid = sl < S;
-      const int e = valid ? idx_out[sl] : 0;
-      uint64_t match = __ballot(valid);
-      for (int b = 0; b < nbits; ++b) {
-        const bool bit = (e >> b) & 1;
-        const uint64_t m = __ballot(bit);
-        match &= bit ? m : ~m;
+// Small batches with few experts (T <= 64, E <= 16, H <= 4096, H a multiple
+// of 512): routing and dispatch in one workgroup of 16 waves, no device-scope
+// synchronisation.  The router is staged transposed in LDS ([e][h], padded
+// rows), wave w takes the hidden slice [w H/16, (w+1) H/16) for all tokens
+// (tokens as the A operand, read from global memory), the 16 partial logit
+// tiles are added in wave order (+ bias), then top-k and the dispatch.
+constexpr int R1_HMAX = 4096;
+constexpr int R1_LDW = R1_HMAX + 8;  // padded router row (bf16)
+template <int MB, int EV>
+__global__ __launch_bounds__(1024) void route_one_kernel(
+    const uint16_t* __restrict__ x, int T, int H, int E, int k,
+    const uint16_t* __restrict__ wr, const float* __restrict__ bias, int tile_rows,
+    int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off,
+    int32_t* __restrict__ active, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  // the staged router, later the 16 partial logit tiles [16][RT_TOK][17]
+  __shared__ __attribute__((aligned(16))) uint16_t wt[16 * R1_LDW];
+  __shared__ float lg[RT_TOK * 17];
+  __shared__ int32_t idx_l[RT_TOK * MOE_MAX_TOPK];
+  __shared__ int32_t cnt[16];
+  __shared__ int32_t off_l[17];
+  __shared__ int32_t rank_l[RT_TOK * MOE_MAX_TOPK];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, kg = lane >> 4;
+
+  // The loads come first, all in flight together: this wave's token
+  // fragments of the first two token blocks, then the router rows.
+  const int hw = H / 16, hb = wave * hw, nks = hw / 32;  // nks <= 8
+  constexpr int KS = R1_HMAX / 16 / 32;
+  u32x4 xa[2][KS];
+  auto load_x = [&](int m0) {
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      const uint16_t* xr = x + (size_t)min((m0 + mm) * 16 + r16, T - 1) * H + hb + kg * 8;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        if (m0 + mm < MB && s < nks) xa[mm][s] = ldg16(xr + s * 32);
+    }
+  };
+  load_x(0);
+  // stage Wr^T: thread h reads router rows h, h + 1024, ... (E bf16 each;
+  // EV = 8 or 16: E is that, and a row is one or two 16-byte loads)
+  constexpr int RPT = R1_HMAX / 1024;
+  if (EV > 0) {
+    u32x4 wv[RPT][EV / 8];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int h = min(tid + i * 1024, H - 1);
+#pragma unroll
+      for (int q = 0; q < EV / 8; ++q) wv[i][q] = ldg16(wr + (size_t)h * EV + q * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int h = tid + i * 1024;
+      if (h < H) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          wt[e * R1_LDW + h] = e < EV ? (uint16_t)(wv[i][e >> 3][(e & 7) >> 1] >> (16 * (e & 1)))
+                                      : (uint16_t)0;
       }
-      const uint64_t earlier = match & below;
-      const int c0 = valid ? cnt[e] : 0;
-      __builtin_amdgcn_wave_barrier();
-      if (valid) {
-        rank_l[sl] = c0 + __popcll(earlier);
-        if (earlier == 0) cnt[e] = c0 + __popcll(match);
-      }
-      __builtin_amdgcn_wave_barrier();
+    }
+  } else {
+    for (int h = tid; h < H; h += 1024) {
+      uint16_t wv[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) wv[e] = e < E ? wr[(size_t)h * E + e] : (uint16_t)0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) wt[e * R1_LDW + h] = wv[e];
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    int o = 0, tt = 0, n = 0;
-    for (int e = 0; e < E; ++e) {
-      off_l[e] = o;
-      offsets[e] = o;
-      counts[e] = cnt[e];
-      tile_off[e] = tt;
-      o += cnt[e];
-      tt += (cnt[e] + tile_rows - 1) / tile_rows;
-      if (cnt[e] > 0) active[n++] = e;
+
+  f32x4 acc[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m0 = 0; m0 < MB; m0 += 2) {
+    if (m0 > 0) load_x(m0);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if (s >= nks) break;
+      const bf16x8 b =
+          as_bf16x8(*reinterpret_cast<const u32x4*>(wt + r16 * R1_LDW + hb + s * 32 + kg * 8));
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm)
+        if (m0 + mm < MB)
+          acc[m0 + mm] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(xa[mm][s]), b, acc[m0 + mm], 0, 0, 0);
     }
-    off_l[E] = o;
-    offsets[E] = o;
-    tile_off[E] = tt;
-    active[E] = n;
-    *counter = 0;  // ready for the next launch
+  }
+  __syncthreads();  // every wave is done with the staged router
+  // 16x16 layout: lane l holds expert column l%16 and token rows 4(l/16)+j
+  float* part = reinterpret_cast<float*>(wt);
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      part[(wave * RT_TOK + m * 16 + 4 * kg + j) * 17 + r16] = acc[m][j];
+  __syncthreads();
+  for (int i = tid; i < T * E; i += 1024) {
+    const int t = i / E, e = i - t * E;
+    float s = part[t * 17 + e];
+    for (int w = 1; w < 16; ++w) s += part[(w * RT_TOK + t) * 17 + e];
+    if (bias) s += bias[e];
+    lg[t * 17 + e] = s;
   }
   __syncthreads();
-  for (int sl = tid; sl < S; sl += 256) {
-    const int p = off_l[idx_out[sl]] + rank_l[sl];
-    perm[p] = sl;
-    inv[sl] = p;
-  }
+  topk_rows(lg, 17, 0, T, E, k, idx_out, w_out, 16, idx_l);
+  __syncthreads();
+  dispatch_small(idx_l, T * k, E, tile_rows, cnt, off_l, rank_l, counts, offsets, tile_off,
+                 active, perm, inv);
 }
 
 }  // namespace
@@ -416,6 +545,23 @@ int launch_router(const RouterArgs& a, hipStream_t st) {
 
 int launch_route_small(const RouterArgs& a, const DispatchArgs& d, int32_t* counter,
                        hipStream_t st) {
+  if (a.E <= 16 && a.H <= R1_HMAX && a.H % 512 == 0 && a.T <= RT_TOK) {
+    auto* xx = (const uint16_t*)a.x;
+    auto* ww = (const uint16_t*)a.wr;
+#define R1_ARGS xx, a.T, a.H, a.E, a.k, ww, a.bias, d.tile_rows, a.idx, a.w, d.counts, \
+                d.offsets, d.tile_off, d.active, d.perm, d.inv
+    const int mb = (a.T + 15) / 16;
+#define R1_MB(EV)                                                         \
+    if (mb <= 1) route_one_kernel<1, EV><<<1, 1024, 0, st>>>(R1_ARGS);    \
+    else if (mb <= 2) route_one_kernel<2, EV><<<1, 1024, 0, st>>>(R1_ARGS); \
+    else route_one_kernel<4, EV><<<1, 1024, 0, st>>>(R1_ARGS);
+    if (a.E == 8) { R1_MB(8) }
+    else if (a.E == 16) { R1_MB(16) }
+    else { R1_MB(0) }
+#undef R1_MB
+#undef R1_ARGS
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   const int ns = router_splits(a.T, a.H);
   const int hs = a.H / ns;
   const int nt = (a.E + 15) / 16;
