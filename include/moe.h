@@ -136,7 +136,10 @@ int moe_forward(moe_layer_t* L, const void* x, int32_t T, float* y, void* stream
  *   MOE_STAGE_DISPATCH histogram, scan, scatter
  *   MOE_STAGE_GATE_UP  gate/up projections + SiLU (one kernel)
  *   MOE_STAGE_DOWN     down projection (one kernel)
- *   MOE_STAGE_COMBINE  weighted combine (+ residual) (one kernel) */
+ *   MOE_STAGE_COMBINE  weighted combine (+ residual) (one kernel)
+ * For bf16 layers with T <= 64 routing and dispatch run as one kernel inside
+ * MOE_STAGE_ROUTE, and MOE_STAGE_DISPATCH is empty (its two events are
+ * recorded back to back; their distance is event overhead only). */
 enum {
   MOE_STAGE_ROUTE = 0,
   MOE_STAGE_DISPATCH = 1,
