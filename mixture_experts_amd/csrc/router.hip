@@ -37,15 +37,15 @@ __device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
   return a.v > b.v || (a.v == b.v && a.e < b.e);
 }
 
-// Top-k + softmax of tokens tile0 + wave, tile0 + wave + nwaves, ...
-// (interleaved so that small batches still spread over the waves).
-// lg: LDS logits [RT_TOK][ldl].  idx_lds (optional): an LDS copy of the
+// Top-k + softmax of tokens tile0 + wave, tile0 + wave + nwaves, ... below
+// tile0 + rows (interleaved so that small batches still spread over the
+// waves).  lg: LDS logits [rows][ldl].  idx_lds (optional): an LDS copy of the
 // picks of the tile, [RT_TOK][k].
 __device__ void topk_rows(const float* lg, int ldl, int tile0, int T, int E, int k,
                           int32_t* idx_out, float* w_out, int nwaves = 4,
-                          int32_t* idx_lds = nullptr) {
+                          int32_t* idx_lds = nullptr, int rows = RT_TOK) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int r = wave; r < RT_TOK; r += nwaves) {
+  for (int r = wave; r < rows; r += nwaves) {
     const int t = tile0 + r;
     if (t >= T) break;
     const float* row = lg + (size_t)r * ldl;
@@ -161,19 +161,24 @@ __device__ void dispatch_small(const int32_t* idx_lds, int S, int E, int tile_ro
 
 // Partial logits of a 64-token tile over one slice of the hidden dimension:
 // part[split][t][e] = sum over h in the slice of x[t][h] * Wr[h][e].  The
-// slice is walked in chunks of RT_HC; each chunk of the router is staged in
-// LDS transposed ([e][h]) so that the MFMA B operand is a 16-byte read.
+// slice is walked in chunks (the whole slice when its router rows fit in
+// 32 KB); each chunk of the router is staged in LDS transposed ([e][h]) so
+// that the MFMA B operand is a 16-byte read, and all token loads of a chunk
+// are issued before the staging, so their latency overlaps it.
+constexpr int RP_MAXCH = 512;  // largest staged chunk (hidden units)
 template <int NT>
 __global__ __launch_bounds__(256) void router_partial_kernel(
     const uint16_t* __restrict__ x, int T, int H, int E, const uint16_t* __restrict__ wr,
     int hslice, float* __restrict__ part) {
   constexpr int EP = NT * 16;
-  constexpr int LDW = RT_HC + RT_PAD;
+  constexpr int MAXCH = EP <= 32 ? RP_MAXCH : RT_HC;
+  constexpr int LDW = MAXCH + RT_PAD;
   __shared__ __attribute__((aligned(16))) uint16_t wt[EP * LDW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile0 = blockIdx.x * RT_TOK;
   const int split = blockIdx.y;
   const int hb = split * hslice;
+  const int ch = (hslice % MAXCH == 0) ? MAXCH : RT_HC;  // hslice is a multiple of RT_HC
   f32x4 acc[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -181,19 +186,21 @@ __global__ __launch_bounds__(256) void router_partial_kernel(
   const bool tok_ok = my_tok < T;
   const uint16_t* xrow = x + (size_t)(tok_ok ? my_tok : 0) * H;
   const int kq = (lane >> 4) * 8;
-  for (int h0 = hb; h0 < hb + hslice; h0 += RT_HC) {
-    u32x4 av[RT_HC / 32];
+  for (int h0 = hb; h0 < hb + hslice; h0 += ch) {
+    u32x4 av[MAXCH / 32];
 #pragma unroll
-    for (int s = 0; s < RT_HC / 32; ++s)
-      av[s] = tok_ok ? ldg16(xrow + h0 + s * 32 + kq) : u32x4{0u, 0u, 0u, 0u};
+    for (int s = 0; s < MAXCH / 32; ++s)
+      if (s * 32 < ch) av[s] = tok_ok ? ldg16(xrow + h0 + s * 32 + kq) : u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
-    for (int i = tid; i < RT_HC * EP; i += 256) {
+#pragma unroll 8
+    for (int i = tid; i < ch * EP; i += 256) {
       const int r = i / EP, e = i % EP;
       wt[e * LDW + r] = (e < E) ? wr[(size_t)(h0 + r) * E + e] : (uint16_t)0;
     }
     __syncthreads();
 #pragma unroll
-    for (int s = 0; s < RT_HC / 32; ++s) {
+    for (int s = 0; s < MAXCH / 32; ++s) {
+      if (s * 32 >= ch) break;
       const bf16x8 a = as_bf16x8(av[s]);
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
@@ -218,16 +225,19 @@ __global__ __launch_bounds__(256) void router_partial_kernel(
 
 // Sum of the partial logits in split order (+ bias), then top-k and softmax.
 // nsplit == 0: `part` holds caller-given logits [T][E], used as they are.
+// RK_TOK tokens per workgroup (4 per wave), so a prefill batch spreads over
+// the whole chip.
+constexpr int RK_TOK = 16;
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ part,
                                                           int nsplit, int T, int E, int k,
                                                           const float* __restrict__ bias,
                                                           int32_t* __restrict__ idx_out,
                                                           float* __restrict__ w_out) {
-  __shared__ float lg[RT_TOK * (MOE_MAX_EXPERTS + 1)];
+  __shared__ float lg[RK_TOK * (MOE_MAX_EXPERTS + 1)];
   const int ldl = E + 1;
   const int tid = threadIdx.x;
-  const int tile0 = blockIdx.x * RT_TOK;
-  for (int i = tid; i < RT_TOK * E; i += 256) {
+  const int tile0 = blockIdx.x * RK_TOK;
+  for (int i = tid; i < RK_TOK * E; i += 256) {
     const int r = i / E, e = i % E, t = tile0 + r;
     if (t >= T) continue;
     float v[RT_MAX_SPLITS];
@@ -242,7 +252,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     lg[r * ldl + e] = s;
   }
   __syncthreads();
-  topk_rows(lg, ldl, tile0, T, E, k, idx_out, w_out);
+  topk_rows(lg, ldl, tile0, T, E, k, idx_out, w_out, 4, nullptr, RK_TOK);
 }
 
 __global__ __launch_bounds__(256) void router_f32_kernel(
@@ -512,6 +522,7 @@ int router_splits(int T, int H) {
 
 int launch_router(const RouterArgs& a, hipStream_t st) {
   const int grid = (a.T + RT_TOK - 1) / RT_TOK;
+  const int kgrid = (a.T + RK_TOK - 1) / RK_TOK;
   if (a.dtype_f32) {
     router_f32_kernel<<<grid, 256, 0, st>>>((const float*)a.x, a.T, a.H, a.E, a.k,
                                             (const float*)a.wr, a.bias, a.logits_in, a.idx,
@@ -519,8 +530,8 @@ int launch_router(const RouterArgs& a, hipStream_t st) {
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
   if (a.logits_in) {
-    router_topk_kernel<<<grid, 256, 0, st>>>(a.logits_in, 0, a.T, a.E, a.k, nullptr, a.idx,
-                                             a.w);
+    router_topk_kernel<<<kgrid, 256, 0, st>>>(a.logits_in, 0, a.T, a.E, a.k, nullptr, a.idx,
+                                              a.w);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
   const int ns = router_splits(a.T, a.H);
@@ -539,7 +550,7 @@ int launch_router(const RouterArgs& a, hipStream_t st) {
     router_partial_kernel<8><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, ww, hs, a.part);
   else
     router_partial_kernel<16><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, ww, hs, a.part);
-  router_topk_kernel<<<grid, 256, 0, st>>>(a.part, ns, a.T, a.E, a.k, a.bias, a.idx, a.w);
+  router_topk_kernel<<<kgrid, 256, 0, st>>>(a.part, ns, a.T, a.E, a.k, a.bias, a.idx, a.w);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
