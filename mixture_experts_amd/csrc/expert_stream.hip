@@ -11,8 +11,8 @@
 // f0..f0+15 for the first kernel, 32 weight rows; down rows h0..h0+15 for the
 // second), over all of the expert's token rows in passes of TR.  The grid is
 // persistent: workgroup b takes items b, b + G, b + 2G, ... and treats the
-// K chunks of all its items as one sequence.  A chunk is CK (256, or 128
-// when K is not a multiple of 256) K elements: the 2 CK-byte run of every
+// K chunks of all its items as one sequence.  A chunk is CK (512, 256 or
+// 128, as K allows) K elements: the 2 CK-byte run of every
 // weight row and of every token row of the pass.  It reaches LDS through
 // direct global->LDS loads, weight rows as non-temporal 1 KB loads of
 // 1024 / (2 CK) row runs each; a ring of NS chunk stages keeps NS-1
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void stream_kernel(
   constexpr int IT = TR / RPI / 4;    // token loads per wave per chunk
   constexpr int KSW = CK / 32 / 4;    // 32-wide K steps per wave per chunk
   constexpr int STAGE = (WR + TR) * RB;
-  static_assert((CK == 128 || CK == 256) && IT >= 1 && TR % (4 * RPI) == 0,
+  static_assert((CK == 128 || CK == 256 || CK == 512) && IT >= 1 && TR % (4 * RPI) == 0,
                 "chunk width and token rows per pass");
   static_assert(NS >= 2 && NS <= 4, "ring depth");
   __shared__ __attribute__((aligned(16))) uint8_t ring[NS][STAGE];
@@ -308,10 +308,14 @@ int launch_tr(const ExpertArgs& a, hipStream_t st) {
 template <bool GATED>
 int launch_stream(const ExpertArgs& a, hipStream_t st) {
   // token rows per pass (experts with more rows take several passes) and the
-  // chunk width: 256 when K allows it (bf16 layers have H % 256 == 0 and
-  // F % 128 == 0), else 128
+  // chunk width: 512 for the down projection of small batches, else 256 when
+  // K allows it (bf16 layers have H % 256 == 0 and F % 128 == 0), else 128
   const int rows = a.rows_hint;
   const int K = GATED ? a.H : a.F;
+  if (!GATED && K % 512 == 0 && rows <= 16) {  // down: 1 KB row runs
+    if (rows <= 8) return launch_tr<GATED, 8, 3, 512>(a, st);
+    return launch_tr<GATED, 16, 3, 512>(a, st);
+  }
   if (K % 256 == 0) {
     if (rows <= 8) return launch_tr<GATED, 8, GATED ? 3 : 4, 256>(a, st);
     if (rows <= 16) return launch_tr<GATED, 16, GATED ? 3 : 4, 256>(a, st);

@@ -99,6 +99,50 @@ __device__ void topk_rows(const float* lg, int ldl, int tile0, int T, int E, int
   }
 }
 
+// Top-k + softmax for E <= 16: each 16-lane group of a wave takes one token
+// (lane = expert), so a wave handles 4 tokens at once: tokens
+// tile0 + 4 (wave + nwaves j) + g, g = lane / 16.  Same ordering (value desc,
+// index asc) and fp64 softmax as topk_rows; lane j of the group evaluates the
+// exponential of pick j.
+__device__ void topk_rows16(const float* lg, int ldl, int tile0, int T, int E, int k,
+                            int32_t* idx_out, float* w_out, int nwaves, int32_t* idx_lds,
+                            int rows) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, el = lane & 15;
+  for (int r0 = wave * 4; r0 < rows; r0 += nwaves * 4) {
+    const int r = r0 + g;
+    const int t = tile0 + r;
+    const bool ok = r < rows && t < T;
+    const float v = (ok && el < E) ? lg[(size_t)r * ldl + el] : 0.0f;
+    bool avail = ok && el < E;
+    float my_v = 0.0f;
+    int my_e = 0;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j >= k) break;
+      Cand best{v, avail ? el : INT32_MAX};
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) {
+        Cand o{__shfl_xor(best.v, off), __shfl_xor(best.e, off)};
+        if (better(o, best)) best = o;
+      }
+      if (best.e == el) avail = false;
+      if (el == j) { my_v = best.v; my_e = best.e; }
+    }
+    // softmax over the picks: lane j < k holds pick j; the maximum is pick 0
+    const float m = __shfl(my_v, lane & ~15);
+    const double ex = el < k ? exp((double)my_v - (double)m) : 0.0;
+    double z = ex;
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+    if (ok && el < k) {
+      idx_out[(size_t)t * k + el] = my_e;
+      w_out[(size_t)t * k + el] = (float)(ex / z);
+      if (idx_lds) idx_lds[r * k + el] = my_e;
+    }
+  }
+}
+
 // Dispatch of S = T*k <= RT_TOK*8 slots whose expert ids are in LDS
 // (idx_lds[S]): wave 0 ranks the slots of each expert with ballot matches
 // in slot order, one thread scans the counts, every thread scatters.  Same
@@ -434,25 +478,37 @@ __global__ __launch_bounds__(1024) void route_one_kernel(
     }
   };
   load_x(0);
-  // stage Wr^T: thread h reads router rows h, h + 1024, ... (E bf16 each;
-  // EV = 8 or 16: E is that, and a row is one or two 16-byte loads)
-  constexpr int RPT = R1_HMAX / 1024;
+  // stage Wr^T (EV = 8: E is 8 and a router row is one 16-byte load)
   if (EV > 0) {
-    u32x4 wv[RPT][EV / 8];
+    // thread i < H/8 takes router rows 8i .. 8i+7 (8 experts per 16-byte
+    // load) in two halves of 4 rows, transposes the 4x8 bf16 blocks in
+    // registers and writes each expert's 4 consecutive hidden units as one
+    // 8-byte LDS store
+    const int g = tid;  // group of 8 rows
+    if (g * 8 < H) {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int h = min(tid + i * 1024, H - 1);
+      for (int half = 0; half < 2; ++half) {
+        u32x4 rv[4][EV / 8];
 #pragma unroll
-      for (int q = 0; q < EV / 8; ++q) wv[i][q] = ldg16(wr + (size_t)h * EV + q * 8);
-    }
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int h = tid + i * 1024;
-      if (h < H) {
+          for (int q = 0; q < EV / 8; ++q)
+            rv[r][q] = ldg16(wr + (size_t)(g * 8 + half * 4 + r) * EV + q * 8);
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          wt[e * R1_LDW + h] = e < EV ? (uint16_t)(wv[i][e >> 3][(e & 7) >> 1] >> (16 * (e & 1)))
-                                      : (uint16_t)0;
+        for (int q = 0; q < EV / 8; ++q)
+#pragma unroll
+          for (int ee = 0; ee < 8; ++ee) {  // expert q*8 + ee
+            uint2 o;
+            const int sh = 16 * (ee & 1);
+            o.x = ((rv[0][q][ee >> 1] >> sh) & 0xffffu) | (((rv[1][q][ee >> 1] >> sh) & 0xffffu) << 16);
+            o.y = ((rv[2][q][ee >> 1] >> sh) & 0xffffu) | (((rv[3][q][ee >> 1] >> sh) & 0xffffu) << 16);
+            *reinterpret_cast<uint2*>(wt + (q * 8 + ee) * R1_LDW + g * 8 + half * 4) = o;
+          }
+      }
+      if (EV == 8) {
+#pragma unroll
+        for (int ee = 8; ee < 16; ++ee)
+          *reinterpret_cast<u32x4*>(wt + ee * R1_LDW + g * 8) = u32x4{0u, 0u, 0u, 0u};
       }
     }
   } else {
@@ -501,7 +557,7 @@ __global__ __launch_bounds__(1024) void route_one_kernel(
     lg[t * 17 + e] = s;
   }
   __syncthreads();
-  topk_rows(lg, 17, 0, T, E, k, idx_out, w_out, 16, idx_l);
+  topk_rows16(lg, 17, 0, T, E, k, idx_out, w_out, 16, idx_l, RT_TOK);
   __syncthreads();
   dispatch_small(idx_l, T * k, E, tile_rows, cnt, off_l, rank_l, counts, offsets, tile_off,
                  active, perm, inv);
@@ -567,7 +623,6 @@ int launch_route_small(const RouterArgs& a, const DispatchArgs& d, int32_t* coun
     else if (mb <= 2) route_one_kernel<2, EV><<<1, 1024, 0, st>>>(R1_ARGS); \
     else route_one_kernel<4, EV><<<1, 1024, 0, st>>>(R1_ARGS);
     if (a.E == 8) { R1_MB(8) }
-    else if (a.E == 16) { R1_MB(16) }
     else { R1_MB(0) }
 #undef R1_MB
 #undef R1_ARGS
