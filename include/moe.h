@@ -72,7 +72,14 @@ enum {
    * through grouped GEMMs on 256x256 tiles.  These flags pin one path
    * (results agree within rounding; both are deterministic). */
   MOE_FLAG_PATH_GROUPED = 1u << 1,
-  MOE_FLAG_PATH_STREAM = 1u << 2
+  MOE_FLAG_PATH_STREAM = 1u << 2,
+  /* Gate variant: the same top-k selection, and the gate weights are the k
+   * selected logits themselves (fp32, no softmax) -- the default router of
+   * m.nxbn.cn/news/47896 sec. 3.2 and www.pnsm.cn/news/1892388.html sec. 3.3.
+   * Without it the weights are the softmax over the k selected logits.
+   * (Soft routing, every expert weighted, is top_k == num_experts with the
+   * softmax gate.) */
+  MOE_FLAG_GATE_RAW = 1u << 3
 };
 
 typedef struct {

@@ -22,6 +22,7 @@ MOE_BF16 = 1
 MOE_FLAG_RESIDUAL_PRENORM = 1 << 0
 MOE_FLAG_PATH_GROUPED = 1 << 1
 MOE_FLAG_PATH_STREAM = 1 << 2
+MOE_FLAG_GATE_RAW = 1 << 3
 
 MOE_STAGE_ROUTE, MOE_STAGE_DISPATCH, MOE_STAGE_GATE_UP, MOE_STAGE_DOWN, MOE_STAGE_COMBINE = range(5)
 MOE_NUM_STAGES = 5

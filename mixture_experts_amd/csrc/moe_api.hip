@@ -42,7 +42,7 @@ struct moe_layer {
 namespace {
 
 constexpr uint32_t kKnownFlags = MOE_FLAG_RESIDUAL_PRENORM | MOE_FLAG_PATH_GROUPED |
-                                 MOE_FLAG_PATH_STREAM;
+                                 MOE_FLAG_PATH_STREAM | MOE_FLAG_GATE_RAW;
 
 struct Arena {
   char* base;
@@ -162,7 +162,8 @@ int run_route(moe_layer* L, const void* x_route, int T, const float* logits_in,
               int tile_rows, hipStream_t st) {
   const moe_layer_desc& d = L->d;
   RouterArgs ra{x_route, T, d.hidden, d.num_experts, d.top_k, d.dtype == MOE_F32 ? 1 : 0,
-                d.router_w, d.router_b, logits_in, L->idx, L->w, L->part};
+                d.router_w, d.router_b, logits_in, L->idx, L->w, L->part,
+                (d.flags & MOE_FLAG_GATE_RAW) ? 1 : 0};
   DispatchArgs da{L->idx, T * d.top_k, d.num_experts, tile_rows, L->hist, L->rank, L->base,
                   L->counts, L->offsets, L->tile_off, L->active, L->perm, L->inv};
   if (small_route(L, T, logits_in)) return launch_route_small(ra, da, L->sync, st) ? MOE_ERR_DEVICE : MOE_OK;
@@ -287,7 +288,8 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
   {
     const moe_layer_desc& dd = L->d;
     RouterArgs ra{xin, T, dd.hidden, dd.num_experts, dd.top_k, f32 ? 1 : 0, dd.router_w,
-                  dd.router_b, nullptr, L->idx, L->w, L->part};
+                  dd.router_b, nullptr, L->idx, L->w, L->part,
+                  (dd.flags & MOE_FLAG_GATE_RAW) ? 1 : 0};
     DispatchArgs da{L->idx, S, dd.num_experts, GG_BT, L->hist, L->rank, L->base, L->counts,
                     L->offsets, L->tile_off, L->active, L->perm, L->inv};
     if (small_route(L, T, nullptr)) {  // one launch: the dispatch stage is empty

@@ -41,7 +41,7 @@ __device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
 // tile0 + rows (interleaved so that small batches still spread over the
 // waves).  lg: LDS logits [rows][ldl].  idx_lds (optional): an LDS copy of the
 // picks of the tile, [RT_TOK][k].
-__device__ void topk_rows(const float* lg, int ldl, int tile0, int T, int E, int k,
+__device__ void topk_rows(const float* lg, int ldl, int tile0, int T, int E, int k, int raw,
                           int32_t* idx_out, float* w_out, int nwaves = 4,
                           int32_t* idx_lds = nullptr, int rows = RT_TOK) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -79,32 +79,33 @@ __device__ void topk_rows(const float* lg, int ldl, int tile0, int T, int E, int
       sel_e[j] = best.e;
       if ((best.e & 63) == lane) avail &= ~(1u << (best.e >> 6));
     }
-    // softmax over the k selected logits, in double
+    // softmax over the k selected logits, in double (raw gate: the logits)
     const double m = (double)sel_v[0];
     double z = 0.0;
     double num = 0.0;
+    float vj = 0.0f;
     int ej = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j >= k) continue;
-      const double ex = exp((double)sel_v[j] - m);
+      const double ex = raw ? 0.0 : exp((double)sel_v[j] - m);
       z += ex;
-      if (j == lane) { num = ex; ej = sel_e[j]; }
+      if (j == lane) { num = ex; ej = sel_e[j]; vj = sel_v[j]; }
     }
     if (lane < k) {
       idx_out[(size_t)t * k + lane] = ej;
-      w_out[(size_t)t * k + lane] = (float)(num / z);
+      w_out[(size_t)t * k + lane] = raw ? vj : (float)(num / z);
       if (idx_lds) idx_lds[r * k + lane] = ej;
     }
   }
 }
 
-// Top-k + softmax for E <= 16: each 16-lane group of a wave takes one token
+// Top-k + softmax (raw gate: the selected logits) for E <= 16: each 16-lane group of a wave takes one token
 // (lane = expert), so a wave handles 4 tokens at once: tokens
 // tile0 + 4 (wave + nwaves j) + g, g = lane / 16.  Same ordering (value desc,
 // index asc) and fp64 softmax as topk_rows; lane j of the group evaluates the
 // exponential of pick j.
-__device__ void topk_rows16(const float* lg, int ldl, int tile0, int T, int E, int k,
+__device__ void topk_rows16(const float* lg, int ldl, int tile0, int T, int E, int k, int raw,
                             int32_t* idx_out, float* w_out, int nwaves, int32_t* idx_lds,
                             int rows) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -131,13 +132,13 @@ __device__ void topk_rows16(const float* lg, int ldl, int tile0, int T, int E, i
     }
     // softmax over the picks: lane j < k holds pick j; the maximum is pick 0
     const float m = __shfl(my_v, lane & ~15);
-    const double ex = el < k ? exp((double)my_v - (double)m) : 0.0;
+    const double ex = (el < k && !raw) ? exp((double)my_v - (double)m) : 0.0;
     double z = ex;
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1) z += __shfl_xor(z, off);
     if (ok && el < k) {
       idx_out[(size_t)t * k + el] = my_e;
-      w_out[(size_t)t * k + el] = (float)(ex / z);
+      w_out[(size_t)t * k + el] = raw ? my_v : (float)(ex / z);
       if (idx_lds) idx_lds[r * k + el] = my_e;
     }
   }
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(256) void router_partial_kernel(
 // the whole chip.
 constexpr int RK_TOK = 16;
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ part,
-                                                          int nsplit, int T, int E, int k,
+                                                          int nsplit, int T, int E, int k, int raw,
                                                           const float* __restrict__ bias,
                                                           int32_t* __restrict__ idx_out,
                                                           float* __restrict__ w_out) {
@@ -296,13 +297,14 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     lg[r * ldl + e] = s;
   }
   __syncthreads();
-  topk_rows(lg, ldl, tile0, T, E, k, idx_out, w_out, 4, nullptr, RK_TOK);
+  topk_rows(lg, ldl, tile0, T, E, k, raw, idx_out, w_out, 4, nullptr, RK_TOK);
 }
 
 __global__ __launch_bounds__(256) void router_f32_kernel(
-    const float* __restrict__ x, int T, int H, int E, int k, const float* __restrict__ wr,
-    const float* __restrict__ bias, const float* __restrict__ logits_in,
-    int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
+    const float* __restrict__ x, int T, int H, int E, int k, int raw,
+    const float* __restrict__ wr, const float* __restrict__ bias,
+    const float* __restrict__ logits_in, int32_t* __restrict__ idx_out,
+    float* __restrict__ w_out) {
   __shared__ float lg[RT_TOK * 257];
   const int ldl = E + 1;
   const int tid = threadIdx.x, wave = tid >> 6;
@@ -321,7 +323,7 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
     lg[r * ldl + e] = s;
   }
   __syncthreads();
-  topk_rows(lg, ldl, tile0, T, E, k, idx_out, w_out);
+  topk_rows(lg, ldl, tile0, T, E, k, raw, idx_out, w_out);
 }
 
 // Branch input of a stacked layer: xt[t] = bf16(h[t] / sqrt(mean(h[t]^2) + 1e-6)).
@@ -353,7 +355,7 @@ __global__ __launch_bounds__(256) void prenorm_kernel(const float* __restrict__ 
 // result does not depend on which workgroup finishes last.
 template <int NT>
 __global__ __launch_bounds__(256) void route_small_kernel(
-    const uint16_t* __restrict__ x, int T, int H, int E, int k,
+    const uint16_t* __restrict__ x, int T, int H, int E, int k, int raw,
     const uint16_t* __restrict__ wr, const float* __restrict__ bias, int hslice,
     float* __restrict__ part, int32_t* __restrict__ counter, int tile_rows,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ counts,
@@ -430,7 +432,7 @@ __global__ __launch_bounds__(256) void route_small_kernel(
     lg[t * ldl + e] = s;
   }
   __syncthreads();
-  topk_rows(lg, ldl, 0, T, E, k, idx_out, w_out, 4, idx_l);
+  topk_rows(lg, ldl, 0, T, E, k, raw, idx_out, w_out, 4, idx_l);
   __syncthreads();
   if (tid == 0) *counter = 0;  // ready for the next launch
   dispatch_small(idx_l, T * k, E, tile_rows, cnt, off_l, rank_l, counts, offsets, tile_off,
@@ -447,7 +449,7 @@ constexpr int R1_HMAX = 4096;
 constexpr int R1_LDW = R1_HMAX + 8;  // padded router row (bf16)
 template <int MB, int EV>
 __global__ __launch_bounds__(1024) void route_one_kernel(
-    const uint16_t* __restrict__ x, int T, int H, int E, int k,
+    const uint16_t* __restrict__ x, int T, int H, int E, int k, int raw,
     const uint16_t* __restrict__ wr, const float* __restrict__ bias, int tile_rows,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off,
@@ -557,7 +559,7 @@ __global__ __launch_bounds__(1024) void route_one_kernel(
     lg[t * 17 + e] = s;
   }
   __syncthreads();
-  topk_rows16(lg, 17, 0, T, E, k, idx_out, w_out, 16, idx_l, RT_TOK);
+  topk_rows16(lg, 17, 0, T, E, k, raw, idx_out, w_out, 16, idx_l, RT_TOK);
   __syncthreads();
   dispatch_small(idx_l, T * k, E, tile_rows, cnt, off_l, rank_l, counts, offsets, tile_off,
                  active, perm, inv);
@@ -580,13 +582,13 @@ int launch_router(const RouterArgs& a, hipStream_t st) {
   const int grid = (a.T + RT_TOK - 1) / RT_TOK;
   const int kgrid = (a.T + RK_TOK - 1) / RK_TOK;
   if (a.dtype_f32) {
-    router_f32_kernel<<<grid, 256, 0, st>>>((const float*)a.x, a.T, a.H, a.E, a.k,
+    router_f32_kernel<<<grid, 256, 0, st>>>((const float*)a.x, a.T, a.H, a.E, a.k, a.raw_gate,
                                             (const float*)a.wr, a.bias, a.logits_in, a.idx,
                                             a.w);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
   if (a.logits_in) {
-    router_topk_kernel<<<kgrid, 256, 0, st>>>(a.logits_in, 0, a.T, a.E, a.k, nullptr, a.idx,
+    router_topk_kernel<<<kgrid, 256, 0, st>>>(a.logits_in, 0, a.T, a.E, a.k, a.raw_gate, nullptr, a.idx,
                                               a.w);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
@@ -606,7 +608,8 @@ int launch_router(const RouterArgs& a, hipStream_t st) {
     router_partial_kernel<8><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, ww, hs, a.part);
   else
     router_partial_kernel<16><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, ww, hs, a.part);
-  router_topk_kernel<<<kgrid, 256, 0, st>>>(a.part, ns, a.T, a.E, a.k, a.bias, a.idx, a.w);
+  router_topk_kernel<<<kgrid, 256, 0, st>>>(a.part, ns, a.T, a.E, a.k, a.raw_gate, a.bias, a.idx,
+                                            a.w);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -615,7 +618,7 @@ int launch_route_small(const RouterArgs& a, const DispatchArgs& d, int32_t* coun
   if (a.E <= 16 && a.H <= R1_HMAX && a.H % 512 == 0 && a.T <= RT_TOK) {
     auto* xx = (const uint16_t*)a.x;
     auto* ww = (const uint16_t*)a.wr;
-#define R1_ARGS xx, a.T, a.H, a.E, a.k, ww, a.bias, d.tile_rows, a.idx, a.w, d.counts, \
+#define R1_ARGS xx, a.T, a.H, a.E, a.k, a.raw_gate, ww, a.bias, d.tile_rows, a.idx, a.w, d.counts, \
                 d.offsets, d.tile_off, d.active, d.perm, d.inv
     const int mb = (a.T + 15) / 16;
 #define R1_MB(EV)                                                         \
@@ -633,7 +636,7 @@ int launch_route_small(const RouterArgs& a, const DispatchArgs& d, int32_t* coun
   const int nt = (a.E + 15) / 16;
   auto* xx = (const uint16_t*)a.x;
   auto* ww = (const uint16_t*)a.wr;
-#define RS_ARGS xx, a.T, a.H, a.E, a.k, ww, a.bias, hs, a.part, counter, d.tile_rows, a.idx, a.w, \
+#define RS_ARGS xx, a.T, a.H, a.E, a.k, a.raw_gate, ww, a.bias, hs, a.part, counter, d.tile_rows, a.idx, a.w, \
                 d.counts, d.offsets, d.tile_off, d.active, d.perm, d.inv
   if (nt <= 1) route_small_kernel<1><<<ns, 256, 0, st>>>(RS_ARGS);
   else if (nt <= 2) route_small_kernel<2><<<ns, 256, 0, st>>>(RS_ARGS);

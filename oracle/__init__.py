@@ -15,13 +15,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
 F32, BF16 = 0, 1
+GATE_SOFTMAX, GATE_RAW = 0, 1
 
 
 class _Layer(ctypes.Structure):
     _fields_ = [("H", ctypes.c_int32), ("F", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
-                ("experts", ctypes.c_void_p), ("stride", ctypes.c_uint64)]
+                ("experts", ctypes.c_void_p), ("stride", ctypes.c_uint64),
+                ("gate", ctypes.c_int32)]
 
 
 def lib():
@@ -34,6 +36,7 @@ def lib():
         vp, i32 = ctypes.c_void_p, ctypes.c_int32
         L.orc_logits.argtypes = [vp, vp, i32, vp]
         L.orc_topk_softmax.argtypes = [i32, i32, i32, vp, vp, vp]
+        L.orc_topk.argtypes = [i32, i32, i32, i32, vp, vp, vp]
         L.orc_dispatch.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
         L.orc_expert_ffn.argtypes = [vp, i32, vp, vp]
         L.orc_expert_rows.argtypes = [vp, vp, i32, vp, vp, vp]
@@ -60,8 +63,9 @@ def _check(rc, what):
 class Layer:
     """One MoE layer's weights as the oracle reads them (numpy arrays kept alive)."""
 
-    def __init__(self, H, F, E, k, dtype, router_w, router_b, experts, stride):
+    def __init__(self, H, F, E, k, dtype, router_w, router_b, experts, stride, gate="softmax"):
         self.H, self.F, self.E, self.k = H, F, E, k
+        self.gate = gate
         self.dtype = dtype
         self.np_dtype = np.float32 if dtype == "f32" else np.uint16
         self.router_w = np.ascontiguousarray(router_w, dtype=self.np_dtype)
@@ -69,7 +73,8 @@ class Layer:
         self.experts = np.ascontiguousarray(experts)
         self.stride = stride
         self._s = _Layer(H, F, E, k, F32 if dtype == "f32" else BF16, _p(self.router_w),
-                         _p(self.router_b), _p(self.experts), stride)
+                         _p(self.router_b), _p(self.experts), stride,
+                         {"softmax": GATE_SOFTMAX, "raw": GATE_RAW}[gate])
 
     @property
     def ref(self):
@@ -130,6 +135,17 @@ def topk_softmax(logits, k):
     return idx, w
 
 
+def topk(logits, k, gate="softmax"):
+    """Selection (value desc, index asc) with the softmax or the raw gate."""
+    logits = np.ascontiguousarray(logits, np.float64)
+    T, E = logits.shape
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    g = {"softmax": GATE_SOFTMAX, "raw": GATE_RAW}[gate]
+    _check(lib().orc_topk(T, E, k, g, _p(logits), _p(idx), _p(w)), "topk")
+    return idx, w
+
+
 def dispatch(idx, E):
     idx = np.ascontiguousarray(idx, np.int32)
     T, k = idx.shape
@@ -169,6 +185,6 @@ def num_threads() -> int:
     return lib().orc_num_threads()
 
 
-def layer_from_gen(shape, router_w, router_b, experts) -> Layer:
+def layer_from_gen(shape, router_w, router_b, experts, gate="softmax") -> Layer:
     return Layer(shape.H, shape.F, shape.E, shape.k, shape.dtype, router_w, router_b, experts,
-                 shape.stride)
+                 shape.stride, gate=gate)

@@ -43,6 +43,7 @@ static int check_layer(const orc_layer_t* L) {
   if (!L || L->H < 1 || L->F < 1 || L->E < 1 || L->k < 1 || L->k > L->E) return -1;
   if (L->dtype != ORC_F32 && L->dtype != ORC_BF16) return -1;
   if (!L->router_w || !L->experts) return -1;
+  if (L->gate != ORC_GATE_SOFTMAX && L->gate != ORC_GATE_RAW) return -1;
   if (L->stride < 3ull * (uint64_t)L->H * (uint64_t)L->F * elem_size(L->dtype)) return -1;
   return 0;
 }
@@ -74,10 +75,25 @@ int orc_logits(const orc_layer_t* L, const void* x, int32_t T, double* logits) {
   return 0;
 }
 
+/* O3: the gate weights of the k picks idx[0..k-1] (pick 0 the largest). */
+static void gate_weights(int32_t k, int32_t gate, const double* Lt, const int32_t* idx,
+                         double* w) {
+  if (gate == ORC_GATE_RAW) {
+    for (int32_t j = 0; j < k; ++j) w[j] = Lt[idx[j]];
+    return;
+  }
+  double m = Lt[idx[0]];
+  double z = 0.0;
+  for (int32_t j = 0; j < k; ++j) z += exp(Lt[idx[j]] - m);
+  for (int32_t j = 0; j < k; ++j) w[j] = exp(Lt[idx[j]] - m) / z;
+}
+
 /* O2 + O3 for one token: k rounds of "largest unpicked logit", scanning e
  * upwards and replacing only on strictly greater, so equal logits go to the
- * lower index; then w_j = exp(L_j - L_0) / sum_i exp(L_i - L_0). */
-static int topk_one(int32_t E, int32_t k, const double* Lt, int32_t* idx, double* w) {
+ * lower index; then w_j = exp(L_j - L_0) / sum_i exp(L_i - L_0), or, with
+ * the raw gate, w_j = L_j. */
+static int topk_one(int32_t E, int32_t k, int32_t gate, const double* Lt, int32_t* idx,
+                    double* w) {
   for (int32_t e = 0; e < E; ++e)
     if (!isfinite(Lt[e])) return -2;
   for (int32_t j = 0; j < k; ++j) {
@@ -91,22 +107,26 @@ static int topk_one(int32_t E, int32_t k, const double* Lt, int32_t* idx, double
     }
     idx[j] = best;
   }
-  double m = Lt[idx[0]];
-  double z = 0.0;
-  for (int32_t j = 0; j < k; ++j) z += exp(Lt[idx[j]] - m);
-  for (int32_t j = 0; j < k; ++j) w[j] = exp(Lt[idx[j]] - m) / z;
+  gate_weights(k, gate, Lt, idx, w);
   return 0;
+}
+
+int orc_topk(int32_t T, int32_t E, int32_t k, int32_t gate, const double* logits,
+             int32_t* idx, double* w) {
+  if (T < 0 || E < 1 || k < 1 || k > E || !logits || !idx || !w) return -1;
+  if (gate != ORC_GATE_SOFTMAX && gate != ORC_GATE_RAW) return -1;
+  int rc = 0;
+  for (int32_t t = 0; t < T; ++t) {
+    int r = topk_one(E, k, gate, logits + (size_t)t * E, idx + (size_t)t * k,
+                     w + (size_t)t * k);
+    if (r) rc = r;
+  }
+  return rc;
 }
 
 int orc_topk_softmax(int32_t T, int32_t E, int32_t k, const double* logits, int32_t* idx,
                      double* w) {
-  if (T < 0 || E < 1 || k < 1 || k > E || !logits || !idx || !w) return -1;
-  int rc = 0;
-  for (int32_t t = 0; t < T; ++t) {
-    int r = topk_one(E, k, logits + (size_t)t * E, idx + (size_t)t * k, w + (size_t)t * k);
-    if (r) rc = r;
-  }
-  return rc;
+  return orc_topk(T, E, k, ORC_GATE_SOFTMAX, logits, idx, w);
 }
 
 /* O4: counting sort of the T*k (token, slot) pairs by expert.  counts[e];
@@ -213,7 +233,7 @@ int orc_layer_forward(const orc_layer_t* L, const void* x, int32_t T, double* y,
   double* yp = (double*)malloc(sizeof(double) * ((size_t)T * k * H + 1));
   int rc = (!logits || !yp) ? -1 : 0;
   if (!rc) rc = orc_logits(L, x, T, logits);
-  if (!rc) rc = orc_topk_softmax(T, E, k, logits, idx, w);
+  if (!rc) rc = orc_topk(T, E, k, L->gate, logits, idx, w);
   if (!rc) rc = orc_dispatch(T, E, k, idx, counts, offsets, perm, inv);
   if (!rc) rc = orc_expert_rows(L, x, T, offsets, perm, yp);
   if (!rc) rc = orc_combine(T, H, k, w, inv, yp, y);
@@ -226,7 +246,7 @@ int orc_layer_forward(const orc_layer_t* L, const void* x, int32_t T, double* y,
  * definition y[t] = sum_j w_j * FFN_{idx_j}(x[t]) (the same value that
  * O1..O6 give row t).  tokens [ntok]; idx_override [ntok*k] or NULL: when
  * given, those experts (in that slot order) replace the top-k choice and the
- * weights are the softmax of the oracle's logits at them.  Outputs y
+ * weights are the gate (softmax or raw) of the oracle's logits at them.  Outputs y
  * [ntok*H], idx [ntok*k], w [ntok*k], logits [ntok*E]. */
 int orc_layer_tokens(const orc_layer_t* L, const void* x, int32_t T, const int32_t* tokens,
                      int32_t ntok, const int32_t* idx_override, double* y, int32_t* idx,
@@ -253,17 +273,13 @@ int orc_layer_tokens(const orc_layer_t* L, const void* x, int32_t T, const int32
     }
     int32_t* it = idx + (size_t)n * k;
     double* wt = w + (size_t)n * k;
-    rc = topk_one(E, k, Lt, it, wt);
+    rc = topk_one(E, k, L->gate, Lt, it, wt);
     if (!rc && idx_override) {
       for (int32_t j = 0; j < k; ++j) {
         it[j] = idx_override[(size_t)n * k + j];
         if (it[j] < 0 || it[j] >= E) rc = -1;
       }
-      if (!rc) {
-        double m = Lt[it[0]], z = 0.0;
-        for (int32_t j = 0; j < k; ++j) z += exp(Lt[it[j]] - m);
-        for (int32_t j = 0; j < k; ++j) wt[j] = exp(Lt[it[j]] - m) / z;
-      }
+      if (!rc) gate_weights(k, L->gate, Lt, it, wt);
     }
   }
   if (!rc) {

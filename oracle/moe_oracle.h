@@ -14,6 +14,10 @@
  *   top-k    the k largest logits per token, ties to the lower expert index,
  *            then a softmax over the k selected logits: www.lmnt.cn/news/246575
  *            sec. 2.2 (route_tokens: logits, top-k, in-place softmax).
+ *            Gate variant ORC_GATE_RAW: the same selection, and the weights
+ *            are the selected raw logits themselves, no softmax (the default
+ *            router of m.nxbn.cn/news/47896 sec. 3.2 and of
+ *            www.pnsm.cn/news/1892388.html sec. 3.3).
  *   dispatch the (token, slot) pairs grouped by expert into one batch per
  *            expert: zskr.cn page sec. 3.3, stage 3.
  *   expert   SwiGLU without bias, gate/up of shape (intermediate, hidden),
@@ -49,6 +53,7 @@ extern "C" {
 #endif
 
 enum { ORC_F32 = 0, ORC_BF16 = 1 };
+enum { ORC_GATE_SOFTMAX = 0, ORC_GATE_RAW = 1 };
 
 typedef struct {
   int32_t H, F, E, k;
@@ -57,11 +62,15 @@ typedef struct {
   const float* router_b;
   const void* experts;
   uint64_t stride;
+  int32_t gate;  /* ORC_GATE_SOFTMAX or ORC_GATE_RAW */
 } orc_layer_t;
 
 int orc_logits(const orc_layer_t* L, const void* x, int32_t T, double* logits);
 int orc_topk_softmax(int32_t T, int32_t E, int32_t k, const double* logits, int32_t* idx,
                      double* w);
+/* the same selection with gate ORC_GATE_SOFTMAX or ORC_GATE_RAW */
+int orc_topk(int32_t T, int32_t E, int32_t k, int32_t gate, const double* logits,
+             int32_t* idx, double* w);
 int orc_dispatch(int32_t T, int32_t E, int32_t k, const int32_t* idx, int32_t* counts,
                  int32_t* offsets, int32_t* perm, int32_t* inv);
 int orc_expert_ffn(const orc_layer_t* L, int32_t e, const double* xrow, double* yrow);

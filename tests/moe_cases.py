@@ -56,7 +56,8 @@ class Case:
         self.d_experts = to_dev(self.experts)
         self.layer = moe.MoELayer(shape.H, shape.F, shape.E, shape.k, max_tokens, dt,
                                   self.d_router, self.d_experts, shape.stride, self.d_bias, flags)
-        self.orc = oracle.layer_from_gen(shape, self.router, self.bias, self.experts)
+        gate = "raw" if flags & moe.MOE_FLAG_GATE_RAW else "softmax"
+        self.orc = oracle.layer_from_gen(shape, self.router, self.bias, self.experts, gate=gate)
 
     def forward(self, x_np: np.ndarray) -> np.ndarray:
         x = to_dev(x_np)

@@ -20,8 +20,8 @@ def _log(*a):
     print(*a, flush=True)
 
 
-def routing_reference(logits32: np.ndarray, E: int, k: int):
-    idx, w = oracle.topk_softmax(logits32.astype(np.float64), k)
+def routing_reference(logits32: np.ndarray, E: int, k: int, gate: str = "softmax"):
+    idx, w = oracle.topk(logits32.astype(np.float64), k, gate)
     counts, offsets, perm, inv = oracle.dispatch(idx, E)
     return dict(idx=idx.ravel(), w=w.ravel(), counts=counts, offsets=offsets, perm=perm, inv=inv)
 
@@ -57,6 +57,22 @@ def test_route_given_logits_bit_exact(E, k, T):
     torch.cuda.synchronize()
     gpu = {kk: v.cpu().numpy() for kk, v in gpu.items()}
     assert_routing_equal(gpu, routing_reference(lg, E, k))
+    c.close()
+
+
+@pytest.mark.parametrize("E,k,T", [(8, 2, 1), (8, 2, 300), (64, 2, 97), (256, 8, 40)])
+def test_route_raw_gate_given_logits_bit_exact(E, k, T):
+    """Raw gate: the same selection; the weights are the given fp32 logits."""
+    rng = np.random.default_rng(7 * E + T)
+    lg = rng.normal(0, 1.5, (T, E)).astype(np.float32)
+    lg[::5] = np.round(lg[::5])
+    c = Case(f32_shape(E, k), T, flags=moe.MOE_FLAG_GATE_RAW)
+    gpu = c.layer.route(None, T, logits_in=torch.from_numpy(lg).cuda())
+    torch.cuda.synchronize()
+    gpu = {kk: v.cpu().numpy() for kk, v in gpu.items()}
+    ref = routing_reference(lg, E, k, "raw")
+    assert_routing_equal(gpu, ref)
+    assert np.array_equal(gpu["w"], np.take_along_axis(lg, gpu["idx"].reshape(T, k).astype(np.int64), 1).ravel())
     c.close()
 
 
@@ -102,6 +118,16 @@ SMALL = [
     ("bf16", 256, 640, 16, 4, 300, moe.MOE_FLAG_PATH_GROUPED),
     ("bf16", 768, 256, 3, 1, 1100, 0),
     ("bf16", 256, 128, 64, 8, 97, 0),
+    # raw-logit gates: fp32 router, each bf16 router kernel, both expert paths
+    ("f32", 64, 128, 8, 2, 32, moe.MOE_FLAG_GATE_RAW),
+    ("bf16", 512, 256, 8, 2, 5, moe.MOE_FLAG_GATE_RAW),
+    ("bf16", 512, 384, 4, 2, 700, moe.MOE_FLAG_GATE_RAW | moe.MOE_FLAG_PATH_GROUPED),
+    ("bf16", 512, 384, 4, 2, 300, moe.MOE_FLAG_GATE_RAW | moe.MOE_FLAG_PATH_STREAM),
+    ("bf16", 256, 128, 64, 8, 60, moe.MOE_FLAG_GATE_RAW),
+    # soft routing: every expert weighted (top_k == num_experts)
+    ("bf16", 512, 256, 8, 8, 50, moe.MOE_FLAG_PATH_STREAM),
+    ("bf16", 512, 256, 8, 8, 300, moe.MOE_FLAG_PATH_GROUPED),
+    ("f32", 64, 128, 6, 6, 32, 0),
 ]
 
 

@@ -214,6 +214,84 @@ def test_sparse_equals_dense_masked(E, k, dtype):
     assert np.abs(r["y"] - y).max() <= 1e-12 * rms
 
 
+# --- gate variants: raw-logit gates, soft routing (k = E) -------------------
+
+
+def test_raw_gate_weights_are_the_selected_logits():
+    """Raw gate [m.nxbn.cn/news/47896 sec. 3.2; www.pnsm.cn/news/1892388.html
+    sec. 3.3]: same selection as the softmax gate, weights = those logits."""
+    rng = np.random.default_rng(3)
+    lg = rng.normal(size=(40, 12))
+    lg[5, 3] = lg[5, 7] = lg[5].max() + 1.0      # planted tie for the top slot
+    lg[9, :] = 0.25                               # all equal
+    i_s, _ = oracle.topk(lg, 4, "softmax")
+    i_r, w_r = oracle.topk(lg, 4, "raw")
+    assert (i_r == i_s).all()
+    assert np.array_equal(w_r, np.take_along_axis(lg, i_r.astype(np.int64), 1))
+    assert list(i_r[5, :2]) == [3, 7] and list(i_r[9]) == [0, 1, 2, 3]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_raw_gate_equals_dense_brute_force(dtype):
+    H, F, E, k, T = 16, 24, 6, 2, 11
+    shape, _, wr, ex = make_layer(H, F, E, k, dtype=dtype)
+    L = oracle.layer_from_gen(shape, wr, None, ex, gate="raw")
+    x = gen.gen_x(shape, T)
+    r = L.forward(x)
+    X = widen(x, dtype)
+    logits = X @ widen(wr, dtype)
+    order = np.argsort(-logits, axis=1, kind="stable")[:, :k]
+    assert (order == r["idx"]).all()
+    mask = np.zeros((T, E))
+    np.put_along_axis(mask, order, np.take_along_axis(logits, order, 1), 1)
+    y = np.zeros((T, H))
+    for e in range(E):
+        Wg, Wu, Wd = (widen(m, dtype) for m in gen.expert_views(shape, ex, e))
+        a = silu(X @ Wg.T) * (X @ Wu.T)
+        if dtype == "bf16":
+            a = np.vectorize(oracle.bf16_round)(a)
+        y += mask[:, e:e + 1] * (a @ Wd.T)
+    assert np.abs(r["y"] - y).max() <= 1e-12 * np.sqrt((y ** 2).mean())
+    t = L.tokens(x, np.array([0, 4, 10], np.int32))
+    assert np.array_equal(t["y"], r["y"][[0, 4, 10]]) and np.array_equal(t["w"], r["w"][[0, 4, 10]])
+
+
+def test_raw_gate_router_scaling_is_exact():
+    """Doubling the router doubles every logit exactly, keeps the selection,
+    and doubles the raw weights, so the output doubles bit for bit."""
+    shape, _, wr, ex = make_layer(16, 24, 8, 2)
+    x = gen.gen_x(shape, 9)
+    r1 = oracle.layer_from_gen(shape, wr, None, ex, gate="raw").forward(x)
+    r2 = oracle.layer_from_gen(shape, 2 * wr, None, ex, gate="raw").forward(x)
+    assert (r1["idx"] == r2["idx"]).all()
+    assert np.array_equal(r2["w"], 2 * r1["w"]) and np.array_equal(r2["y"], 2 * r1["y"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_soft_routing_k_equals_E_is_dense_softmax_mixture(dtype):
+    """Soft routing, read as weighting every expert instead of a hard top-k
+    selection [m.nxbn.cn/news/47896 sec. 2.2, soft_route()]: with k = E the
+    layer is sum_e softmax(L)_e FFN_e(x) over all experts."""
+    H, F, E, T = 16, 24, 8, 7
+    shape, L, wr, ex = make_layer(H, F, E, E, dtype=dtype)
+    x = gen.gen_x(shape, T)
+    r = L.forward(x)
+    X = widen(x, dtype)
+    logits = X @ widen(wr, dtype)
+    p = np.exp(logits - logits.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    assert np.allclose(np.sort(r["w"], 1), np.sort(p, 1), rtol=0, atol=1e-15)
+    assert all(sorted(row) == list(range(E)) for row in r["idx"].tolist())
+    y = np.zeros((T, H))
+    for e in range(E):
+        Wg, Wu, Wd = (widen(m, dtype) for m in gen.expert_views(shape, ex, e))
+        a = silu(X @ Wg.T) * (X @ Wu.T)
+        if dtype == "bf16":
+            a = np.vectorize(oracle.bf16_round)(a)
+        y += p[:, e:e + 1] * (a @ Wd.T)
+    assert np.abs(r["y"] - y).max() <= 1e-12 * np.sqrt((y ** 2).mean())
+
+
 # --- P8: algebraic properties --------------------------------------------
 
 
