@@ -23,7 +23,7 @@ class _Layer(ctypes.Structure):
                 ("k", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
                 ("experts", ctypes.c_void_p), ("stride", ctypes.c_uint64),
-                ("gate", ctypes.c_int32)]
+                ("gate", ctypes.c_int32), ("capacity", ctypes.c_int32)]
 
 
 def lib():
@@ -38,11 +38,12 @@ def lib():
         L.orc_topk_softmax.argtypes = [i32, i32, i32, vp, vp, vp]
         L.orc_topk.argtypes = [i32, i32, i32, i32, vp, vp, vp]
         L.orc_dispatch.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
+        L.orc_dispatch_cap.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
         L.orc_expert_ffn.argtypes = [vp, i32, vp, vp]
         L.orc_expert_rows.argtypes = [vp, vp, i32, vp, vp, vp]
         L.orc_combine.argtypes = [i32, i32, i32, vp, vp, vp, vp]
         L.orc_layer_forward.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, vp, vp]
-        L.orc_layer_tokens.argtypes = [vp, vp, i32, vp, i32, vp, vp, vp, vp, vp]
+        L.orc_layer_tokens.argtypes = [vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp]
         L.orc_prenorm_bf16.argtypes = [i32, i32, vp, vp]
         L.orc_bf16_round.argtypes = [ctypes.c_double]
         L.orc_bf16_round.restype = ctypes.c_double
@@ -63,9 +64,11 @@ def _check(rc, what):
 class Layer:
     """One MoE layer's weights as the oracle reads them (numpy arrays kept alive)."""
 
-    def __init__(self, H, F, E, k, dtype, router_w, router_b, experts, stride, gate="softmax"):
+    def __init__(self, H, F, E, k, dtype, router_w, router_b, experts, stride, gate="softmax",
+                 capacity=0):
         self.H, self.F, self.E, self.k = H, F, E, k
         self.gate = gate
+        self.capacity = capacity
         self.dtype = dtype
         self.np_dtype = np.float32 if dtype == "f32" else np.uint16
         self.router_w = np.ascontiguousarray(router_w, dtype=self.np_dtype)
@@ -74,7 +77,7 @@ class Layer:
         self.stride = stride
         self._s = _Layer(H, F, E, k, F32 if dtype == "f32" else BF16, _p(self.router_w),
                          _p(self.router_b), _p(self.experts), stride,
-                         {"softmax": GATE_SOFTMAX, "raw": GATE_RAW}[gate])
+                         {"softmax": GATE_SOFTMAX, "raw": GATE_RAW}[gate], capacity)
 
     @property
     def ref(self):
@@ -110,17 +113,21 @@ class Layer:
                                        _p(r["perm"]), _p(r["inv"])), "layer_forward")
         return r
 
-    def tokens(self, x, tokens, idx_override=None):
-        """Output rows of the listed tokens only: dict y, idx, w, logits."""
+    def tokens(self, x, tokens, idx_override=None, keep=None):
+        """Output rows of the listed tokens only: dict y, idx, w, logits.
+        keep [n, k] (optional): slots that count (a capacity's drops)."""
         x = self._x(x)
         tokens = np.ascontiguousarray(tokens, np.int32)
         n, k = tokens.size, self.k
         ov = None if idx_override is None else np.ascontiguousarray(idx_override, np.int32)
         if ov is not None:
             assert ov.shape == (n, k)
+        kp = None if keep is None else np.ascontiguousarray(keep, np.int32)
+        if kp is not None:
+            assert kp.shape == (n, k)
         r = dict(y=np.empty((n, self.H), np.float64), idx=np.empty((n, k), np.int32),
                  w=np.empty((n, k), np.float64), logits=np.empty((n, self.E), np.float64))
-        _check(lib().orc_layer_tokens(self.ref, _p(x), x.shape[0], _p(tokens), n, _p(ov),
+        _check(lib().orc_layer_tokens(self.ref, _p(x), x.shape[0], _p(tokens), n, _p(ov), _p(kp),
                                       _p(r["y"]), _p(r["idx"]), _p(r["w"]), _p(r["logits"])),
                "layer_tokens")
         return r
@@ -146,15 +153,15 @@ def topk(logits, k, gate="softmax"):
     return idx, w
 
 
-def dispatch(idx, E):
+def dispatch(idx, E, capacity=0):
     idx = np.ascontiguousarray(idx, np.int32)
     T, k = idx.shape
     counts = np.empty(E, np.int32)
     offsets = np.empty(E + 1, np.int32)
     perm = np.empty(T * k, np.int32)
     inv = np.empty(T * k, np.int32)
-    _check(lib().orc_dispatch(T, E, k, _p(idx), _p(counts), _p(offsets), _p(perm), _p(inv)),
-           "dispatch")
+    _check(lib().orc_dispatch_cap(T, E, k, capacity, _p(idx), _p(counts), _p(offsets), _p(perm),
+                                  _p(inv)), "dispatch")
     return counts, offsets, perm, inv
 
 
@@ -185,6 +192,6 @@ def num_threads() -> int:
     return lib().orc_num_threads()
 
 
-def layer_from_gen(shape, router_w, router_b, experts, gate="softmax") -> Layer:
+def layer_from_gen(shape, router_w, router_b, experts, gate="softmax", capacity=0) -> Layer:
     return Layer(shape.H, shape.F, shape.E, shape.k, shape.dtype, router_w, router_b, experts,
-                 shape.stride, gate=gate)
+                 shape.stride, gate=gate, capacity=capacity)

@@ -44,6 +44,7 @@ static int check_layer(const orc_layer_t* L) {
   if (L->dtype != ORC_F32 && L->dtype != ORC_BF16) return -1;
   if (!L->router_w || !L->experts) return -1;
   if (L->gate != ORC_GATE_SOFTMAX && L->gate != ORC_GATE_RAW) return -1;
+  if (L->capacity < 0) return -1;
   if (L->stride < 3ull * (uint64_t)L->H * (uint64_t)L->F * elem_size(L->dtype)) return -1;
   return 0;
 }
@@ -129,26 +130,36 @@ int orc_topk_softmax(int32_t T, int32_t E, int32_t k, const double* logits, int3
   return orc_topk(T, E, k, ORC_GATE_SOFTMAX, logits, idx, w);
 }
 
-/* O4: counting sort of the T*k (token, slot) pairs by expert.  counts[e];
- * offsets = exclusive prefix sum of counts (E+1 entries); then pairs are
- * placed in order of ascending token, then ascending slot, each at the next
- * free position of its expert: perm[p] = t*k + j and inv[t*k + j] = p. */
-int orc_dispatch(int32_t T, int32_t E, int32_t k, const int32_t* idx, int32_t* counts,
-                 int32_t* offsets, int32_t* perm, int32_t* inv) {
-  if (T < 0 || E < 1 || k < 1 || !idx || !counts || !offsets || !perm || !inv) return -1;
+/* O4: counting sort of the T*k (token, slot) pairs by expert.  The pairs
+ * of each expert are taken in order of ascending token, then ascending slot.
+ * With a capacity C > 0 an expert keeps only its first C pairs, the rest are
+ * dropped (reading: lowest token index kept first).  counts[e] = the pairs
+ * kept; offsets = exclusive prefix sum of counts (E+1 entries); the kept
+ * pairs sit at the next free position of their expert: perm[p] = t*k + j,
+ * inv[t*k + j] = p; a dropped pair has inv = -1 and perm[p] = -1 for
+ * offsets[E] <= p < T*k. */
+int orc_dispatch_cap(int32_t T, int32_t E, int32_t k, int32_t cap, const int32_t* idx,
+                     int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv) {
+  if (T < 0 || E < 1 || k < 1 || cap < 0 || !idx || !counts || !offsets || !perm || !inv)
+    return -1;
   for (int32_t e = 0; e < E; ++e) counts[e] = 0;
   for (int32_t s = 0; s < T * k; ++s) {
     if (idx[s] < 0 || idx[s] >= E) return -1;
-    counts[idx[s]] += 1;
+    if (cap == 0 || counts[idx[s]] < cap) counts[idx[s]] += 1;
   }
   offsets[0] = 0;
   for (int32_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
   int32_t* next = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
   if (!next) return -1;
   for (int32_t e = 0; e < E; ++e) next[e] = offsets[e];
+  for (int32_t p = offsets[E]; p < T * k; ++p) perm[p] = -1;
   for (int32_t t = 0; t < T; ++t) {
     for (int32_t j = 0; j < k; ++j) {
       int32_t s = t * k + j;
+      if (next[idx[s]] == offsets[idx[s] + 1]) {  /* the expert is full */
+        inv[s] = -1;
+        continue;
+      }
       int32_t p = next[idx[s]]++;
       perm[p] = s;
       inv[s] = p;
@@ -156,6 +167,11 @@ int orc_dispatch(int32_t T, int32_t E, int32_t k, const int32_t* idx, int32_t* c
   }
   free(next);
   return 0;
+}
+
+int orc_dispatch(int32_t T, int32_t E, int32_t k, const int32_t* idx, int32_t* counts,
+                 int32_t* offsets, int32_t* perm, int32_t* inv) {
+  return orc_dispatch_cap(T, E, k, 0, idx, counts, offsets, perm, inv);
 }
 
 /* O5 for one row: g_f = sum_h x_h Wg[f][h], u_f = sum_h x_h Wu[f][h],
@@ -215,8 +231,8 @@ int orc_combine(int32_t T, int32_t H, int32_t k, const double* w, const int32_t*
   for (int32_t t = 0; t < T; ++t)
     for (int32_t h = 0; h < H; ++h) {
       double s = 0.0;
-      for (int32_t j = 0; j < k; ++j)
-        s += w[(size_t)t * k + j] * yp[(size_t)inv[t * k + j] * H + h];
+      for (int32_t j = 0; j < k; ++j)  /* a dropped pair (inv < 0) adds nothing */
+        if (inv[t * k + j] >= 0) s += w[(size_t)t * k + j] * yp[(size_t)inv[t * k + j] * H + h];
       y[(size_t)t * H + h] = s;
     }
   return 0;
@@ -234,7 +250,7 @@ int orc_layer_forward(const orc_layer_t* L, const void* x, int32_t T, double* y,
   int rc = (!logits || !yp) ? -1 : 0;
   if (!rc) rc = orc_logits(L, x, T, logits);
   if (!rc) rc = orc_topk(T, E, k, L->gate, logits, idx, w);
-  if (!rc) rc = orc_dispatch(T, E, k, idx, counts, offsets, perm, inv);
+  if (!rc) rc = orc_dispatch_cap(T, E, k, L->capacity, idx, counts, offsets, perm, inv);
   if (!rc) rc = orc_expert_rows(L, x, T, offsets, perm, yp);
   if (!rc) rc = orc_combine(T, H, k, w, inv, yp, y);
   free(logits);
@@ -244,13 +260,15 @@ int orc_layer_forward(const orc_layer_t* L, const void* x, int32_t T, double* y,
 
 /* The layer output of selected tokens only, straight from the per-token
  * definition y[t] = sum_j w_j * FFN_{idx_j}(x[t]) (the same value that
- * O1..O6 give row t).  tokens [ntok]; idx_override [ntok*k] or NULL: when
+ * O1..O6 give row t without a capacity).  keep [ntok*k] or NULL: with it,
+ * only the slots with keep != 0 count (a capacity's drops, which depend on
+ * the other tokens, are given by the caller).  tokens [ntok]; idx_override [ntok*k] or NULL: when
  * given, those experts (in that slot order) replace the top-k choice and the
  * weights are the gate (softmax or raw) of the oracle's logits at them.  Outputs y
  * [ntok*H], idx [ntok*k], w [ntok*k], logits [ntok*E]. */
 int orc_layer_tokens(const orc_layer_t* L, const void* x, int32_t T, const int32_t* tokens,
-                     int32_t ntok, const int32_t* idx_override, double* y, int32_t* idx,
-                     double* w, double* logits) {
+                     int32_t ntok, const int32_t* idx_override, const int32_t* keep, double* y,
+                     int32_t* idx, double* w, double* logits) {
   if (check_layer(L) || !x || T < 0 || ntok < 0 || !tokens || !y || !idx || !w || !logits)
     return -1;
   const int32_t H = L->H, E = L->E, k = L->k;
@@ -294,7 +312,9 @@ int orc_layer_tokens(const orc_layer_t* L, const void* x, int32_t T, const int32
     for (int32_t n = 0; n < ntok; ++n)
       for (int32_t h = 0; h < H; ++h) {
         double s = 0.0;
-        for (int32_t j = 0; j < k; ++j) s += w[(size_t)n * k + j] * ye[((size_t)n * k + j) * H + h];
+        for (int32_t j = 0; j < k; ++j)
+          if (!keep || keep[(size_t)n * k + j])
+            s += w[(size_t)n * k + j] * ye[((size_t)n * k + j) * H + h];
         y[(size_t)n * H + h] = s;
       }
   }

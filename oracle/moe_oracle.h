@@ -19,7 +19,12 @@
  *            router of m.nxbn.cn/news/47896 sec. 3.2 and of
  *            www.pnsm.cn/news/1892388.html sec. 3.3).
  *   dispatch the (token, slot) pairs grouped by expert into one batch per
- *            expert: zskr.cn page sec. 3.3, stage 3.
+ *            expert: zskr.cn page sec. 3.3, stage 3.  Optional expert
+ *            capacity C: an expert takes at most C pairs per call, the rest
+ *            are dropped (www.cf-1.com/news/4750020/ sec. 4.2,
+ *            --expert-capacity; zskr.cn page sec. 2.2, hard_capacity);
+ *            reading: the pairs of lowest token index (then slot) are kept,
+ *            a dropped pair adds nothing, the other weights are unchanged.
  *   expert   SwiGLU without bias, gate/up of shape (intermediate, hidden),
  *            down of shape (hidden, intermediate): zskr.cn page sec. 3.1 and
  *            sec. 3.3 stage 4 (gate_proj, up_proj, SiLU, down_proj).
@@ -62,7 +67,8 @@ typedef struct {
   const float* router_b;
   const void* experts;
   uint64_t stride;
-  int32_t gate;  /* ORC_GATE_SOFTMAX or ORC_GATE_RAW */
+  int32_t gate;      /* ORC_GATE_SOFTMAX or ORC_GATE_RAW */
+  int32_t capacity;  /* pairs an expert takes per call; 0 = no limit */
 } orc_layer_t;
 
 int orc_logits(const orc_layer_t* L, const void* x, int32_t T, double* logits);
@@ -73,6 +79,9 @@ int orc_topk(int32_t T, int32_t E, int32_t k, int32_t gate, const double* logits
              int32_t* idx, double* w);
 int orc_dispatch(int32_t T, int32_t E, int32_t k, const int32_t* idx, int32_t* counts,
                  int32_t* offsets, int32_t* perm, int32_t* inv);
+/* the same with capacity cap (0 = none): dropped pairs get inv = -1 */
+int orc_dispatch_cap(int32_t T, int32_t E, int32_t k, int32_t cap, const int32_t* idx,
+                     int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv);
 int orc_expert_ffn(const orc_layer_t* L, int32_t e, const double* xrow, double* yrow);
 int orc_expert_rows(const orc_layer_t* L, const void* x, int32_t T, const int32_t* offsets,
                     const int32_t* perm, double* yp);
@@ -82,8 +91,8 @@ int orc_layer_forward(const orc_layer_t* L, const void* x, int32_t T, double* y,
                       double* w, int32_t* counts, int32_t* offsets, int32_t* perm,
                       int32_t* inv);
 int orc_layer_tokens(const orc_layer_t* L, const void* x, int32_t T, const int32_t* tokens,
-                     int32_t ntok, const int32_t* idx_override, double* y, int32_t* idx,
-                     double* w, double* logits);
+                     int32_t ntok, const int32_t* idx_override, const int32_t* keep, double* y,
+                     int32_t* idx, double* w, double* logits);
 int orc_prenorm_bf16(int32_t T, int32_t H, const float* h, uint16_t* xt);
 double orc_bf16_round(double v);
 int orc_num_threads(void);

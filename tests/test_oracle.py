@@ -292,6 +292,87 @@ def test_soft_routing_k_equals_E_is_dense_softmax_mixture(dtype):
     assert np.abs(r["y"] - y).max() <= 1e-12 * np.sqrt((y ** 2).mean())
 
 
+# --- expert capacity with token dropping -------------------------------------
+
+
+def _capacity_reference(idx, E, cap):
+    """Independent statement of the rule: per expert, its (token, slot) pairs
+    in ascending slot id s = t*k + j, the first `cap` kept."""
+    flat = idx.ravel()
+    keep = np.zeros(flat.size, bool)
+    for e in range(E):
+        s_e = np.flatnonzero(flat == e)          # ascending
+        keep[s_e[:cap] if cap > 0 else s_e] = True
+    return keep
+
+
+@pytest.mark.parametrize("E,k,T,cap", [(8, 2, 300, 50), (5, 3, 64, 7), (16, 1, 40, 1), (4, 4, 30, 30)])
+def test_capacity_dispatch_brute_force(E, k, T, cap):
+    rng = np.random.default_rng(E * 100 + cap)
+    # heavily skewed routing: experts 0 and 1 get most pairs
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    idx[: T // 2, 0] = 0
+    idx[: T // 2, 1 % k] = 1 if k > 1 else 0
+    for t in range(T):  # keep the k experts of a token distinct
+        if len(set(idx[t])) < k:
+            idx[t] = rng.permutation(E)[:k]
+    counts, offsets, perm, inv = oracle.dispatch(idx, E, capacity=cap)
+    keep = _capacity_reference(idx, E, cap)
+    raw = np.bincount(idx.ravel(), minlength=E)
+    assert (counts == np.minimum(raw, cap)).all()
+    assert offsets[0] == 0 and (np.diff(offsets) == counts).all()
+    nk = int(offsets[-1])
+    assert (inv[~keep] == -1).all() and (perm[nk:] == -1).all()
+    kept_s = np.flatnonzero(keep)
+    assert sorted(perm[:nk].tolist()) == kept_s.tolist()          # a bijection onto the kept pairs
+    assert (inv[perm[:nk]] == np.arange(nk)).all()
+    for e in range(E):                                           # expert-major, slot order inside
+        seg = perm[offsets[e]:offsets[e + 1]]
+        assert (idx.ravel()[seg] == e).all() and (np.diff(seg) > 0).all()
+
+
+def test_capacity_at_or_above_the_largest_count_changes_nothing():
+    shape, L0, wr, ex = make_layer(16, 24, 8, 2)
+    x = gen.gen_x(shape, 40)
+    r0 = L0.forward(x)
+    cap = int(r0["counts"].max())
+    for c in (cap, cap + 5):
+        r = oracle.layer_from_gen(shape, wr, None, ex, capacity=c).forward(x)
+        for key in ("y", "idx", "w", "counts", "offsets", "perm", "inv"):
+            assert np.array_equal(r[key], r0[key]), (c, key)
+
+
+@pytest.mark.parametrize("dtype,cap", [("f32", 3), ("bf16", 5), ("f32", 1)])
+def test_capacity_forward_equals_dense_masked(dtype, cap):
+    H, F, E, k, T = 16, 24, 6, 2, 25
+    shape, _, wr, ex = make_layer(H, F, E, k, dtype=dtype)
+    L = oracle.layer_from_gen(shape, wr, None, ex, capacity=cap)
+    x = gen.gen_x(shape, T)
+    r = L.forward(x)
+    X = widen(x, dtype)
+    logits = X @ widen(wr, dtype)
+    order = np.argsort(-logits, axis=1, kind="stable")[:, :k]
+    assert (order == r["idx"]).all()
+    sel = np.take_along_axis(logits, order, 1)
+    g = np.exp(sel - sel[:, :1])
+    gates = g / g.sum(1, keepdims=True)
+    keep = _capacity_reference(order, E, cap).reshape(T, k)
+    assert keep.sum() < T * k                                      # the capacity bites
+    y = np.zeros((T, H))
+    for e in range(E):
+        Wg, Wu, Wd = (widen(m, dtype) for m in gen.expert_views(shape, ex, e))
+        a = silu(X @ Wg.T) * (X @ Wu.T)
+        if dtype == "bf16":
+            a = np.vectorize(oracle.bf16_round)(a)
+        ye = a @ Wd.T
+        wcol = np.where((order == e) & keep, gates, 0.0).sum(1)      # unrenormalised weights
+        y += wcol[:, None] * ye
+    assert np.abs(r["y"] - y).max() <= 1e-12 * np.sqrt((y ** 2).mean())
+    toks = np.array([0, 7, 24], np.int32)
+    t = L.tokens(x, toks, keep=keep[toks].astype(np.int32))
+    assert np.array_equal(t["y"], r["y"][toks])
+
+
 # --- P8: algebraic properties --------------------------------------------
 
 
