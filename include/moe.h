@@ -102,6 +102,16 @@ typedef struct {
                              so g_f = sum_h x_h Wg[f][h] and
                              y_h = sum_f a_f Wd[h][f] */
   uint64_t expert_stride; /* bytes, >= 3*H*F*sizeof(dtype), multiple of 256 */
+  int32_t expert_capacity;/* (token, slot) pairs an expert takes per call, 0 = no
+                             limit.  Pairs beyond it are dropped: the pairs of
+                             each expert are taken in ascending token (then
+                             slot) order and the first expert_capacity kept; a
+                             dropped pair adds nothing to its token's output and
+                             the other gate weights are unchanged (the pages'
+                             hard_capacity, www.cf-1.com/news/4750020/ sec. 4.2
+                             --expert-capacity; zskr.cn page sec. 2.2).  A soft
+                             capacity is a larger value of this limit. */
+  int32_t reserved;       /* 0 */
 } moe_layer_desc;
 
 /* Validates *d, allocates the workspace for d->max_tokens on the current
@@ -118,12 +128,15 @@ moe_layer_t* moe_layer_create(const moe_layer_desc* d, int* status);
  *              logits are used as they are
  *   topk_idx   [T][k] int32 out: expert of slot j of token t, slots ordered by
  *              descending logit, equal logits by ascending expert index
- *   topk_w     [T][k] fp32 out: softmax of the selected logits
- *   counts     [E] int32 out or NULL: tokens routed to each expert
+ *   topk_w     [T][k] fp32 out: softmax of the selected logits (the logits
+ *              themselves with MOE_FLAG_GATE_RAW)
+ *   counts     [E] int32 out or NULL: pairs each expert takes (routed, capped
+ *              at expert_capacity)
  *   offsets    [E+1] int32 out or NULL: exclusive prefix sum of counts
  *   perm       [T*k] int32 out or NULL: perm[p] = t*k + j of the p-th pair in
- *              (expert, token) order
- *   inv        [T*k] int32 out or NULL: inv[t*k + j] = p, the inverse of perm */
+ *              (expert, token) order, p < offsets[E]; -1 beyond
+ *   inv        [T*k] int32 out or NULL: inv[t*k + j] = p, the inverse of perm,
+ *              or -1 for a pair dropped by the capacity */
 int moe_route(moe_layer_t* L, const void* x, int32_t T, const float* logits_in,
               int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
               int32_t* perm, int32_t* inv, void* stream);

@@ -46,7 +46,8 @@ class moe_layer_desc(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
                 ("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
-                ("expert_base", ctypes.c_void_p), ("expert_stride", ctypes.c_uint64)]
+                ("expert_base", ctypes.c_void_p), ("expert_stride", ctypes.c_uint64),
+                ("expert_capacity", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _LIB = None
@@ -93,10 +94,10 @@ def _stream(s):
 
 
 def make_desc(hidden, ffn, num_experts, top_k, max_tokens, dtype, router_w, expert_base,
-              expert_stride, router_b=None, flags=0) -> moe_layer_desc:
+              expert_stride, router_b=None, flags=0, expert_capacity=0) -> moe_layer_desc:
     return moe_layer_desc(ctypes.sizeof(moe_layer_desc), hidden, ffn, num_experts, top_k,
                           max_tokens, dtype, flags, _ptr(router_w), _ptr(router_b),
-                          _ptr(expert_base), expert_stride)
+                          _ptr(expert_base), expert_stride, expert_capacity, 0)
 
 
 def moe_layer_create(desc: moe_layer_desc) -> int:
@@ -140,14 +141,15 @@ class MoELayer:
     """Owns a libmoe layer handle and keeps the weight tensors it borrows alive."""
 
     def __init__(self, hidden, ffn, num_experts, top_k, max_tokens, dtype, router_w, experts,
-                 expert_stride, router_b=None, flags=0):
+                 expert_stride, router_b=None, flags=0, expert_capacity=0):
         self._keep = (router_w, experts, router_b)
         self.H, self.F, self.E, self.k = hidden, ffn, num_experts, top_k
         self.max_tokens = max_tokens
         self.dtype = dtype
         self.flags = flags
+        self.expert_capacity = expert_capacity
         desc = make_desc(hidden, ffn, num_experts, top_k, max_tokens, dtype, router_w, experts,
-                         expert_stride, router_b, flags)
+                         expert_stride, router_b, flags, expert_capacity)
         self.handle = moe_layer_create(desc)
 
     def forward(self, x, y, T=None, stream=None):

@@ -1,6 +1,7 @@
 // combine.hip -- step 5: y[t] = sum_{j<k} w[t][j] * yp[inv[t*k+j]], slots in
-// ascending order, one fp32 fused multiply-add per slot, no atomics; plus the
-// residual h[t] when the layer runs inside a residual stack.
+// ascending order, one fp32 fused multiply-add per slot, no atomics, slots
+// dropped by an expert capacity (inv < 0) skipped; plus the residual h[t]
+// when the layer runs inside a residual stack.
 //
 // The pages accumulate the K expert outputs weighted by their gate scores
 // [zskr.cn/news/2275853 "Colibri：面向MoE架构的C语言高效推理引擎解析" sec. 3.3
@@ -28,7 +29,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   f32x4 acc{0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < k; ++j) {
     const float wj = w[(size_t)t * k + j];
-    const int p = min(max(inv[(size_t)t * k + j], 0), S - 1);  // in range by construction
+    const int pi = inv[(size_t)t * k + j];
+    if (pi < 0) continue;  // a pair dropped by the expert capacity
+    const int p = min(pi, S - 1);  // in range by construction
     f32x4 v = *reinterpret_cast<const f32x4*>(yp + (size_t)p * H + c);
     for (int pl = 1; pl < nplanes; ++pl)  // partial sums of a split K, in plane order
       v += *reinterpret_cast<const f32x4*>(yp + ((size_t)pl * S + p) * H + c);

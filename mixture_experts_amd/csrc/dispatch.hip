@@ -6,6 +6,11 @@
 // s = t*k + j by expert: counts[e], offsets = exclusive prefix sum,
 // perm[p] = s for the p-th pair in (expert, token) order, inv[s] = p.
 //
+// With a capacity C an expert keeps the first C of its pairs in slot order
+// (www.cf-1.com/news/4750020/ sec. 4.2, --expert-capacity): counts, offsets
+// and the tile schedule count the kept pairs, a dropped pair gets inv = -1,
+// perm is -1 beyond the kept pairs.
+//
 // Three kernels, all deterministic (no ordering depends on atomics):
 //   hist    one wave per run of 512 slots; the rank of a slot among the
 //           earlier slots of the same expert in its run comes from a
@@ -51,16 +56,16 @@ __global__ __launch_bounds__(64) void dispatch_hist_kernel(const int32_t* __rest
   for (int e = lane; e < E; e += 64) hist[(size_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// One workgroup of MOE_MAX_EXPERTS threads.  base[r][e] = offsets[e] + sum of
-// hist[r'][e] for r' < r.  tile_off[e] = sum over e' < e of ceil(counts[e'] /
-// tile_rows).  active[0..n) = the experts with counts > 0, ascending;
-// active[E] = n.
+// One workgroup of MOE_MAX_EXPERTS threads.  base[r][e] = sum of hist[r'][e]
+// for r' < r (the expert's pairs in earlier runs).  counts[e] = the pairs
+// kept (capped at cap when cap > 0).  tile_off[e] = sum over e' < e of
+// ceil(counts[e'] / tile_rows).  active[0..n) = the experts with counts > 0,
+// ascending; active[E] = n.
 __global__ __launch_bounds__(MOE_MAX_EXPERTS) void dispatch_scan_kernel(
-    const int32_t* __restrict__ hist, int nrun, int E, int tile_rows,
+    const int32_t* __restrict__ hist, int nrun, int E, int tile_rows, int cap,
     int32_t* __restrict__ base, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ tile_off, int32_t* __restrict__ active) {
   __shared__ int32_t sc[MOE_MAX_EXPERTS];
-  __shared__ int32_t so[MOE_MAX_EXPERTS + 1];
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
@@ -69,6 +74,7 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void dispatch_scan_kernel(
       base[(size_t)r * E + e] = run;
       run += h;
     }
+    if (cap > 0 && run > cap) run = cap;
     counts[e] = run;
   }
   sc[e] = (e < E) ? run : 0;
@@ -76,40 +82,39 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void dispatch_scan_kernel(
   if (e == 0) {
     int o = 0, t = 0, n = 0;
     for (int i = 0; i < E; ++i) {
-      so[i] = o;
       offsets[i] = o;
       tile_off[i] = t;
       o += sc[i];
       t += (sc[i] + tile_rows - 1) / tile_rows;
       if (sc[i] > 0) active[n++] = i;
     }
-    so[E] = o;
     offsets[E] = o;
     tile_off[E] = t;
     active[E] = n;
-  }
-  __syncthreads();
-  if (e < E) {
-    const int o = so[e];
-    for (int r = 0; r < nrun; ++r) base[(size_t)r * E + e] += o;
   }
 }
 
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ rank,
-    const int32_t* __restrict__ base, int S, int E, int32_t* __restrict__ perm,
-    int32_t* __restrict__ inv) {
+    const int32_t* __restrict__ base, const int32_t* __restrict__ offsets, int S, int E,
+    int cap, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
   const int s = blockIdx.x * 256 + threadIdx.x;
   if (s >= S) return;
   const int e = idx[s];
-  const int p = base[(size_t)(s / DISPATCH_RUN) * E + e] + rank[s];
-  // p is in [0, S) by construction; the guard keeps a logic error from
-  // turning into an out-of-bounds store (inv then points at a valid row)
+  const int g = base[(size_t)(s / DISPATCH_RUN) * E + e] + rank[s];  // rank in the expert
+  if (s >= offsets[E]) perm[s] = -1;  // beyond the kept pairs (never a kept p below)
+  if (cap > 0 && g >= cap) {
+    inv[s] = -1;  // dropped
+    return;
+  }
+  const int p = offsets[e] + g;
+  // p is in [0, offsets[E]) by construction; the guard keeps a logic error
+  // from turning into an out-of-bounds store
   if (p >= 0 && p < S) {
     perm[p] = s;
     inv[s] = p;
   } else {
-    inv[s] = 0;
+    inv[s] = -1;
   }
 }
 
@@ -121,10 +126,10 @@ int launch_dispatch(const DispatchArgs& a, hipStream_t st) {
   int nbits = 0;
   while ((1 << nbits) < a.E) ++nbits;
   dispatch_hist_kernel<<<nrun, 64, 0, st>>>(a.idx, S, a.E, nbits, a.hist, a.rank);
-  dispatch_scan_kernel<<<1, MOE_MAX_EXPERTS, 0, st>>>(a.hist, nrun, a.E, a.tile_rows, a.base,
-                                                      a.counts, a.offsets, a.tile_off,
-                                                      a.active);
-  dispatch_scatter_kernel<<<(S + 255) / 256, 256, 0, st>>>(a.idx, a.rank, a.base, S, a.E,
-                                                           a.perm, a.inv);
+  dispatch_scan_kernel<<<1, MOE_MAX_EXPERTS, 0, st>>>(a.hist, nrun, a.E, a.tile_rows,
+                                                      a.capacity, a.base, a.counts, a.offsets,
+                                                      a.tile_off, a.active);
+  dispatch_scatter_kernel<<<(S + 255) / 256, 256, 0, st>>>(a.idx, a.rank, a.base, a.offsets, S,
+                                                           a.E, a.capacity, a.perm, a.inv);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

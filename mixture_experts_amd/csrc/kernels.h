@@ -41,6 +41,7 @@ struct DispatchArgs {
   int32_t* active;     // [E+1]
   int32_t* perm;       // [S]
   int32_t* inv;        // [S]
+  int capacity;        // pairs an expert keeps, 0 = all
 };
 
 struct ExpertArgs {

@@ -89,6 +89,7 @@ int validate_desc(const moe_layer_desc* d) {
   if (S * (H > F ? H : F) >= lim || 3 * H * F >= lim || (uint64_t)d->max_tokens * H >= lim)
     return MOE_ERR_UNSUPPORTED;
   if (d->expert_stride % es) return MOE_ERR_INVALID_ARG;
+  if (d->expert_capacity < 0 || d->reserved != 0) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
@@ -165,7 +166,8 @@ int run_route(moe_layer* L, const void* x_route, int T, const float* logits_in,
                 d.router_w, d.router_b, logits_in, L->idx, L->w, L->part,
                 (d.flags & MOE_FLAG_GATE_RAW) ? 1 : 0};
   DispatchArgs da{L->idx, T * d.top_k, d.num_experts, tile_rows, L->hist, L->rank, L->base,
-                  L->counts, L->offsets, L->tile_off, L->active, L->perm, L->inv};
+                  L->counts, L->offsets, L->tile_off, L->active, L->perm, L->inv,
+                  d.expert_capacity};
   if (small_route(L, T, logits_in)) return launch_route_small(ra, da, L->sync, st) ? MOE_ERR_DEVICE : MOE_OK;
   if (launch_router(ra, st)) return MOE_ERR_DEVICE;
   if (launch_dispatch(da, st)) return MOE_ERR_DEVICE;
@@ -291,7 +293,7 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
                   dd.router_b, nullptr, L->idx, L->w, L->part,
                   (dd.flags & MOE_FLAG_GATE_RAW) ? 1 : 0};
     DispatchArgs da{L->idx, S, dd.num_experts, GG_BT, L->hist, L->rank, L->base, L->counts,
-                    L->offsets, L->tile_off, L->active, L->perm, L->inv};
+                    L->offsets, L->tile_off, L->active, L->perm, L->inv, dd.expert_capacity};
     if (small_route(L, T, nullptr)) {  // one launch: the dispatch stage is empty
       if (launch_route_small(ra, da, L->sync, st)) return MOE_ERR_DEVICE;
       if (!mark(MOE_STAGE_DISPATCH)) return MOE_ERR_DEVICE;

@@ -146,9 +146,11 @@ __device__ void topk_rows16(const float* lg, int ldl, int tile0, int T, int E, i
 
 // Dispatch of S = T*k <= RT_TOK*8 slots whose expert ids are in LDS
 // (idx_lds[S]): wave 0 ranks the slots of each expert with ballot matches
-// in slot order, one thread scans the counts, every thread scatters.  Same
-// stable counting sort as the dispatch kernels.  cnt, off_l, rank_l: LDS.
-__device__ void dispatch_small(const int32_t* idx_lds, int S, int E, int tile_rows,
+// in slot order, one thread scans the counts (capped at cap > 0), every
+// thread scatters (a slot ranked at or beyond cap is dropped: inv = -1).
+// Same stable counting sort as the dispatch kernels.  cnt, off_l, rank_l:
+// LDS.
+__device__ void dispatch_small(const int32_t* idx_lds, int S, int E, int tile_rows, int cap,
                                int32_t* cnt, int32_t* off_l, int32_t* rank_l,
                                int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                int32_t* __restrict__ tile_off, int32_t* __restrict__ active,
@@ -183,13 +185,14 @@ __device__ void dispatch_small(const int32_t* idx_lds, int S, int E, int tile_ro
   if (tid == 0) {
     int o = 0, tt = 0, n = 0;
     for (int e = 0; e < E; ++e) {
+      const int c = (cap > 0 && cnt[e] > cap) ? cap : cnt[e];  // pairs kept
       off_l[e] = o;
       offsets[e] = o;
-      counts[e] = cnt[e];
+      counts[e] = c;
       tile_off[e] = tt;
-      o += cnt[e];
-      tt += (cnt[e] + tile_rows - 1) / tile_rows;
-      if (cnt[e] > 0) active[n++] = e;
+      o += c;
+      tt += (c + tile_rows - 1) / tile_rows;
+      if (c > 0) active[n++] = e;
     }
     off_l[E] = o;
     offsets[E] = o;
@@ -198,6 +201,11 @@ __device__ void dispatch_small(const int32_t* idx_lds, int S, int E, int tile_ro
   }
   __syncthreads();
   for (int sl = tid; sl < S; sl += blockDim.x) {
+    if (sl >= off_l[E]) perm[sl] = -1;  // beyond the kept pairs
+    if (cap > 0 && rank_l[sl] >= cap) {
+      inv[sl] = -1;  // dropped
+      continue;
+    }
     const int p = off_l[idx_lds[sl]] + rank_l[sl];
     perm[p] = sl;
     inv[sl] = p;
@@ -357,7 +365,7 @@ template <int NT>
 __global__ __launch_bounds__(256) void route_small_kernel(
     const uint16_t* __restrict__ x, int T, int H, int E, int k, int raw,
     const uint16_t* __restrict__ wr, const float* __restrict__ bias, int hslice,
-    float* __restrict__ part, int32_t* __restrict__ counter, int tile_rows,
+    float* __restrict__ part, int32_t* __restrict__ counter, int tile_rows, int cap,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off,
     int32_t* __restrict__ active, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
@@ -435,7 +443,7 @@ __global__ __launch_bounds__(256) void route_small_kernel(
   topk_rows(lg, ldl, 0, T, E, k, raw, idx_out, w_out, 4, idx_l);
   __syncthreads();
   if (tid == 0) *counter = 0;  // ready for the next launch
-  dispatch_small(idx_l, T * k, E, tile_rows, cnt, off_l, rank_l, counts, offsets, tile_off,
+  dispatch_small(idx_l, T * k, E, tile_rows, cap, cnt, off_l, rank_l, counts, offsets, tile_off,
                  active, perm, inv);
 }
 
@@ -450,7 +458,7 @@ constexpr int R1_LDW = R1_HMAX + 8;  // padded router row (bf16)
 template <int MB, int EV>
 __global__ __launch_bounds__(1024) void route_one_kernel(
     const uint16_t* __restrict__ x, int T, int H, int E, int k, int raw,
-    const uint16_t* __restrict__ wr, const float* __restrict__ bias, int tile_rows,
+    const uint16_t* __restrict__ wr, const float* __restrict__ bias, int tile_rows, int cap,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off,
     int32_t* __restrict__ active, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
@@ -561,7 +569,7 @@ __global__ __launch_bounds__(1024) void route_one_kernel(
   __syncthreads();
   topk_rows16(lg, 17, 0, T, E, k, raw, idx_out, w_out, 16, idx_l, RT_TOK);
   __syncthreads();
-  dispatch_small(idx_l, T * k, E, tile_rows, cnt, off_l, rank_l, counts, offsets, tile_off,
+  dispatch_small(idx_l, T * k, E, tile_rows, cap, cnt, off_l, rank_l, counts, offsets, tile_off,
                  active, perm, inv);
 }
 
@@ -618,7 +626,7 @@ int launch_route_small(const RouterArgs& a, const DispatchArgs& d, int32_t* coun
   if (a.E <= 16 && a.H <= R1_HMAX && a.H % 512 == 0 && a.T <= RT_TOK) {
     auto* xx = (const uint16_t*)a.x;
     auto* ww = (const uint16_t*)a.wr;
-#define R1_ARGS xx, a.T, a.H, a.E, a.k, a.raw_gate, ww, a.bias, d.tile_rows, a.idx, a.w, d.counts, \
+#define R1_ARGS xx, a.T, a.H, a.E, a.k, a.raw_gate, ww, a.bias, d.tile_rows, d.capacity, a.idx, a.w, d.counts, \
                 d.offsets, d.tile_off, d.active, d.perm, d.inv
     const int mb = (a.T + 15) / 16;
 #define R1_MB(EV)                                                         \
@@ -636,7 +644,7 @@ int launch_route_small(const RouterArgs& a, const DispatchArgs& d, int32_t* coun
   const int nt = (a.E + 15) / 16;
   auto* xx = (const uint16_t*)a.x;
   auto* ww = (const uint16_t*)a.wr;
-#define RS_ARGS xx, a.T, a.H, a.E, a.k, a.raw_gate, ww, a.bias, hs, a.part, counter, d.tile_rows, a.idx, a.w, \
+#define RS_ARGS xx, a.T, a.H, a.E, a.k, a.raw_gate, ww, a.bias, hs, a.part, counter, d.tile_rows, d.capacity, a.idx, a.w, \
                 d.counts, d.offsets, d.tile_off, d.active, d.perm, d.inv
   if (nt <= 1) route_small_kernel<1><<<ns, 256, 0, st>>>(RS_ARGS);
   else if (nt <= 2) route_small_kernel<2><<<ns, 256, 0, st>>>(RS_ARGS);

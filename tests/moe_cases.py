@@ -43,7 +43,7 @@ class Case:
     """A device layer and the oracle over the very same host arrays."""
 
     def __init__(self, shape: gen.LayerShape, max_tokens: int, flags: int = 0, layer: int = 0,
-                 router=None, bias="default", experts=None):
+                 router=None, bias="default", experts=None, capacity: int = 0):
         wr, b, ex = host_inputs(shape, layer) if router is None or experts is None else (
             None, None, None)
         self.router = wr if router is None else router
@@ -54,10 +54,13 @@ class Case:
         self.d_router = to_dev(self.router)
         self.d_bias = None if self.bias is None else to_dev(self.bias)
         self.d_experts = to_dev(self.experts)
+        self.capacity = capacity
         self.layer = moe.MoELayer(shape.H, shape.F, shape.E, shape.k, max_tokens, dt,
-                                  self.d_router, self.d_experts, shape.stride, self.d_bias, flags)
+                                  self.d_router, self.d_experts, shape.stride, self.d_bias, flags,
+                                  expert_capacity=capacity)
         gate = "raw" if flags & moe.MOE_FLAG_GATE_RAW else "softmax"
-        self.orc = oracle.layer_from_gen(shape, self.router, self.bias, self.experts, gate=gate)
+        self.orc = oracle.layer_from_gen(shape, self.router, self.bias, self.experts, gate=gate,
+                                         capacity=capacity)
 
     def forward(self, x_np: np.ndarray) -> np.ndarray:
         x = to_dev(x_np)
@@ -84,8 +87,13 @@ def near_tie_gap(logits: np.ndarray, k: int) -> np.ndarray:
 
 
 def check_rows(case: Case, x_np: np.ndarray, tokens, y_gpu_rows: np.ndarray,
-               gpu_idx_rows: np.ndarray, tol: float | None = None) -> dict:
-    """Compare GPU output rows of `tokens` with the oracle, near-tie rule applied."""
+               gpu_idx_rows: np.ndarray, tol: float | None = None,
+               keep_rows: np.ndarray | None = None) -> dict:
+    """Compare GPU output rows of `tokens` with the oracle, near-tie rule applied.
+    keep_rows [len(tokens), k]: with an expert capacity, the slots that are
+    kept under the GPU's routing of all tokens (which tokens an expert drops
+    depends on the others); the reference then uses the GPU's experts for
+    every row, after the near-tie check has validated them."""
     k = case.shape.k
     tol = TOL[case.shape.dtype] if tol is None else tol
     tokens = np.asarray(tokens, np.int32)
@@ -109,6 +117,10 @@ def check_rows(case: Case, x_np: np.ndarray, tokens, y_gpu_rows: np.ndarray,
         fix = np.nonzero(differs)[0]
         r2 = case.orc.tokens(x_np, tokens[fix], idx_override=gpu_idx_rows[fix])
         y_ref[fix] = r2["y"]
+    if keep_rows is not None:
+        y_ref = case.orc.tokens(x_np, tokens, idx_override=gpu_idx_rows,
+                                keep=np.asarray(keep_rows, np.int32).reshape(len(tokens), k))["y"]
+        stats["dropped_slots"] = int((np.asarray(keep_rows) == 0).sum())
     rms = float(np.sqrt(np.mean(y_ref ** 2)))
     err = float(np.abs(y_gpu_rows.astype(np.float64) - y_ref).max()) if len(tokens) else 0.0
     stats.update(rms=rms, max_err=err, rel=err / rms if rms > 0 else err)

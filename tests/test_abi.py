@@ -33,9 +33,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_desc_layout():
-    assert ctypes.sizeof(moe.moe_layer_desc) == 64
+    assert ctypes.sizeof(moe.moe_layer_desc) == 72
     assert moe.moe_layer_desc.router_w.offset == 32
     assert moe.moe_layer_desc.expert_stride.offset == 56
+    assert moe.moe_layer_desc.expert_capacity.offset == 64
 
 
 def _desc(**kw):
@@ -61,6 +62,7 @@ def _desc(**kw):
     (dict(expert_stride=3 * 256 * 256 * 2 - 256), moe.MOE_ERR_INVALID_ARG),
     (dict(expert_stride=3 * 256 * 256 * 2 + 128), moe.MOE_ERR_INVALID_ARG),
     (dict(flags=1 << 7), moe.MOE_ERR_INVALID_ARG),
+    (dict(expert_capacity=-1), moe.MOE_ERR_INVALID_ARG),
     (dict(flags=moe.MOE_FLAG_PATH_GROUPED | moe.MOE_FLAG_PATH_STREAM), moe.MOE_ERR_INVALID_ARG),
     (dict(num_experts=300, top_k=2), moe.MOE_ERR_UNSUPPORTED),
     (dict(top_k=9, num_experts=16), moe.MOE_ERR_UNSUPPORTED),
@@ -79,7 +81,15 @@ def test_create_rejects_bad_descriptors(kw, code):
 
 def test_struct_size_is_checked():
     d = _desc()
-    d.struct_size = 60
+    d.struct_size = 64
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_layer_create(d)
+    assert ei.value.code == moe.MOE_ERR_INVALID_ARG
+
+
+def test_reserved_field_must_be_zero():
+    d = _desc()
+    d.reserved = 1
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_layer_create(d)
     assert ei.value.code == moe.MOE_ERR_INVALID_ARG

@@ -20,9 +20,10 @@ def _log(*a):
     print(*a, flush=True)
 
 
-def routing_reference(logits32: np.ndarray, E: int, k: int, gate: str = "softmax"):
+def routing_reference(logits32: np.ndarray, E: int, k: int, gate: str = "softmax",
+                      capacity: int = 0):
     idx, w = oracle.topk(logits32.astype(np.float64), k, gate)
-    counts, offsets, perm, inv = oracle.dispatch(idx, E)
+    counts, offsets, perm, inv = oracle.dispatch(idx, E, capacity)
     return dict(idx=idx.ravel(), w=w.ravel(), counts=counts, offsets=offsets, perm=perm, inv=inv)
 
 
@@ -264,3 +265,79 @@ def test_grouped_path_matches_stream_path_on_every_row(name, shape, T):
     row_err = np.abs(g - s).max(axis=1)
     _log(f"  max |grouped - stream| / rms = {row_err.max() / rms:.3e}")
     assert np.all(row_err <= 1e-2 * rms), np.nonzero(row_err > 1e-2 * rms)[0][:20]
+
+
+# ------------------------------------------------------- expert capacity ---
+
+
+@pytest.mark.parametrize("E,k,T,cap", [(8, 2, 300, 40), (8, 2, 1000, 100), (64, 2, 777, 10),
+                                       (3, 3, 100, 1), (128, 4, 2500, 60), (8, 2, 20, 100)])
+def test_route_capacity_given_logits_bit_exact(E, k, T, cap):
+    """Capacity on the multi-run dispatch kernels: counts capped, the first
+    pairs of each expert in slot order kept, dropped pairs inv = -1, perm -1
+    beyond the kept pairs; bit-exact against the oracle."""
+    _log("route capacity", E, k, T, cap)
+    rng = np.random.default_rng(11 * E + T)
+    lg = rng.normal(0, 1.5, (T, E)).astype(np.float32)
+    lg[:, 0] += 1.0  # skew: expert 0 over-subscribed
+    c = Case(f32_shape(E, k), T, capacity=cap)
+    gpu = c.layer.route(None, T, logits_in=torch.from_numpy(lg).cuda())
+    torch.cuda.synchronize()
+    gpu = {kk: v.cpu().numpy() for kk, v in gpu.items()}
+    ref = routing_reference(lg, E, k, capacity=cap)
+    assert_routing_equal(gpu, ref)
+    assert (gpu["counts"] <= cap).all()
+    c.close()
+
+
+CAP_CASES = [
+    # dtype, H, F, E, k, T, capacity, flags  (router + dispatch kernel, expert path)
+    ("bf16", 512, 256, 8, 2, 40, 6, 0),                              # one-workgroup routing, stream
+    ("bf16", 256, 128, 64, 8, 60, 3, 0),                             # split-H small routing, stream
+    ("bf16", 512, 384, 4, 2, 700, 200, moe.MOE_FLAG_PATH_GROUPED),   # dispatch kernels, grouped
+    ("bf16", 512, 384, 4, 2, 700, 200, moe.MOE_FLAG_PATH_STREAM),    # dispatch kernels, stream
+    ("f32", 64, 128, 8, 2, 32, 4, 0),
+]
+
+
+@pytest.mark.parametrize("dtype,H,F,E,k,T,cap,flags", CAP_CASES)
+def test_forward_with_capacity(dtype, H, F, E, k, T, cap, flags):
+    _log("forward capacity", dtype, H, F, E, k, T, cap, flags)
+    shape = gen.LayerShape(f"c{H}_{F}_{E}_{k}", H=H, F=F, E=E, k=k, dtype=dtype)
+    c = Case(shape, T, flags=flags, capacity=cap)
+    x = gen.gen_x(shape, T)
+    y = c.forward(x)
+    r = c.route(x)
+    counts, offsets, perm, inv = oracle.dispatch(r["idx"].reshape(T, k), E, cap)
+    for key, ref in (("counts", counts), ("offsets", offsets), ("perm", perm), ("inv", inv)):
+        assert np.array_equal(r[key], ref), key  # the dispatch of the GPU's own routing
+    keep = (inv >= 0).reshape(T, k)
+    assert not keep.all()  # the capacity bites
+    st = check_rows(c, x, np.arange(T), y, r["idx"], keep_rows=keep)
+    _log("  ", st)
+    assert np.array_equal(y, c.forward(x))
+    c.close()
+
+
+def test_deepseek_skewed_with_capacity():
+    """The Zipf-skewed 128-expert workload with capacity 1.25 T k / E: the hot
+    experts are cut to the capacity, every other expert keeps all its rows."""
+    shape, T = gen.DEEPSEEK, 8192
+    cap = int(1.25 * T * shape.k / shape.E)
+    _log("deepseek capacity", cap)
+    c = Case(shape, T, capacity=cap)
+    x = gen.gen_x(shape, T)
+    y = c.forward(x)
+    r = c.route(x)
+    idx = r["idx"].reshape(T, shape.k)
+    counts, offsets, perm, inv = oracle.dispatch(idx, shape.E, cap)
+    for key, ref in (("counts", counts), ("offsets", offsets), ("perm", perm), ("inv", inv)):
+        assert np.array_equal(r[key], ref), key
+    raw = np.bincount(idx.ravel(), minlength=shape.E)
+    assert (raw > cap).sum() >= 5 and (counts == np.minimum(raw, cap)).all()
+    keep = (inv >= 0).reshape(T, shape.k)
+    rng = np.random.default_rng(9)
+    toks = np.unique(np.concatenate([[0, 1, T // 2, T - 1], rng.choice(T, 28, False)]))
+    st = check_rows(c, x, toks, y[toks], idx[toks], keep_rows=keep[toks])
+    _log("  ", st)
+    c.close()
