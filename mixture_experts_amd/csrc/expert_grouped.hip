@@ -26,11 +26,11 @@
 // the matrix cores keep issuing while LDS and the load path work in their
 // shadow; one workgroup barrier per K step publishes a landed stage.
 //
-// Tiles are built on the device from the expert offsets (no host sync): the
-// grid is sized for the worst case, and block b maps to (expert, token tile,
-// weight tile) through tile_off; blocks are renumbered so that each XCD gets
-// a contiguous range, and consecutive blocks on an XCD cover groups of 8
-// weight tiles x all token tiles of one expert, which then share L2.
+// The kernels are persistent (one workgroup per compute unit) and build their
+// tile lists on the device from the expert offsets (no host sync).  A
+// workgroup starts the first K steps of its next tile before it writes out
+// the current one, so tile boundaries cost little.  In a tile whose token
+// rows end early, waves skip the MFMAs of 32-row blocks past the end.
 #include "common.h"
 #include "kernels.h"
 
@@ -42,6 +42,11 @@ constexpr int kGroupW = 8;  // weight tiles per L2 group
 constexpr int kBK = 32;     // K step (elements): one 64-byte row slice
 constexpr int kCPR = 4;     // 16-byte chunks per LDS row
 constexpr int kNS = 4;      // LDS ring depth (4 x 32 KB)
+constexpr int kStage = 2 * 256 * kCPR;   // 16-byte chunks per ring stage (32 KB)
+// down projection: its output is staged in the 64 KB from kStageOut, clear of
+// ring stages 0-2 where the next tile's first K steps land meanwhile
+constexpr int kStageOut = 3 * kStage;
+constexpr int kLdsDown = kStageOut + 64 * 1024 / 16;  // 160 KB
 
 // Chunk c of row r sits at physical chunk c ^ ((r / 4) % 4): the 16 lanes of
 // one MFMA operand read take 16 consecutive rows at one logical chunk, and
@@ -52,6 +57,12 @@ __device__ __forceinline__ int lds_slot(int row, int c) {
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0f70)
+#define GG_BARRIER() asm volatile("s_barrier" ::: "memory")
+
+// One tile: expert e, K slice ks, weight tile mt, token rows p0 .. p0+rows-1.
+struct Tile {
+  int e, ks, mt, p0, rows;
+};
 
 template <bool GATED, int NS>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
@@ -59,68 +70,91 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
     const uint16_t* __restrict__ tok, const int32_t* __restrict__ perm, int k_top,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off, int E, int H,
     int F, int T, int ksplit, size_t plane, void* __restrict__ out) {
-  // [stage][0: weight rows, 1: token rows][256 rows x 4 chunks]; after the
-  // K loop the ring is reused to stage the output tile
-  __shared__ u32x4 lds[NS][2][256 * kCPR];
-  static_assert(sizeof(lds) >= 256 * 272 && sizeof(lds) >= 128 * 1024,
-                "output staging must fit in the operand ring");
+  // ring stage s at lds + s * kStage: [weight rows | token rows] x 256 x 4 chunks
+  __shared__ u32x4 lds[GATED ? NS * kStage : kLdsDown];
+  static_assert(GATED || (NS - 1) * kStage <= kStageOut, "LDS layout");
 
   // ksplit > 1 (down projection only): the K range is cut into ksplit
   // slices, slice ks writes its partial sums to plane ks of the output.
   const int K = (GATED ? H : F) / ksplit;
-  const int MW = GATED ? F / 128 : H / 256;
-  const int tiles = tile_off[E] * MW;
-  const int total = tiles * ksplit;
-  const uint32_t n8 = ((uint32_t)total + 7u) & ~7u;
-  if (blockIdx.x >= n8) return;
-  const int L0 = (int)xcd_logical_id(blockIdx.x, n8);
-  if (L0 >= total) return;
-  const int ks = L0 / tiles;
-  const int L = L0 - ks * tiles;
-  const int kbase = ks * K;
+  const int nk = K / kBK;
+  const int MW = GATED ? F / 128 : H / 256;  // weight tiles per expert
+  const int ngpe = (MW + kGroupW - 1) / kGroupW;
 
-  const int e = upper_segment(tile_off, E, L / MW);
-  const int nt_e = tile_off[e + 1] - tile_off[e];
-  const int local = L - tile_off[e] * MW;
-  const int fg = local / (nt_e * kGroupW);
-  const int rem = local - fg * nt_e * kGroupW;
-  const int gsz = min(kGroupW, MW - fg * kGroupW);
-  const int tt = rem / gsz;
-  const int mt = fg * kGroupW + rem % gsz;
+  // Persistent schedule.  Tiles are numbered (K slice, weight group, expert,
+  // token tile, weight tile), a weight group being a run of up to 8 weight
+  // tiles; the tiles of one (K slice, weight group, expert) share weight rows
+  // and token rows.  Each XCD (workgroup b runs on XCD b % 8) takes one
+  // contiguous eighth of the numbering and its workgroups take those tiles in
+  // turn, so tiles running together on an XCD share data in its L2, and each
+  // XCD sees every expert, whatever the routing skew.
+  const int xcd = blockIdx.x & 7;
+  const int nw = gridDim.x >> 3;  // workgroups per XCD
+  const int ntt = tile_off[E];    // token tiles over all experts
+  const int per_ks = ntt * MW;
+  const int ntiles = ksplit * per_ks;
+  const int q_end = (int)(((int64_t)(xcd + 1) * ntiles) >> 3);
+  auto locate = [&](int q, Tile& t) -> bool {
+    if (q >= q_end) return false;
+    const int ks = q / per_ks;
+    const int r = q - ks * per_ks;
+    const int fg = min(r / (ntt * kGroupW), ngpe - 1);
+    const int r2 = r - fg * ntt * kGroupW;
+    const int gsz = min(kGroupW, MW - fg * kGroupW);
+    const int u = r2 / gsz;  // token tile over all experts
+    const int e = upper_segment(tile_off, E, u);
+    t.e = e;
+    t.ks = ks;
+    t.mt = fg * kGroupW + (r2 - u * gsz);
+    t.p0 = offsets[e] + (u - tile_off[e]) * GG_BT;
+    t.rows = min(offsets[e + 1] - t.p0, GG_BT);
+    return true;
+  };
 
-  const int p_beg = offsets[e];
-  const int rows_left = offsets[e + 1] - p_beg - tt * GG_BT;  // >= 1
-  const int p0 = p_beg + tt * GG_BT;
-
-  const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave & 1, wn = wave >> 1;
 
   // Loads: per K step each wave moves weight rows and token rows
   // [64 wave, 64 wave + 64), 4 + 4 instructions of 16 rows x 64 bytes; lane l
   // fills row l / 4, physical chunk l % 4, from the logical chunk stored there.
-  const uint16_t* eb = experts + (size_t)stride_elems * e;
+  const uint16_t* eb = experts;
   uint32_t aoff[4], boff[4];
+  // gate/up: the slot ids of this lane's 4 token rows (rows past the tile's
+  // end repeat its last row)
+  auto load_perm = [&](const Tile& t, int (&pv)[4]) {
+    if (!GATED) return;
+    int ln;  // the lane id, opaque so that the addressing below is not kept live across tiles
+    asm volatile("v_and_b32 %0, 63, %1" : "=v"(ln) : "v"((int)threadIdx.x));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = wave * 64 + i * 16 + (lane >> 2);
-    const int lc = (lane & 3) ^ ((r >> 2) & 3);
-    if (GATED) {
-      const int f0 = mt * 128;
-      aoff[i] = (r < 128) ? (uint32_t)(f0 + r) * H : (uint32_t)F * H + (uint32_t)(f0 + r - 128) * H;
-    } else {
-      aoff[i] = 2u * (uint32_t)F * H + (uint32_t)(mt * 256 + r) * F;
+    for (int i = 0; i < 4; ++i) pv[i] = perm[t.p0 + min(wave * 64 + i * 16 + (ln >> 2), t.rows - 1)];
+  };
+  auto set_tile = [&](const Tile& t, const int (&pv)[4]) {
+    eb = experts + (size_t)stride_elems * t.e;
+    const int kbase = t.ks * K;
+    int ln;  // the lane id, opaque as above
+    asm volatile("v_and_b32 %0, 63, %1" : "=v"(ln) : "v"((int)threadIdx.x));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wave * 64 + i * 16 + (ln >> 2);
+      const int lc = (ln & 3) ^ ((r >> 2) & 3);
+      uint32_t a;
+      if (GATED) {
+        const int f0 = t.mt * 128;
+        a = (r < 128) ? (uint32_t)(f0 + r) * H : (uint32_t)F * H + (uint32_t)(f0 + r - 128) * H;
+      } else {
+        a = 2u * (uint32_t)F * H + (uint32_t)(t.mt * 256 + r) * F;
+      }
+      const int p = t.p0 + min(r, t.rows - 1);
+      const uint32_t b = GATED ? (uint32_t)min(max(pv[i], 0) / k_top, T - 1) * H : (uint32_t)p * F;
+      aoff[i] = a + lc * 8 + kbase;
+      boff[i] = b + lc * 8 + kbase;
     }
-    const int p = p0 + min(r, rows_left - 1);
-    boff[i] = GATED ? (uint32_t)min(max(perm[p], 0) / k_top, T - 1) * H : (uint32_t)p * F;
-    aoff[i] += lc * 8 + kbase;
-    boff[i] += lc * 8 + kbase;
-  }
-  const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) u32x4*)&lds[0][0][0]);
+  };
+  const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) u32x4*)&lds[0]);
   // one 16-row load: operand op (0 weights, 1 tokens), row group i, K step s
   auto dma = [&](int s, int op, int i) {
     const uint16_t* src = (op == 0 ? eb + aoff[i] : tok + boff[i]) + s * kBK;
-    const uint32_t dst = lds_base + (uint32_t)(((s % NS) * 2 + op) * 256 * kCPR * 16) +
+    const uint32_t dst = lds_base + (uint32_t)(((s % NS) * kStage + op * 256 * kCPR) * 16) +
                          (uint32_t)((wave * 64 + i * 16) * kCPR * 16);
     // one wait state between the M0 write and the LDS-DMA load that reads it
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
@@ -128,175 +162,220 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
                  : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(src)
                  : "memory", "m0");
   };
-
-  int arow[4], brow[4];
+  // the first NS-1 K steps of a tile (ring stages 0 .. NS-2)
+  auto prologue = [&]() {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    arow[i] = (GATED ? ((i < 2) ? wm * 64 + 32 * i : 128 + wm * 64 + 32 * (i - 2))
-                     : wm * 128 + 32 * i) + (lane & 31);
-    brow[i] = wn * 128 + 32 * i + (lane & 31);
-  }
-  const int kg = lane >> 5;
-
-  f32x16 acc[4][4];
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < nk) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) dma(s, 0, i);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  // fragments of one half step (16 k): lane group kg reads chunk 2 kg + h, a
-  // fixed permutation of the summation index applied to both operands
-  bf16x8 fa[2][4], fb[2][4];
-  // the 8 reads of half step (s, h) in the order of first use by the MFMAs
-  // (row block i of the weights, then token blocks 0..3, then weights 1..3)
-  auto rd = [&](int buf, int s, int h, int n) {
-    const int c = kg * 2 + h;
-    const int st = s % NS;
-    if (n == 0) fa[buf][0] = as_bf16x8(lds[st][0][lds_slot(arow[0], c)]);
-    else if (n < 5) fb[buf][n - 1] = as_bf16x8(lds[st][1][lds_slot(brow[n - 1], c)]);
-    else fa[buf][n - 4] = as_bf16x8(lds[st][0][lds_slot(arow[n - 4], c)]);
+        for (int i = 0; i < 4; ++i) dma(s, 1, i);
+      }
   };
-  // 16 MFMAs on fragment buffer buf, with the 8 reads of (rs, rh) into the
-  // other buffer and up to four 16-row loads of K step ls (half lh) woven in.
-  // RD / LD are std::bool_constant (fixed) or bool (decided at run time).
-  auto half_step = [&](int buf, auto RD, int rs, int rh, auto LD, int ls, int lh) {
+
+  // The K loop of one tile for a wave that computes its first NJ token
+  // blocks (the others lie beyond the tile's rows).  Loads never depend on
+  // NJ, so every wave keeps the same load and barrier sequence.
+  auto kloop = [&](auto NJc, f32x16 (&acc)[4][4]) {
+    constexpr int NJ = decltype(NJc)::value;
+    int ln;  // the lane id, opaque as above
+    asm volatile("v_and_b32 %0, 63, %1" : "=v"(ln) : "v"((int)threadIdx.x));
+    // MFMA operands: row block i of the weights (for gate/up blocks 0-1 are
+    // gate rows, 2-3 the matching up rows) and token block j; wave (wm, wn)
+    // owns token blocks 2j + wn, j = 0..3, so that a ragged tile's rows
+    // split evenly over the two wave columns
+    int arow[4], brow[4];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const int i = m >> 2, j = m & 3;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
-      if ((m & 1) == 0 && RD) rd(buf ^ 1, rs, rh, m >> 1);
-      if ((m & 3) == 1 && LD) dma(ls, lh, m >> 2);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < 4; ++i) {
+      arow[i] = (GATED ? ((i < 2) ? wm * 64 + 32 * i : 128 + wm * 64 + 32 * (i - 2))
+                       : wm * 128 + 32 * i) + (ln & 31);
+      brow[i] = (2 * i + wn) * 32 + (ln & 31);
     }
+    const int kg = ln >> 5;
+    // fragments of one half step (16 k): lane group kg reads chunk 2 kg + h,
+    // a fixed permutation of the summation index applied to both operands
+    bf16x8 fa[2][4], fb[2][4];
+    // the 8 reads of half step (s, h) in the order of first use by the MFMAs
+    // (row block i of the weights, then token blocks 0..3, then weights 1..3)
+    auto rd = [&](int buf, int s, int h, int n) {
+      const int c = kg * 2 + h;
+      const u32x4* st = lds + (s % NS) * kStage;
+      if (n == 0) fa[buf][0] = as_bf16x8(st[lds_slot(arow[0], c)]);
+      else if (n < 5) {
+        if (n - 1 < NJ) fb[buf][n - 1] = as_bf16x8(st[256 * kCPR + lds_slot(brow[n - 1], c)]);
+      } else fa[buf][n - 4] = as_bf16x8(st[lds_slot(arow[n - 4], c)]);
+    };
+    // the MFMAs of fragment buffer buf, with the 8 reads of (rs, rh) into the
+    // other buffer and up to four 16-row loads of K step ls (half lh) woven in.
+    // RD / LD are std::bool_constant (fixed) or bool (decided at run time).
+    auto half_step = [&](int buf, auto RD, int rs, int rh, auto LD, int ls, int lh) {
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const int i = m >> 2, j = m & 3;
+        if (j < NJ)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+        if ((m & 1) == 0 && RD) rd(buf ^ 1, rs, rh, m >> 1);
+        if ((m & 3) == 1 && LD) dma(ls, lh, m >> 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+#pragma unroll
+    for (int n = 0; n < 8; ++n) rd(0, 0, 0, n);
+    // K step k:  half 0 computes (k, 0) while reading (k, 1) and loading the
+    // token rows of step k+NS-2 into the stage of step k-2;  then every wave
+    // waits for its loads of step k+1 and a barrier publishes that stage and
+    // ends all reads of step k-1;  half 1 computes (k, 1) while reading
+    // (k+1, 0) and loading the weight rows of step k+NS-1 into the stage of
+    // step k-1.  Loads complete in issue order, so after half 0 of step k the
+    // loads still allowed in flight are those of steps k+2 .. k+NS-2.
+    // The steps 1 .. nk-NS run with every read and load present and take the
+    // branch-free body; the first and the last NS-1 steps decide at run time.
+    auto step = [&](int k) {
+      half_step(0, std::true_type(), k, 1, k >= 1 && k + NS - 2 < nk, k + NS - 2, 1);
+      if (k + NS - 2 < nk) WAIT_VMCNT((NS - 3) * 8); else WAIT_VMCNT(0);
+      GG_BARRIER();
+      half_step(1, k + 1 < nk, k + 1, 0, k + NS - 1 < nk, k + NS - 1, 0);
+    };
+    int k = 0;
+    if (nk > 0) step(k++);
+    for (; k + NS - 1 < nk; ++k) {
+      half_step(0, std::true_type(), k, 1, std::true_type(), k + NS - 2, 1);
+      WAIT_VMCNT((NS - 3) * 8);
+      GG_BARRIER();
+      half_step(1, std::true_type(), k + 1, 0, std::true_type(), k + NS - 1, 0);
+    }
+    for (; k < nk; ++k) step(k);
   };
-#define GG_BARRIER() asm volatile("s_barrier" ::: "memory")
 
-  const int nk = K / kBK;
-  // prologue: K steps 0 .. NS-2 in flight, wait for step 0
+  // Output.  Gate/up, straight from the accumulators: lane (tcol, rsub) of
+  // wave (wm, wn) holds 4 consecutive f for token tcol of each token block
+  // and writes SiLU(g) * u as 8 bf16 bytes; the four waves together write
+  // every 128-byte line of the tile's rows.  Down: the fp32 partial sums go
+  // through LDS in four rounds, round j holding token blocks 2j and 2j+1 as
+  // [64 tokens][256 h] 1 KB rows whose 16-byte chunks are XOR-swizzled by
+  // the row (chunk c of row r at c ^ (r % 16)), written out as 1 KB runs.
+  auto epilogue = [&](const Tile& t, f32x16 (&acc)[4][4]) {
+    int tid;  // the thread id, opaque so that the addressing below is not kept live across tiles
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
+    const int tcol = tid & 31;
+    const int rsub = 4 * ((tid >> 5) & 1);
+    if (GATED) {
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) {
+      for (int j = 0; j < 4; ++j) {
+        const int tl = (2 * j + wn) * 32 + tcol;
+        if (tl >= t.rows) continue;
+        uint16_t* row = (uint16_t*)out + (size_t)(t.p0 + tl) * F + t.mt * 128 + wm * 64 + rsub;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma(s, 0, i);
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma(s, 1, i);
-    }
-  if (nk >= NS - 1) WAIT_VMCNT((NS - 2) * 8); else WAIT_VMCNT(0);
-  GG_BARRIER();
+          for (int q = 0; q < 4; ++q) {
+            float o[4];
 #pragma unroll
-  for (int n = 0; n < 8; ++n) rd(0, 0, 0, n);
-
-  // K step k:  half 0 computes (k, 0) while reading (k, 1) and loading the
-  // token rows of step k+NS-2 into the stage of step k-2;  then every wave
-  // waits for its loads of step k+1 and a barrier publishes that stage and
-  // ends all reads of step k-1;  half 1 computes (k, 1) while reading
-  // (k+1, 0) and loading the weight rows of step k+NS-1 into the stage of
-  // step k-1.  Loads complete in issue order, so after half 0 of step k the
-  // loads still allowed in flight are those of steps k+2 .. k+NS-2.
-  // The steps 1 .. nk-NS run with every read and load present and take the
-  // branch-free body; the first and the last NS-1 steps decide at run time.
-  auto step = [&](int k) {
-    half_step(0, std::true_type(), k, 1, k >= 1 && k + NS - 2 < nk, k + NS - 2, 1);
-    if (k + NS - 2 < nk) WAIT_VMCNT((NS - 3) * 8); else WAIT_VMCNT(0);
-    GG_BARRIER();
-    half_step(1, k + 1 < nk, k + 1, 0, k + NS - 1 < nk, k + NS - 1, 0);
-  };
-  int k = 0;
-  if (nk > 0) step(k++);
-  for (; k + NS - 1 < nk; ++k) {
-    half_step(0, std::true_type(), k, 1, std::true_type(), k + NS - 2, 1);
-    WAIT_VMCNT((NS - 3) * 8);
-    GG_BARRIER();
-    half_step(1, std::true_type(), k + 1, 0, std::true_type(), k + NS - 1, 0);
-  }
-  for (; k < nk; ++k) step(k);
-#undef GG_BARRIER
-
-  const int tcol = lane & 31;
-  const int rsub = 4 * (lane >> 5);
-  if (GATED) {
-    // SiLU(g) * u to bf16, staged through LDS as [token][f] rows (272-byte
-    // pitch: 16 bytes of padding spread the 8-byte writes of one MFMA column
-    // over the banks), then written out as 256-byte row runs.
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    constexpr int OP = 272;
-    uint8_t* ob = (uint8_t*)&lds[0][0][0];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tl = wn * 128 + 32 * j + tcol;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int fl = wm * 64 + 32 * i + 8 * q + rsub;
-          float o[4];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const float g = acc[i][j][4 * q + jj];
-            o[jj] = silu_f32(g) * acc[i + 2][j][4 * q + jj];
-          }
-          const bf16x2 lo = {(__bf16)o[0], (__bf16)o[1]}, hi = {(__bf16)o[2], (__bf16)o[3]};
-          uint2 pk;
-          pk.x = __builtin_bit_cast(uint32_t, lo);
-          pk.y = __builtin_bit_cast(uint32_t, hi);
-          *reinterpret_cast<uint2*>(ob + tl * OP + fl * 2) = pk;
-        }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    uint16_t* act = (uint16_t*)out;
-    const int c = threadIdx.x & 15;
-#pragma unroll 4
-    for (int r0 = 0; r0 < 256; r0 += 16) {
-      const int row = r0 + (threadIdx.x >> 4);
-      if (row < rows_left)
-        *reinterpret_cast<u32x4*>(act + (size_t)(p0 + row) * F + mt * 128 + c * 8) =
-            *reinterpret_cast<const u32x4*>(ob + row * OP + c * 16);
-    }
-  } else {
-    // fp32 partial rows, staged through LDS in two rounds (token rows
-    // 0-127, then 128-255) as [token][256 h] 1 KB rows whose 16-byte chunks
-    // are XOR-swizzled by the row (chunk c of row t at c ^ (t % 16)), then
-    // written out as 1 KB row runs.
-    float* yp = (float*)out + (size_t)ks * plane;
-    uint8_t* ob = (uint8_t*)&lds[0][0][0];  // 128 KB: exactly the ring
-    const int c = threadIdx.x & 63;
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      if (wn == r) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int tl = 32 * j + tcol;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int hc = (wm * 128 + 32 * i + 8 * q + rsub) >> 2;
-              f32x4 o{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                      acc[i][j][4 * q + 3]};
-              *reinterpret_cast<f32x4*>(ob + tl * 1024 + ((hc ^ (tl & 15)) << 4)) = o;
+            for (int jj = 0; jj < 4; ++jj) {
+              // read each accumulator where it is used: left to itself the
+              // compiler copies all of them to VGPRs at once and spills
+              float g, u;
+              asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(g) : "a"(acc[i][j][4 * q + jj]));
+              asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(u) : "a"(acc[i + 2][j][4 * q + jj]));
+              o[jj] = silu_f32(g) * u;
             }
+            const bf16x2 lo = {(__bf16)o[0], (__bf16)o[1]}, hi = {(__bf16)o[2], (__bf16)o[3]};
+            uint2 pk;
+            pk.x = __builtin_bit_cast(uint32_t, lo);
+            pk.y = __builtin_bit_cast(uint32_t, hi);
+            *reinterpret_cast<uint2*>(row + 32 * i + 8 * q) = pk;
+          }
+      }
+    } else {
+      uint8_t* ob = (uint8_t*)&lds[kStageOut];
+      float* yp = (float*)out + (size_t)t.ks * plane;
+      const int c = tid & 63;
+      const int sr = wn * 32 + tcol;  // staging row of this lane's token
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j > 0) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int hc = (wm * 128 + 32 * i + 8 * q + rsub) >> 2;
+            *reinterpret_cast<f32x4*>(ob + sr * 1024 + ((hc ^ (sr & 15)) << 4)) =
+                f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll 4
+        for (int r0 = 0; r0 < 64; r0 += 4) {
+          const int row = r0 + (tid >> 6);
+          const int tl = (2 * j + (row >> 5)) * 32 + (row & 31);
+          if (tl < t.rows)
+            *reinterpret_cast<u32x4*>(yp + (size_t)(t.p0 + tl) * H + t.mt * 256 + ((c ^ (row & 15)) << 2)) =
+                *reinterpret_cast<const u32x4*>(ob + row * 1024 + (c << 4));
         }
       }
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-#pragma unroll 4
-      for (int r0 = 0; r0 < 128; r0 += 4) {
-        const int row = r0 + (threadIdx.x >> 6);
-        const int tl = r * 128 + row;
-        if (tl < rows_left)
-          *reinterpret_cast<u32x4*>(yp + (size_t)(p0 + tl) * H + mt * 256 + ((c ^ (row & 15)) << 2)) =
-              *reinterpret_cast<const u32x4*>(ob + row * 1024 + (c << 4));
-      }
     }
+  };
+
+  int q = (int)(((int64_t)xcd * ntiles) >> 3) + (int)(blockIdx.x >> 3);
+  Tile cur, nxt;
+  if (!locate(q, cur)) return;
+  {
+    int pv[4];
+    load_perm(cur, pv);
+    set_tile(cur, pv);
+  }
+  prologue();
+  // one tile for waves that compute NJ token blocks; returns whether a next
+  // tile exists (then its first stages are in flight)
+  auto tile = [&](auto NJc) -> bool {
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    // the next tile, located and its token rows looked up while this one
+    // computes (those loads precede the K loop's and only strengthen its waits)
+    const bool more = locate(q + nw, nxt);
+    int pn[4] = {0, 0, 0, 0};
+    if (more) load_perm(nxt, pn);
+    kloop(NJc, acc);
+    // every load of the tile has landed; end every wave's reads of the ring,
+    // then start the next tile's first stages under this tile's epilogue
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (more) {
+      set_tile(nxt, pn);
+      prologue();
+    }
+    epilogue(cur, acc);
+    return more;
+  };
+  for (;;) {
+    // this tile's first NS-1 stages have landed (and the previous tile's
+    // output stores have completed, as vmcnt counts both); the barrier also
+    // ends every wave's reads of the previous tile's output staging
+    WAIT_VMCNT(0);
+    GG_BARRIER();
+    const int nb = (cur.rows + 31) >> 5;        // 32-row token blocks in the tile
+    const int nj = max((nb - wn + 1) >> 1, 1);  // this wave's (at least one)
+    bool more;
+    switch (nj) {
+      case 1: more = tile(std::integral_constant<int, 1>()); break;
+      case 2: more = tile(std::integral_constant<int, 2>()); break;
+      case 3: more = tile(std::integral_constant<int, 3>()); break;
+      default: more = tile(std::integral_constant<int, 4>()); break;
+    }
+    if (!more) break;
+    cur = nxt;
+    q += nw;
   }
 }
 
-int grid_for(const ExpertArgs& a, int mw, int ksplit) {
-  const int max_tiles = (a.S + GG_BT - 1) / GG_BT + (a.E < a.S ? a.E : a.S);
-  const int g = max_tiles * mw * ksplit;
-  return (g + 7) & ~7;
+// One workgroup per compute unit, a multiple of 8 (one share per XCD).
+int persistent_grid() {
+  const int w = cu_count() / 8;
+  return 8 * (w < 1 ? 1 : w);
 }
 
 }  // namespace
@@ -309,16 +388,14 @@ int grouped_down_ksplit(const ExpertArgs& a) {
 }
 
 int launch_grouped_gate_up(const ExpertArgs& a, hipStream_t st) {
-  const int grid = grid_for(a, a.F / 128, 1);
-  grouped_gemm_kernel<true, kNS><<<grid, 256, 0, st>>>(
+  grouped_gemm_kernel<true, kNS><<<persistent_grid(), 256, 0, st>>>(
       (const uint16_t*)a.experts, a.stride_elems, (const uint16_t*)a.x, a.perm, a.k, a.offsets,
       a.tile_off, a.E, a.H, a.F, a.T, 1, 0, a.act);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_grouped_down(const ExpertArgs& a, int ksplit, hipStream_t st) {
-  const int grid = grid_for(a, a.H / 256, ksplit);
-  grouped_gemm_kernel<false, kNS><<<grid, 256, 0, st>>>(
+  grouped_gemm_kernel<false, kNS><<<persistent_grid(), 256, 0, st>>>(
       (const uint16_t*)a.experts, a.stride_elems, (const uint16_t*)a.act, a.perm, a.k,
       a.offsets, a.tile_off, a.E, a.H, a.F, a.T, ksplit, (size_t)a.S * a.H, a.yp);
   return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -274,20 +274,6 @@ __global__ __launch_bounds__(256) void stream_kernel(
   WAIT_VMCNT(0);
 }
 
-int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 template <bool GATED, int TR, int NS, int CK>
 int launch_tr(const ExpertArgs& a, hipStream_t st) {
   constexpr int NA = GATED ? 2 : 1, NB = (TR + 15) / 16;
@@ -326,6 +312,20 @@ int launch_stream(const ExpertArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
 
 int launch_stream_gate_up(const ExpertArgs& a, hipStream_t st) { return launch_stream<true>(a, st); }
 int launch_stream_down(const ExpertArgs& a, hipStream_t st) { return launch_stream<false>(a, st); }

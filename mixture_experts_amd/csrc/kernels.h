@@ -67,6 +67,9 @@ int launch_route_small(const RouterArgs& a, const DispatchArgs& d, int32_t* coun
                        hipStream_t st);
 int launch_dispatch(const DispatchArgs& a, hipStream_t st);
 
+// compute units of the current device (cached per device)
+int cu_count();
+
 // bf16 expert FFN, grouped MFMA GEMMs (many rows per expert)
 int launch_grouped_gate_up(const ExpertArgs& a, hipStream_t st);
 // split-K factor the grouped down projection uses for this call (1 or 2);
