@@ -16,6 +16,14 @@ _LIB = None
 
 F32, BF16 = 0, 1
 GATE_SOFTMAX, GATE_RAW = 0, 1
+EXPERT_DTYPE, EXPERT_U8 = 0, 1
+U8_PARAMS_BYTES = 64
+
+
+class U8Params(ctypes.Structure):
+    _fields_ = [("scale", ctypes.c_float * 3), ("zero", ctypes.c_int32 * 3),
+                ("min", ctypes.c_float * 3), ("max", ctypes.c_float * 3),
+                ("pad", ctypes.c_uint32 * 4)]
 
 
 class _Layer(ctypes.Structure):
@@ -23,7 +31,8 @@ class _Layer(ctypes.Structure):
                 ("k", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
                 ("experts", ctypes.c_void_p), ("stride", ctypes.c_uint64),
-                ("gate", ctypes.c_int32), ("capacity", ctypes.c_int32)]
+                ("gate", ctypes.c_int32), ("capacity", ctypes.c_int32),
+                ("expert_format", ctypes.c_int32)]
 
 
 def lib():
@@ -45,6 +54,9 @@ def lib():
         L.orc_layer_forward.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, vp, vp]
         L.orc_layer_tokens.argtypes = [vp, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp]
         L.orc_prenorm_bf16.argtypes = [i32, i32, vp, vp]
+        L.orc_quantize_u8.argtypes = [vp, ctypes.c_size_t, vp, vp, i32]
+        L.orc_quantize_experts_u8.argtypes = [vp, ctypes.c_uint64, i32, i32, i32, vp,
+                                              ctypes.c_uint64]
         L.orc_bf16_round.argtypes = [ctypes.c_double]
         L.orc_bf16_round.restype = ctypes.c_double
         L.orc_num_threads.argtypes = []
@@ -65,7 +77,7 @@ class Layer:
     """One MoE layer's weights as the oracle reads them (numpy arrays kept alive)."""
 
     def __init__(self, H, F, E, k, dtype, router_w, router_b, experts, stride, gate="softmax",
-                 capacity=0):
+                 capacity=0, expert_format="dtype"):
         self.H, self.F, self.E, self.k = H, F, E, k
         self.gate = gate
         self.capacity = capacity
@@ -77,7 +89,8 @@ class Layer:
         self.stride = stride
         self._s = _Layer(H, F, E, k, F32 if dtype == "f32" else BF16, _p(self.router_w),
                          _p(self.router_b), _p(self.experts), stride,
-                         {"softmax": GATE_SOFTMAX, "raw": GATE_RAW}[gate], capacity)
+                         {"softmax": GATE_SOFTMAX, "raw": GATE_RAW}[gate], capacity,
+                         {"dtype": EXPERT_DTYPE, "u8": EXPERT_U8}[expert_format])
 
     @property
     def ref(self):
@@ -192,6 +205,42 @@ def num_threads() -> int:
     return lib().orc_num_threads()
 
 
-def layer_from_gen(shape, router_w, router_b, experts, gate="softmax", capacity=0) -> Layer:
+def layer_from_gen(shape, router_w, router_b, experts, gate="softmax", capacity=0,
+                   u8_experts=None, u8_stride=0) -> Layer:
+    """The layer of a generated workload; with u8_experts (uint8 experts and
+    their parameter blocks, stride u8_stride) the expert weights are those."""
+    if u8_experts is not None:
+        return Layer(shape.H, shape.F, shape.E, shape.k, shape.dtype, router_w, router_b,
+                     u8_experts, u8_stride, gate=gate, capacity=capacity, expert_format="u8")
     return Layer(shape.H, shape.F, shape.E, shape.k, shape.dtype, router_w, router_b, experts,
                  shape.stride, gate=gate, capacity=capacity)
+
+
+def quantize_u8(w_bf16):
+    """One matrix of bf16 bit patterns -> (uint8 codes, scale, zero, min, max)."""
+    w = np.ascontiguousarray(w_bf16, np.uint16)
+    q = np.empty(w.shape, np.uint8)
+    p = U8Params()
+    _check(lib().orc_quantize_u8(_p(w), w.size, _p(q), ctypes.byref(p), 0), "quantize_u8")
+    return q, p.scale[0], p.zero[0], p.min[0], p.max[0]
+
+
+def u8_stride(H, F):
+    """Bytes per uint8 expert: three matrices and the parameter block, to 256."""
+    return (3 * H * F + U8_PARAMS_BYTES + 255) // 256 * 256
+
+
+def quantize_experts_u8(experts, src_stride, E, H, F, dst_stride=None):
+    """bf16 experts (bytes or uint16 array, E * src_stride bytes) -> uint8
+    experts with parameter blocks (uint8 array of E * dst_stride bytes)."""
+    src = np.ascontiguousarray(experts).view(np.uint8)
+    dst_stride = u8_stride(H, F) if dst_stride is None else dst_stride
+    dst = np.zeros(E * dst_stride, np.uint8)
+    _check(lib().orc_quantize_experts_u8(_p(src), src_stride, E, H, F, _p(dst), dst_stride),
+           "quantize_experts_u8")
+    return dst
+
+
+def u8_params(u8_experts, stride, e, H, F) -> U8Params:
+    off = e * stride + 3 * H * F
+    return U8Params.from_buffer_copy(np.ascontiguousarray(u8_experts[off:off + U8_PARAMS_BYTES]))

@@ -45,8 +45,45 @@ static int check_layer(const orc_layer_t* L) {
   if (!L->router_w || !L->experts) return -1;
   if (L->gate != ORC_GATE_SOFTMAX && L->gate != ORC_GATE_RAW) return -1;
   if (L->capacity < 0) return -1;
-  if (L->stride < 3ull * (uint64_t)L->H * (uint64_t)L->F * elem_size(L->dtype)) return -1;
+  const uint64_t hf = (uint64_t)L->H * (uint64_t)L->F;
+  if (L->expert_format == ORC_EXPERT_U8) {
+    if (L->dtype != ORC_BF16 || L->stride < 3ull * hf + sizeof(orc_u8_params_t)) return -1;
+  } else if (L->expert_format != ORC_EXPERT_DTYPE || L->stride < 3ull * hf * elem_size(L->dtype)) {
+    return -1;
+  }
   return 0;
+}
+
+/* Weight matrix m (0 Wg, 1 Wu, 2 Wd) of an expert block: element i as a
+ * double, exactly (a stored value, or (q - zero) * scale of a uint8 code). */
+typedef struct {
+  const unsigned char* base;
+  int32_t dtype, u8;
+  double scale, zero;
+} orc_mat_t;
+
+static orc_mat_t expert_matrix(const orc_layer_t* L, const unsigned char* blk, int m) {
+  orc_mat_t M;
+  const size_t hf = (size_t)L->H * L->F;
+  M.dtype = L->dtype;
+  M.u8 = L->expert_format == ORC_EXPERT_U8;
+  M.scale = 1.0;
+  M.zero = 0.0;
+  if (M.u8) {
+    orc_u8_params_t p;
+    memcpy(&p, blk + 3 * hf, sizeof p);
+    M.base = blk + (size_t)m * hf;
+    M.scale = (double)p.scale[m];
+    M.zero = (double)p.zero[m];
+  } else {
+    M.base = blk + (size_t)m * hf * elem_size(L->dtype);
+  }
+  return M;
+}
+
+static double mat_at(const orc_mat_t* M, size_t i) {
+  if (M->u8) return ((double)M->base[i] - M->zero) * M->scale;
+  return widen(M->base, M->dtype, i);
 }
 
 /* Round a double to the nearest bfloat16 value (8 significant bits), ties to
@@ -180,23 +217,21 @@ int orc_dispatch(int32_t T, int32_t E, int32_t k, const int32_t* idx, int32_t* c
 int orc_expert_ffn(const orc_layer_t* L, int32_t e, const double* xrow, double* yrow) {
   if (check_layer(L) || e < 0 || e >= L->E || !xrow || !yrow) return -1;
   const int32_t H = L->H, F = L->F;
-  const size_t es = elem_size(L->dtype);
   const unsigned char* blk = (const unsigned char*)L->experts + (size_t)e * L->stride;
-  const void* Wg = blk;
-  const void* Wu = blk + (size_t)F * H * es;
-  const void* Wd = blk + 2 * (size_t)F * H * es;
+  const orc_mat_t Wg = expert_matrix(L, blk, 0), Wu = expert_matrix(L, blk, 1),
+                  Wd = expert_matrix(L, blk, 2);
   double* a = (double*)malloc(sizeof(double) * (size_t)F);
   if (!a) return -1;
   for (int32_t f = 0; f < F; ++f) {
     double g = 0.0, u = 0.0;
-    for (int32_t h = 0; h < H; ++h) g += xrow[h] * widen(Wg, L->dtype, (size_t)f * H + h);
-    for (int32_t h = 0; h < H; ++h) u += xrow[h] * widen(Wu, L->dtype, (size_t)f * H + h);
+    for (int32_t h = 0; h < H; ++h) g += xrow[h] * mat_at(&Wg, (size_t)f * H + h);
+    for (int32_t h = 0; h < H; ++h) u += xrow[h] * mat_at(&Wu, (size_t)f * H + h);
     double act = g / (1.0 + exp(-g)) * u;
     a[f] = (L->dtype == ORC_BF16) ? orc_bf16_round(act) : act;
   }
   for (int32_t h = 0; h < H; ++h) {
     double s = 0.0;
-    for (int32_t f = 0; f < F; ++f) s += a[f] * widen(Wd, L->dtype, (size_t)h * F + f);
+    for (int32_t f = 0; f < F; ++f) s += a[f] * mat_at(&Wd, (size_t)h * F + f);
     yrow[h] = s;
   }
   free(a);
@@ -336,6 +371,59 @@ int orc_prenorm_bf16(int32_t T, int32_t H, const float* h, uint16_t* xt) {
       memcpy(&bits, &f, sizeof bits);
       xt[(size_t)t * H + i] = (uint16_t)(bits >> 16);
     }
+  }
+  return 0;
+}
+
+/* Affine uint8 quantisation of one weight matrix from its range, as the
+ * pages convert expert weights after training: per-matrix minimum and
+ * maximum, 255 levels (www.pnsm.cn/news/1892388.html sec. 3.1), read back as
+ * (q - zero) * scale with an integer zero point (same page, sec. 5.2).
+ * Readings: the range is widened to include 0 so that the zero point is a
+ * code in [0, 255] and 0 is exact; codes are unsigned bytes; every step is
+ * fp32 arithmetic (IEEE, round to nearest even), written out in order. */
+int orc_quantize_u8(const uint16_t* w, size_t n, uint8_t* q, orc_u8_params_t* p, int32_t m) {
+  if (!w || !q || !p || m < 0 || m > 2) return -1;
+  float mn = 0.0f, mx = 0.0f;
+  for (size_t i = 0; i < n; ++i) {
+    const float v = (float)widen(w, ORC_BF16, i);
+    if (!isfinite(v)) return -1;
+    if (v < mn) mn = v;
+    if (v > mx) mx = v;
+  }
+  float scale = (mx - mn) / 255.0f;
+  if (!(scale > 0.0f)) scale = 1.0f;
+  int32_t zero = (int32_t)rintf(-mn / scale);
+  if (zero < 0) zero = 0;
+  if (zero > 255) zero = 255;
+  for (size_t i = 0; i < n; ++i) {
+    const float v = (float)widen(w, ORC_BF16, i);
+    int32_t c = (int32_t)rintf(v / scale) + zero;
+    if (c < 0) c = 0;
+    if (c > 255) c = 255;
+    q[i] = (uint8_t)c;
+  }
+  p->scale[m] = scale;
+  p->zero[m] = zero;
+  p->min[m] = mn;
+  p->max[m] = mx;
+  return 0;
+}
+
+int orc_quantize_experts_u8(const void* src, uint64_t src_stride, int32_t E, int32_t H,
+                            int32_t F, void* dst, uint64_t dst_stride) {
+  if (!src || !dst || E < 1 || H < 1 || F < 1) return -1;
+  const size_t hf = (size_t)H * F;
+  if (src_stride < 3 * hf * 2 || dst_stride < 3 * hf + sizeof(orc_u8_params_t)) return -1;
+  for (int32_t e = 0; e < E; ++e) {
+    const unsigned char* sb = (const unsigned char*)src + (size_t)e * src_stride;
+    unsigned char* db = (unsigned char*)dst + (size_t)e * dst_stride;
+    orc_u8_params_t p;
+    memset(&p, 0, sizeof p);
+    for (int32_t m = 0; m < 3; ++m)
+      if (orc_quantize_u8((const uint16_t*)(sb + (size_t)m * hf * 2), hf, db + (size_t)m * hf, &p, m))
+        return -1;
+    memcpy(db + 3 * hf, &p, sizeof p);
   }
   return 0;
 }

@@ -34,12 +34,20 @@
  *   stack    residual inside the forward call: www.pnsm.cn/news/1892388.html
  *            sec. 2.1; with a parameter-free RMS normalisation of the branch
  *            input (a reading: the literal residual stack overflows).
+ *   uint8    expert weights quantised after training, one affine map per
+ *   experts  weight matrix from its minimum and maximum, 255 levels, read as
+ *            w = (q - zero) * scale: www.pnsm.cn page sec. 3.1 (per-expert
+ *            min/max quantisation) and sec. 5.2 (dequantisation with an
+ *            integer zero point); the layer is then the same method on the
+ *            dequantised weights.
  *
  * Storage (all row-major):
  *   x        [T][H]   dtype          Wr  [H][E] dtype       b [E] fp32
  *   expert e at byte offset e*stride of `experts`:
  *            Wg [F][H], Wu [F][H], Wd [H][F]   dtype
  *   dtype ORC_F32: float; ORC_BF16: bfloat16 bit patterns (uint16).
+ *   expert_format ORC_EXPERT_U8 (bf16 layers): the three matrices as uint8
+ *            codes, then at byte 3*H*F an orc_u8_params_t block.
  * Every stored value is widened exactly to double; all sums are in double,
  * in ascending index order.  In bf16 layers the SwiGLU activation is rounded
  * to bf16 (round to nearest even) before the down projection, because the
@@ -59,6 +67,15 @@ extern "C" {
 
 enum { ORC_F32 = 0, ORC_BF16 = 1 };
 enum { ORC_GATE_SOFTMAX = 0, ORC_GATE_RAW = 1 };
+enum { ORC_EXPERT_DTYPE = 0, ORC_EXPERT_U8 = 1 };
+
+/* per-expert quantisation parameters, matrix m = 0 (Wg), 1 (Wu), 2 (Wd) */
+typedef struct {
+  float scale[3];
+  int32_t zero[3];
+  float min[3], max[3]; /* the range the map was made from (includes 0) */
+  uint32_t pad[4];
+} orc_u8_params_t;      /* 64 bytes */
 
 typedef struct {
   int32_t H, F, E, k;
@@ -69,6 +86,7 @@ typedef struct {
   uint64_t stride;
   int32_t gate;      /* ORC_GATE_SOFTMAX or ORC_GATE_RAW */
   int32_t capacity;  /* pairs an expert takes per call; 0 = no limit */
+  int32_t expert_format; /* ORC_EXPERT_DTYPE or ORC_EXPERT_U8 */
 } orc_layer_t;
 
 int orc_logits(const orc_layer_t* L, const void* x, int32_t T, double* logits);
@@ -94,6 +112,15 @@ int orc_layer_tokens(const orc_layer_t* L, const void* x, int32_t T, const int32
                      int32_t ntok, const int32_t* idx_override, const int32_t* keep, double* y,
                      int32_t* idx, double* w, double* logits);
 int orc_prenorm_bf16(int32_t T, int32_t H, const float* h, uint16_t* xt);
+/* uint8 quantisation of n bf16 weights (one matrix), in fp32 arithmetic:
+ * mn = min(0, min w), mx = max(0, max w), scale = (mx - mn) / 255 (1 if 0),
+ * zero = clamp(rint(-mn / scale), 0, 255),
+ * q = clamp(rint(w / scale) + zero, 0, 255); rint rounds half to even. */
+int orc_quantize_u8(const uint16_t* w, size_t n, uint8_t* q, orc_u8_params_t* p, int32_t m);
+/* every matrix of E bf16 experts (stride src_stride bytes) into uint8
+ * experts with their parameter blocks (stride dst_stride >= 3*H*F + 64) */
+int orc_quantize_experts_u8(const void* src, uint64_t src_stride, int32_t E, int32_t H,
+                            int32_t F, void* dst, uint64_t dst_stride);
 double orc_bf16_round(double v);
 int orc_num_threads(void);
 
