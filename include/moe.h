@@ -61,6 +61,30 @@ enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+/* Storage of the expert weights (moe_layer_desc.expert_format). */
+enum {
+  MOE_EXPERT_DTYPE = 0, /* in the layer's dtype */
+  /* uint8 codes with one affine map per weight matrix, weight = (q - zero) *
+   * scale: post-training quantisation of each expert matrix from its range,
+   * 255 levels, integer zero point [www.pnsm.cn/news/1892388.html sec. 3.1
+   * and sec. 5.2].  Expert e at expert_base + e*expert_stride holds
+   *   Wg [F][H], Wu [F][H], Wd [H][F]   uint8 (same orientation as above)
+   *   at byte 3*H*F: moe_u8_params (64 bytes)
+   * and expert_stride >= 3*H*F + 64 (a multiple of 256).  bf16 layers only;
+   * x, the router and the activation stay bf16, the expert FFN runs on the
+   * weight-streaming kernels for every batch size (MOE_FLAG_PATH_GROUPED is
+   * unsupported), which read one byte per weight. */
+  MOE_EXPERT_U8 = 1
+};
+
+/* Parameters of a uint8 expert, matrix m = 0 (Wg), 1 (Wu), 2 (Wd). */
+typedef struct {
+  float scale[3];
+  int32_t zero[3];      /* 0..255 */
+  float min[3], max[3]; /* the range the map was made from; it includes 0 */
+  uint32_t pad[4];
+} moe_u8_params;
+
 enum {
   /* Stacked-layer mode: x is the fp32 residual stream h [T][H]; the branch
    * input is bf16(h[t] / sqrt(mean_h h[t]^2 + 1e-6)) and y = h + MoE(.).
@@ -111,7 +135,7 @@ typedef struct {
                              hard_capacity, www.cf-1.com/news/4750020/ sec. 4.2
                              --expert-capacity; zskr.cn page sec. 2.2).  A soft
                              capacity is a larger value of this limit. */
-  int32_t reserved;       /* 0 */
+  int32_t expert_format;  /* MOE_EXPERT_DTYPE or MOE_EXPERT_U8 */
 } moe_layer_desc;
 
 /* Validates *d, allocates the workspace for d->max_tokens on the current
@@ -170,6 +194,22 @@ enum {
 };
 int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* stream,
                    void* const* stage_events);
+
+/* Quantises E bf16 experts (src: expert e at src + e*src_stride bytes, laid
+ * out as in moe_layer_desc) into uint8 experts for MOE_EXPERT_U8 (dst, e at
+ * dst + e*dst_stride).  Per matrix, in fp32 arithmetic with IEEE division
+ * and rint (ties to even):
+ *   mn = min(0, min w), mx = max(0, max w), scale = (mx - mn) / 255 (1 if 0),
+ *   zero = clamp(rint(-mn / scale), 0, 255),
+ *   q = clamp(rint(w / scale) + zero, 0, 255).
+ * Both buffers are device memory, 16-byte aligned; src_stride >= 6*H*F,
+ * dst_stride >= 3*H*F + 64, both multiples of 256; H % 16 == 0 and F % 16
+ * == 0; 3*H*F < 2^31.  Queued on `stream`; allocates nothing (the parameter
+ * blocks of dst serve as scratch).  Errors: MOE_ERR_INVALID_ARG, or
+ * MOE_ERR_DEVICE on a launch failure.  Non-finite weights give unspecified
+ * codes. */
+int moe_quantize_experts_u8(const void* src, uint64_t src_stride, int32_t E, int32_t H,
+                            int32_t F, void* dst, uint64_t dst_stride, void* stream);
 
 /* Releases the workspace (after synchronising the device).  NULL-safe. */
 void moe_layer_free(moe_layer_t* L);

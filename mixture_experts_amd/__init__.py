@@ -23,12 +23,16 @@ MOE_FLAG_RESIDUAL_PRENORM = 1 << 0
 MOE_FLAG_PATH_GROUPED = 1 << 1
 MOE_FLAG_PATH_STREAM = 1 << 2
 MOE_FLAG_GATE_RAW = 1 << 3
+MOE_EXPERT_DTYPE = 0
+MOE_EXPERT_U8 = 1
+U8_PARAMS_BYTES = 64
 
 MOE_STAGE_ROUTE, MOE_STAGE_DISPATCH, MOE_STAGE_GATE_UP, MOE_STAGE_DOWN, MOE_STAGE_COMBINE = range(5)
 MOE_NUM_STAGES = 5
 STAGE_NAMES = ("route", "dispatch", "gate_up", "down", "combine")
 
-EXPORTED = ("moe_layer_create", "moe_route", "moe_forward", "moe_forward_ev", "moe_layer_free")
+EXPORTED = ("moe_layer_create", "moe_route", "moe_forward", "moe_forward_ev", "moe_layer_free",
+            "moe_quantize_experts_u8")
 
 _ERRS = {MOE_ERR_INVALID_ARG: "invalid argument", MOE_ERR_NO_MEMORY: "out of device memory",
          MOE_ERR_DEVICE: "device error", MOE_ERR_UNSUPPORTED: "unsupported shape or mode"}
@@ -47,7 +51,7 @@ class moe_layer_desc(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
                 ("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
                 ("expert_base", ctypes.c_void_p), ("expert_stride", ctypes.c_uint64),
-                ("expert_capacity", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("expert_capacity", ctypes.c_int32), ("expert_format", ctypes.c_int32)]
 
 
 _LIB = None
@@ -71,6 +75,9 @@ def lib():
         L.moe_forward_ev.restype = ctypes.c_int
         L.moe_layer_free.argtypes = [vp]
         L.moe_layer_free.restype = None
+        L.moe_quantize_experts_u8.argtypes = [vp, ctypes.c_uint64, i32, i32, i32, vp,
+                                              ctypes.c_uint64, vp]
+        L.moe_quantize_experts_u8.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -94,10 +101,23 @@ def _stream(s):
 
 
 def make_desc(hidden, ffn, num_experts, top_k, max_tokens, dtype, router_w, expert_base,
-              expert_stride, router_b=None, flags=0, expert_capacity=0) -> moe_layer_desc:
+              expert_stride, router_b=None, flags=0, expert_capacity=0,
+              expert_format=MOE_EXPERT_DTYPE) -> moe_layer_desc:
     return moe_layer_desc(ctypes.sizeof(moe_layer_desc), hidden, ffn, num_experts, top_k,
                           max_tokens, dtype, flags, _ptr(router_w), _ptr(router_b),
-                          _ptr(expert_base), expert_stride, expert_capacity, 0)
+                          _ptr(expert_base), expert_stride, expert_capacity, expert_format)
+
+
+def u8_stride(H, F):
+    """Bytes per uint8 expert: three matrices and the parameter block, to 256."""
+    return (3 * H * F + U8_PARAMS_BYTES + 255) // 256 * 256
+
+
+def moe_quantize_experts_u8(src, src_stride, E, H, F, dst, dst_stride, stream=None):
+    rc = lib().moe_quantize_experts_u8(_ptr(src), src_stride, E, H, F, _ptr(dst), dst_stride,
+                                       _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_quantize_experts_u8")
 
 
 def moe_layer_create(desc: moe_layer_desc) -> int:
@@ -141,15 +161,17 @@ class MoELayer:
     """Owns a libmoe layer handle and keeps the weight tensors it borrows alive."""
 
     def __init__(self, hidden, ffn, num_experts, top_k, max_tokens, dtype, router_w, experts,
-                 expert_stride, router_b=None, flags=0, expert_capacity=0):
+                 expert_stride, router_b=None, flags=0, expert_capacity=0,
+                 expert_format=MOE_EXPERT_DTYPE):
         self._keep = (router_w, experts, router_b)
         self.H, self.F, self.E, self.k = hidden, ffn, num_experts, top_k
         self.max_tokens = max_tokens
         self.dtype = dtype
         self.flags = flags
         self.expert_capacity = expert_capacity
+        self.expert_format = expert_format
         desc = make_desc(hidden, ffn, num_experts, top_k, max_tokens, dtype, router_w, experts,
-                         expert_stride, router_b, flags, expert_capacity)
+                         expert_stride, router_b, flags, expert_capacity, expert_format)
         self.handle = moe_layer_create(desc)
 
     def forward(self, x, y, T=None, stream=None):

@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
-SOURCES = ["moe_api.hip", "router.hip", "dispatch.hip", "expert_grouped.hip",
+SOURCES = ["moe_api.hip", "router.hip", "dispatch.hip", "expert_grouped.hip", "quantize.hip",
            "expert_stream.hip", "expert_f32.hip", "combine.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -22,8 +22,20 @@
 // 32-wide K steps of a chunk, and the four partial sums are added in LDS in
 // a fixed order (deterministic) before the gate/up epilogue applies SiLU(g)*u
 // and stores bf16, or the down epilogue stores fp32 rows for the combine.
+//
+// uint8 experts (weights (q - zero) * scale, one map per matrix
+// [www.pnsm.cn/news/1892388.html sec. 3.1 and sec. 5.2]): the weight runs
+// hold one byte per weight, so a chunk moves half the bytes; an item is 32
+// weight rows in both kernels.  In registers each group of 4 codes becomes
+// two fp16 pairs by a byte permute with 0x64 (fp16 1024 + q) and one packed
+// fp16 add of -(1024 + zero), exactly (q - zero); the bf16 token operand
+// becomes fp16 exactly (bf16 values in fp16's normal range are fp16
+// values), the MFMA is v_mfma_f32_16x16x32_f16, and the scale multiplies
+// the reduced sums once per output.
 #include "common.h"
 #include "kernels.h"
+
+#include <type_traits>
 
 namespace {
 
@@ -35,35 +47,72 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// One LDS row run holds CK/8 chunks of 16 bytes; chunk c of run r sits at
-// slot c ^ (r % 16), so the 16 lanes of an MFMA operand read (16 runs, one
-// chunk) hit 16 distinct bank groups.
-__device__ __forceinline__ int run_slot(int r, int c) { return c ^ (r & 15); }
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 
-template <bool GATED, int TR, int NS, int CK>
+__device__ __forceinline__ f32x4 mfma16(h8_t a, h8_t b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// 8 uint8 codes -> 8 fp16 values q - zero (bias = -(1024 + zero) in both
+// halves): byte permute of each code under the constant byte 0x64 gives the
+// fp16 value 1024 + q, exactly, and one packed add subtracts 1024 + zero.
+__device__ __forceinline__ h8_t dequant8(uint2 w, h2_t bias) {
+  constexpr uint32_t k64 = 0x64646464u;
+  const h2_t p0 = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(k64, w.x, 0x04010400u)) + bias;
+  const h2_t p1 = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(k64, w.x, 0x04030402u)) + bias;
+  const h2_t p2 = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(k64, w.y, 0x04010400u)) + bias;
+  const h2_t p3 = __builtin_bit_cast(h2_t, __builtin_amdgcn_perm(k64, w.y, 0x04030402u)) + bias;
+  return h8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+// 8 bf16 -> 8 fp16 (exact for magnitudes in fp16's normal range)
+__device__ __forceinline__ h8_t bf16_to_h8(u32x4 v) {
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  h8_t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto p = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(d[i] << 16),
+                                              __uint_as_float(d[i] & 0xFFFF0000u));
+    const h2_t h = __builtin_bit_cast(h2_t, p);
+    r[2 * i] = h.x;
+    r[2 * i + 1] = h.y;
+  }
+  return r;
+}
+
+// One LDS row run holds its chunks of 16 bytes with chunk c of run r at slot
+// c ^ (r % SPR) (SPR = chunks per run, at most 16), so the 16 lanes of an
+// MFMA operand read (16 runs, one chunk) spread over the bank groups.
+template <int SPR>
+__device__ __forceinline__ int run_slot(int r, int c) { return c ^ (r & ((SPR < 16 ? SPR : 16) - 1)); }
+
+template <bool GATED, bool Q8, int TR, int NS, int CK>
 __global__ __launch_bounds__(256) void stream_kernel(
-    const uint16_t* __restrict__ experts, uint64_t stride_elems,
+    const uint8_t* __restrict__ experts, uint64_t stride_elems,
     const uint16_t* __restrict__ tok, const int32_t* __restrict__ perm, int k_top,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ active, int E, int H,
     int F, int T, void* __restrict__ out) {
-  constexpr int NA = GATED ? 2 : 1;   // weight row blocks of 16 (gate, up)
-  constexpr int WR = 16 * NA;         // weight rows per item
-  constexpr int NB = (TR + 15) / 16;  // token column blocks of the MFMA
-  constexpr int RB = 2 * CK;          // bytes per row run
-  constexpr int SPR = CK / 8;         // 16-byte slots per run
-  constexpr int RPI = 64 / SPR;       // runs per 1 KB load
-  constexpr int IW = WR / RPI / 4;    // weight loads per wave per chunk
-  constexpr int IT = TR / RPI / 4;    // token loads per wave per chunk
-  constexpr int KSW = CK / 32 / 4;    // 32-wide K steps per wave per chunk
-  constexpr int STAGE = (WR + TR) * RB;
-  static_assert((CK == 128 || CK == 256 || CK == 512) && IT >= 1 && TR % (4 * RPI) == 0,
+  constexpr int WE = Q8 ? 1 : 2;                // bytes per weight
+  constexpr int NA = (GATED || Q8) ? 2 : 1;     // weight row blocks of 16 (gate, up)
+  constexpr int WR = 16 * NA;                   // weight rows per item
+  constexpr int NB = (TR + 15) / 16;            // token column blocks of the MFMA
+  constexpr int RBW = WE * CK, RBT = 2 * CK;    // bytes per weight / token row run
+  constexpr int SPRW = RBW / 16, SPRT = RBT / 16;  // 16-byte slots per run
+  constexpr int RPIW = 64 / SPRW, RPIT = 64 / SPRT;  // runs per 1 KB load
+  constexpr int IW = WR / RPIW / 4;             // weight loads per wave per chunk
+  constexpr int IT = TR / RPIT / 4;             // token loads per wave per chunk
+  constexpr int KSW = CK / 32 / 4;              // 32-wide K steps per wave per chunk
+  constexpr int STAGE = WR * RBW + TR * RBT;
+  static_assert((CK == 128 || CK == 256 || CK == 512) && IT >= 1 && TR % (4 * RPIT) == 0 &&
+                    IW >= 1 && WR % (4 * RPIW) == 0,
                 "chunk width and token rows per pass");
   static_assert(NS >= 2 && NS <= 4, "ring depth");
   __shared__ __attribute__((aligned(16))) uint8_t ring[NS][STAGE];
   __shared__ f32x4 red[4][NA * NB][64];
 
   const int K = GATED ? H : F;
-  const int NWT = (GATED ? F : H) / 16;
+  const int NWT = GATED ? F / 16 : H / WR;
   const int NC = K / CK;
   const int n_items = active[E] * NWT;
   const int G = gridDim.x;
@@ -73,7 +122,7 @@ __global__ __launch_bounds__(256) void stream_kernel(
   // ---- the load cursor: (item j of this workgroup, token pass, chunk) ----
   int l_j = 0, l_pass = 0, l_c = 0, l_npass = 0;
   bool l_ok = false;
-  const uint16_t* wsrc[IW];
+  const uint8_t* wsrc[IW];
   const uint16_t* tsrc[IT];
   auto l_item = [&]() {  // sets l_ok, l_npass and the weight sources for item l_j
     const int item = blockIdx.x + l_j * G;
@@ -83,19 +132,19 @@ __global__ __launch_bounds__(256) void stream_kernel(
     const int e = active[slot];
     const int n_e = offsets[e + 1] - offsets[e];
     l_npass = (n_e + TR - 1) / TR;
-    const uint16_t* eb = experts + (size_t)stride_elems * e;
+    const uint8_t* eb = experts + (size_t)stride_elems * WE * e;
 #pragma unroll
     for (int i = 0; i < IW; ++i) {
-      const int r = (wave * IW + i) * RPI + lane / SPR;  // weight row of the item
-      const uint16_t* row;
+      const int r = (wave * IW + i) * RPIW + lane / SPRW;  // weight row of the item
+      size_t w;  // weight index of the row's first element
       if (GATED)
-        row = eb + (size_t)(r < 16 ? 0 : F) * H + (size_t)(wt * 16 + (r & 15)) * H;
+        w = (size_t)(r < 16 ? 0 : F) * H + (size_t)(wt * 16 + (r & 15)) * H;
       else
-        row = eb + 2 * (size_t)F * H + (size_t)(wt * 16 + r) * F;
-      wsrc[i] = row + run_slot(r, lane % SPR) * 8;
+        w = 2 * (size_t)F * H + (size_t)(wt * WR + r) * F;
+      wsrc[i] = eb + w * WE + run_slot<SPRW>(r, lane % SPRW) * 16;
     }
   };
-  // token sources of pass l_pass of item l_j.  Each load covers RPI token
+  // token sources of pass l_pass of item l_j.  Each load covers RPIT token
   // rows; their indices are read with scalar loads (uniform addresses), so
   // no vector load the compiler would have to wait for joins the loads in
   // flight.
@@ -105,15 +154,15 @@ __global__ __launch_bounds__(256) void stream_kernel(
     const int p_beg = offsets[e], n_e = offsets[e + 1] - p_beg;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
-      const int r0 = (wave * IT + i) * RPI;  // token rows r0 .. r0 + RPI - 1 of the pass
+      const int r0 = (wave * IT + i) * RPIT;  // token rows r0 .. r0 + RPIT - 1 of the pass
       int xr = 0;
 #pragma unroll
-      for (int u = 0; u < RPI; ++u) {
+      for (int u = 0; u < RPIT; ++u) {
         const int p = p_beg + min(l_pass * TR + r0 + u, n_e - 1);
         const int x = GATED ? min(max(perm[p], 0) / k_top, T - 1) : p;
-        if (lane / SPR == u) xr = x;
+        if (lane / SPRT == u) xr = x;
       }
-      tsrc[i] = tok + (size_t)xr * K + run_slot(r0 + lane / SPR, lane % SPR) * 8;
+      tsrc[i] = tok + (size_t)xr * K + run_slot<SPRT>(r0 + lane / SPRT, lane % SPRT) * 8;
     }
   };
   // issue the chunk under the load cursor into stage st, then advance it
@@ -123,15 +172,15 @@ __global__ __launch_bounds__(256) void stream_kernel(
     const int k0 = l_c * CK;
 #pragma unroll
     for (int i = 0; i < IW; ++i) {
-      const uint32_t dst = base + (uint32_t)((wave * IW + i) * RPI * RB);
+      const uint32_t dst = base + (uint32_t)((wave * IW + i) * RPIW * RBW);
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
                    :
-                   : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(wsrc[i] + k0)
+                   : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(wsrc[i] + k0 * WE)
                    : "memory", "m0");
     }
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
-      const uint32_t dst = base + (uint32_t)((WR + (wave * IT + i) * RPI) * RB);
+      const uint32_t dst = base + (uint32_t)(WR * RBW + (wave * IT + i) * RPIT * RBT);
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                    :
                    : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(tsrc[i] + k0)
@@ -152,6 +201,8 @@ __global__ __launch_bounds__(256) void stream_kernel(
   int c_j = 0, c_pass = 0, c_c = 0;
   int c_wt = 0, c_pbeg = 0, c_ne = 0, c_npass = 0;
   bool c_ok = false;
+  float c_scale[NA];  // uint8 experts: scale of each weight row block
+  h2_t c_bias[NA];    // and -(1024 + zero point) for the dequantisation
   auto c_item = [&]() {
     const int item = blockIdx.x + c_j * G;
     c_ok = item < n_items;
@@ -162,6 +213,16 @@ __global__ __launch_bounds__(256) void stream_kernel(
     c_pbeg = offsets[e];
     c_ne = offsets[e + 1] - c_pbeg;
     c_npass = (c_ne + TR - 1) / TR;
+    if (Q8) {  // parameter block after the three matrices: scale[3], zero[3]
+      const uint8_t* pb = experts + (size_t)stride_elems * e + 3 * (size_t)F * H;
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        const int m = GATED ? i : 2;
+        c_scale[i] = reinterpret_cast<const float*>(pb)[m];
+        const _Float16 b = (_Float16)(-(1024 + reinterpret_cast<const int32_t*>(pb)[3 + m]));
+        c_bias[i] = h2_t{b, b};
+      }
+    }
   };
 
   l_item();
@@ -202,19 +263,28 @@ __global__ __launch_bounds__(256) void stream_kernel(
     const uint8_t* sb = &ring[st][0];
 #pragma unroll
     for (int s2 = 0; s2 < KSW; ++s2) {
-      const int c = (wave * KSW + s2) * 4 + kg;  // 16-byte chunk of the run
-      bf16x8 a[NA], b[NB];
+      const int c = (wave * KSW + s2) * 4 + kg;  // group of 8 K elements in the run
+      using op_t = typename std::conditional<Q8, h8_t, bf16x8>::type;
+      op_t a[NA], b[NB];
 #pragma unroll
       for (int i = 0; i < NA; ++i) {
         const int r = i * 16 + r16;
-        a[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(sb + r * RB + run_slot(r, c) * 16));
+        if constexpr (Q8) {  // 8 bytes: half of 16-byte chunk c / 2
+          const uint2 w8 = *reinterpret_cast<const uint2*>(sb + r * RBW +
+                                                           run_slot<SPRW>(r, c >> 1) * 16 + (c & 1) * 8);
+          a[i] = dequant8(w8, c_bias[i]);
+        } else {
+          a[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(sb + r * RBW + run_slot<SPRW>(r, c) * 16));
+        }
       }
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
         // token columns beyond TR read row 0 again; their results are dropped
         const int r = n * 16 + r16 < TR ? n * 16 + r16 : 0;
-        b[n] = as_bf16x8(
-            *reinterpret_cast<const u32x4*>(sb + (WR + r) * RB + run_slot(r, c) * 16));
+        const u32x4 v =
+            *reinterpret_cast<const u32x4*>(sb + WR * RBW + r * RBT + run_slot<SPRT>(r, c) * 16);
+        if constexpr (Q8) b[n] = bf16_to_h8(v);
+        else b[n] = as_bf16x8(v);
       }
 #pragma unroll
       for (int n = 0; n < NB; ++n)
@@ -242,16 +312,18 @@ __global__ __launch_bounds__(256) void stream_kernel(
         const int t = c_pass * TR + col;
         if (col < TR && t < c_ne) {
           const int p = c_pbeg + t;
-          const int r0 = c_wt * 16 + 4 * (l >> 4);
+          const int r0 = c_wt * (GATED ? 16 : WR) + 4 * (l >> 4);
           f32x4 g = red[0][n][l];
           g += red[1][n][l];
           g += red[2][n][l];
           g += red[3][n][l];
+          if (Q8) g *= c_scale[0];
           if (GATED) {
             f32x4 u = red[0][NB + n][l];
             u += red[1][NB + n][l];
             u += red[2][NB + n][l];
             u += red[3][NB + n][l];
+            if (Q8) u *= c_scale[1];
             const bf16x2 lo = {(__bf16)(silu_f32(g[0]) * u[0]), (__bf16)(silu_f32(g[1]) * u[1])};
             const bf16x2 hi = {(__bf16)(silu_f32(g[2]) * u[2]), (__bf16)(silu_f32(g[3]) * u[3])};
             uint2 pk;
@@ -260,6 +332,13 @@ __global__ __launch_bounds__(256) void stream_kernel(
             *reinterpret_cast<uint2*>((uint16_t*)out + (size_t)p * F + r0) = pk;
           } else {
             *reinterpret_cast<f32x4*>((float*)out + (size_t)p * H + r0) = g;
+            if (NA == 2) {  // uint8 experts: the item's second block of 16 rows
+              f32x4 g2 = red[0][NB + n][l];
+              g2 += red[1][NB + n][l];
+              g2 += red[2][NB + n][l];
+              g2 += red[3][NB + n][l];
+              *reinterpret_cast<f32x4*>((float*)out + (size_t)p * H + r0 + 16) = g2 * c_scale[1];
+            }
           }
         }
       }
@@ -274,41 +353,46 @@ __global__ __launch_bounds__(256) void stream_kernel(
   WAIT_VMCNT(0);
 }
 
-template <bool GATED, int TR, int NS, int CK>
+template <bool GATED, bool Q8, int TR, int NS, int CK>
 int launch_tr(const ExpertArgs& a, hipStream_t st) {
-  constexpr int NA = GATED ? 2 : 1, NB = (TR + 15) / 16;
-  constexpr int lds = NS * (16 * NA + TR) * 2 * CK + 4 * NA * NB * 64 * 16;
+  constexpr int NA = (GATED || Q8) ? 2 : 1, NB = (TR + 15) / 16;
+  constexpr int lds = NS * (16 * NA * (Q8 ? 1 : 2) + TR * 2) * CK + 4 * NA * NB * 64 * 16;
   const int per_cu = (160 * 1024) / lds;
-  const int nwt = (GATED ? a.F : a.H) / 16;
+  const int nwt = GATED ? a.F / 16 : a.H / (16 * NA);
   const int slots = a.E < a.S ? a.E : a.S;
   int grid = cu_count() * (per_cu < 1 ? 1 : per_cu);
   if (grid > nwt * slots) grid = nwt * slots;
   const uint16_t* tok = GATED ? (const uint16_t*)a.x : (const uint16_t*)a.act;
   void* out = GATED ? a.act : (void*)a.yp;
-  stream_kernel<GATED, TR, NS, CK><<<grid, 256, 0, st>>>(
-      (const uint16_t*)a.experts, a.stride_elems, tok, a.perm, a.k, a.offsets, a.active, a.E,
+  stream_kernel<GATED, Q8, TR, NS, CK><<<grid, 256, 0, st>>>(
+      (const uint8_t*)a.experts, a.stride_elems, tok, a.perm, a.k, a.offsets, a.active, a.E,
       a.H, a.F, a.T, out);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-template <bool GATED>
-int launch_stream(const ExpertArgs& a, hipStream_t st) {
+template <bool GATED, bool Q8>
+int launch_stream_q(const ExpertArgs& a, hipStream_t st) {
   // token rows per pass (experts with more rows take several passes) and the
   // chunk width: 512 for the down projection of small batches, else 256 when
   // K allows it (bf16 layers have H % 256 == 0 and F % 128 == 0), else 128
   const int rows = a.rows_hint;
   const int K = GATED ? a.H : a.F;
   if (!GATED && K % 512 == 0 && rows <= 16) {  // down: 1 KB row runs
-    if (rows <= 8) return launch_tr<GATED, 8, 3, 512>(a, st);
-    return launch_tr<GATED, 16, 3, 512>(a, st);
+    if (rows <= 8) return launch_tr<GATED, Q8, 8, 3, 512>(a, st);
+    return launch_tr<GATED, Q8, 16, 3, 512>(a, st);
   }
   if (K % 256 == 0) {
-    if (rows <= 8) return launch_tr<GATED, 8, GATED ? 3 : 4, 256>(a, st);
-    if (rows <= 16) return launch_tr<GATED, 16, GATED ? 3 : 4, 256>(a, st);
-    return launch_tr<GATED, 32, GATED ? 2 : 3, 256>(a, st);
+    if (rows <= 8) return launch_tr<GATED, Q8, 8, GATED ? 3 : 4, 256>(a, st);
+    if (rows <= 16) return launch_tr<GATED, Q8, 16, GATED ? 3 : 4, 256>(a, st);
+    return launch_tr<GATED, Q8, 32, GATED ? 2 : 3, 256>(a, st);
   }
-  if (rows <= 16) return launch_tr<GATED, 16, 4, 128>(a, st);
-  return launch_tr<GATED, 32, GATED ? 3 : 4, 128>(a, st);
+  if (rows <= 16) return launch_tr<GATED, Q8, 16, 4, 128>(a, st);
+  return launch_tr<GATED, Q8, 32, GATED ? 3 : 4, 128>(a, st);
+}
+
+template <bool GATED>
+int launch_stream(const ExpertArgs& a, hipStream_t st) {
+  return a.u8 ? launch_stream_q<GATED, true>(a, st) : launch_stream_q<GATED, false>(a, st);
 }
 
 }  // namespace

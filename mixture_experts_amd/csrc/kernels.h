@@ -47,7 +47,8 @@ struct DispatchArgs {
 struct ExpertArgs {
   const void* x;            // [T][H] layer input (bf16 or fp32)
   const void* experts;      // expert blocks
-  uint64_t stride_elems;    // expert stride in elements
+  uint64_t stride_elems;    // expert stride in elements (bytes for uint8 experts)
+  int u8;                   // experts are uint8 codes + parameter blocks
   int T, H, F, E, k, S;
   int rows_hint;            // rows per expert one streaming pass should cover
   const int32_t* perm;      // [S]
@@ -76,12 +77,17 @@ int launch_grouped_gate_up(const ExpertArgs& a, hipStream_t st);
 // with 2 it writes two partial planes yp[2][S][H]
 int grouped_down_ksplit(const ExpertArgs& a);
 int launch_grouped_down(const ExpertArgs& a, int ksplit, hipStream_t st);
-// bf16 expert FFN, weight-streaming MFMA kernels (few rows per expert)
+// bf16 expert FFN, weight-streaming MFMA kernels (few rows per expert; every
+// batch for uint8 experts)
 int launch_stream_gate_up(const ExpertArgs& a, hipStream_t st);
 int launch_stream_down(const ExpertArgs& a, hipStream_t st);
 // fp32 expert FFN (plain FMA)
 int launch_f32_gate_up(const ExpertArgs& a, hipStream_t st);
 int launch_f32_down(const ExpertArgs& a, hipStream_t st);
+
+// uint8 expert weights from bf16 ones (parameter blocks of dst as scratch)
+int launch_quantize_u8(const void* src, uint64_t src_stride, int E, int H, int F, void* dst,
+                       uint64_t dst_stride, hipStream_t st);
 
 // y[t] = resid[t] + sum_j w[t][j] * (sum over planes q of yp[q][inv[t*k+j]])
 int launch_combine(const float* yp, int nplanes, const float* w, const int32_t* inv,

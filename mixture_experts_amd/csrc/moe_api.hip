@@ -79,7 +79,13 @@ int validate_desc(const moe_layer_desc* d) {
   if (d->router_b && ((uintptr_t)d->router_b & 3u)) return MOE_ERR_INVALID_ARG;
   const uint64_t es = d->dtype == MOE_F32 ? 4 : 2;
   const uint64_t H = (uint64_t)d->hidden, F = (uint64_t)d->ffn;
-  if (d->expert_stride < 3 * H * F * es || (d->expert_stride & 255u)) return MOE_ERR_INVALID_ARG;
+  if (d->expert_format != MOE_EXPERT_DTYPE && d->expert_format != MOE_EXPERT_U8)
+    return MOE_ERR_INVALID_ARG;
+  const bool u8 = d->expert_format == MOE_EXPERT_U8;
+  const uint64_t need = u8 ? 3 * H * F + sizeof(moe_u8_params) : 3 * H * F * es;
+  if (d->expert_stride < need || (d->expert_stride & 255u)) return MOE_ERR_INVALID_ARG;
+  if (u8 && (d->dtype != MOE_BF16 || (d->flags & MOE_FLAG_PATH_GROUPED)))
+    return MOE_ERR_UNSUPPORTED;
   if (d->num_experts > MOE_MAX_EXPERTS || d->top_k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   if (d->dtype == MOE_BF16 && (H % 256 || F % 128)) return MOE_ERR_UNSUPPORTED;
   if (d->dtype == MOE_F32 && (H % 4 || F % 4)) return MOE_ERR_UNSUPPORTED;
@@ -88,8 +94,7 @@ int validate_desc(const moe_layer_desc* d) {
   const uint64_t lim = 1ull << 31;
   if (S * (H > F ? H : F) >= lim || 3 * H * F >= lim || (uint64_t)d->max_tokens * H >= lim)
     return MOE_ERR_UNSUPPORTED;
-  if (d->expert_stride % es) return MOE_ERR_INVALID_ARG;
-  if (d->expert_capacity < 0 || d->reserved != 0) return MOE_ERR_INVALID_ARG;
+  if (d->expert_capacity < 0) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
@@ -146,6 +151,7 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 bool use_stream_path(const moe_layer* L, int T) {
+  if (L->d.expert_format == MOE_EXPERT_U8) return true;
   if (L->d.flags & MOE_FLAG_PATH_STREAM) return true;
   if (L->d.flags & MOE_FLAG_PATH_GROUPED) return false;
   // average rows per expert; the grouped GEMM works on 256-row tiles
@@ -306,7 +312,8 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
   ExpertArgs ea{};
   ea.x = xin;
   ea.experts = d.expert_base;
-  ea.stride_elems = d.expert_stride / L->esize;
+  ea.u8 = d.expert_format == MOE_EXPERT_U8;
+  ea.stride_elems = ea.u8 ? d.expert_stride : d.expert_stride / L->esize;
   ea.T = T;
   ea.H = d.hidden;
   ea.F = d.ffn;
@@ -347,6 +354,24 @@ void moe_layer_free(moe_layer_t* L) {
     if (L->ws) (void)hipFree(L->ws);
   }
   free(L);
+}
+
+int moe_quantize_experts_u8(const void* src, uint64_t src_stride, int32_t E, int32_t H,
+                            int32_t F, void* dst, uint64_t dst_stride, void* stream) {
+  static_assert(sizeof(moe_u8_params) == 64, "parameter block");
+  if (!src || !dst || !aligned16(src) || !aligned16(dst)) return MOE_ERR_INVALID_ARG;
+  if (E < 1 || H < 1 || F < 1 || H % 16 || F % 16) return MOE_ERR_INVALID_ARG;
+  const uint64_t hf = (uint64_t)H * (uint64_t)F;
+  if (3 * hf >= (1ull << 31)) return MOE_ERR_INVALID_ARG;
+  if (src_stride < 6 * hf || dst_stride < 3 * hf + sizeof(moe_u8_params) || (src_stride & 255u) ||
+      (dst_stride & 255u))
+    return MOE_ERR_INVALID_ARG;
+  const uint64_t ns = (uint64_t)(E - 1) * src_stride + 6 * hf;
+  const uint64_t nd = (uint64_t)(E - 1) * dst_stride + 3 * hf + sizeof(moe_u8_params);
+  if (ranges_overlap(src, ns, dst, nd)) return MOE_ERR_INVALID_ARG;
+  if (launch_quantize_u8(src, src_stride, E, H, F, dst, dst_stride, (hipStream_t)stream))
+    return MOE_ERR_DEVICE;
+  return MOE_OK;
 }
 
 }  // extern "C"

@@ -37,6 +37,7 @@ def test_desc_layout():
     assert moe.moe_layer_desc.router_w.offset == 32
     assert moe.moe_layer_desc.expert_stride.offset == 56
     assert moe.moe_layer_desc.expert_capacity.offset == 64
+    assert moe.moe_layer_desc.expert_format.offset == 68
 
 
 def _desc(**kw):
@@ -72,6 +73,15 @@ def _desc(**kw):
     (dict(dtype=moe.MOE_F32, flags=moe.MOE_FLAG_RESIDUAL_PRENORM,
           expert_stride=3 * 256 * 256 * 4), moe.MOE_ERR_UNSUPPORTED),
     (dict(hidden=65536, ffn=65536, expert_stride=3 * 65536 * 65536 * 2), moe.MOE_ERR_UNSUPPORTED),
+    (dict(expert_format=2), moe.MOE_ERR_INVALID_ARG),
+    (dict(expert_format=-1), moe.MOE_ERR_INVALID_ARG),
+    # uint8 experts: room for the 64-byte parameter block, bf16 layers, streaming path only
+    (dict(expert_format=moe.MOE_EXPERT_U8, expert_stride=3 * 256 * 256), moe.MOE_ERR_INVALID_ARG),
+    (dict(expert_format=moe.MOE_EXPERT_U8, expert_stride=3 * 256 * 256 + 256 + 128), moe.MOE_ERR_INVALID_ARG),
+    (dict(expert_format=moe.MOE_EXPERT_U8, expert_stride=3 * 256 * 256 + 256, dtype=moe.MOE_F32),
+     moe.MOE_ERR_UNSUPPORTED),
+    (dict(expert_format=moe.MOE_EXPERT_U8, expert_stride=3 * 256 * 256 + 256, flags=moe.MOE_FLAG_PATH_GROUPED),
+     moe.MOE_ERR_UNSUPPORTED),
 ])
 def test_create_rejects_bad_descriptors(kw, code):
     with pytest.raises(moe.MoeError) as ei:
@@ -87,11 +97,25 @@ def test_struct_size_is_checked():
     assert ei.value.code == moe.MOE_ERR_INVALID_ARG
 
 
-def test_reserved_field_must_be_zero():
-    d = _desc()
-    d.reserved = 1
+def test_u8_stride_helper():
+    assert moe.u8_stride(4096, 14336) == 3 * 4096 * 14336 + 256
+    assert moe.u8_stride(256, 256) % 256 == 0 and moe.u8_stride(256, 256) >= 3 * 65536 + 64
+
+
+@pytest.mark.parametrize("kw", [
+    dict(src=None), dict(dst=None), dict(src=0x10008), dict(dst=0x20004), dict(E=0),
+    dict(H=24), dict(F=40), dict(src_stride=6 * 256 * 256 - 256), dict(src_stride=6 * 65536 + 16),
+    dict(dst_stride=3 * 256 * 256), dict(dst_stride=3 * 65536 + 320),
+    dict(dst=0x10000 + 6 * 65536 - 256),                 # overlaps the source
+    dict(H=32768, F=32768, src_stride=6 * 2 ** 30, dst_stride=3 * 2 ** 30 + 256),
+])
+def test_quantize_rejects_bad_arguments(kw):
+    args = dict(src=0x10000, src_stride=6 * 256 * 256, E=2, H=256, F=256, dst=0x10000000,
+                dst_stride=3 * 256 * 256 + 256)
+    args.update(kw)
     with pytest.raises(moe.MoeError) as ei:
-        moe.moe_layer_create(d)
+        moe.moe_quantize_experts_u8(args["src"], args["src_stride"], args["E"], args["H"],
+                                    args["F"], args["dst"], args["dst_stride"], stream=0)
     assert ei.value.code == moe.MOE_ERR_INVALID_ARG
 
 
