@@ -5,7 +5,9 @@ bf16 weights and activations, fp32 accumulation) on a prefill batch of
 T=4096 tokens; one step = one full layer forward (router, top-k + softmax,
 dispatch, gate/up + SiLU, down, combine) over the batch, inputs resident in
 HBM.  Then decode batches T = 1, 4, 16, 64 on the same layer shape (HIP-graph
-replays over four copies of the weights) and the 32-layer stacked decode.
+replays over four copies of the weights) and the 32-layer stacked decode, each
+with bf16 experts and again with uint8 experts (one affine map per matrix,
+quantised on the device from the same bf16 weights).
 
 Prints ONE JSON line.  `roofline` describes the dominant kernel (the
 gate/up GEMM of the prefill step), timed with HIP events recorded by the
@@ -68,13 +70,61 @@ def parse():
     return ap.parse_args()
 
 
-def bench_decode(shape, x, y, K, W, run_ev):
+def expert_blob(shape, n_blocks, u8, layer_of=lambda b: 0):
+    """Device buffer of n_blocks layers' experts (block b generated as layer
+    layer_of(b)); with u8, quantised on the device from the bf16 weights.
+    Returns (buffer, bytes per expert)."""
+    import torch
+
+    import gen
+    import mixture_experts_amd as moe
+    st = torch.cuda.current_stream()
+    if not u8:
+        blob = torch.empty(n_blocks * shape.E * shape.stride, dtype=torch.uint8, device="cuda")
+        for b in range(n_blocks):
+            gen.experts_device(shape, blob.data_ptr() + b * shape.E * shape.stride,
+                               layer=layer_of(b), stream=st.cuda_stream)
+        return blob, shape.stride
+    ust = moe.u8_stride(shape.H, shape.F)
+    blob = torch.empty(n_blocks * shape.E * ust, dtype=torch.uint8, device="cuda")
+    tmp = torch.empty(shape.E * shape.stride, dtype=torch.uint8, device="cuda")
+    for b in range(n_blocks):
+        gen.experts_device(shape, tmp.data_ptr(), layer=layer_of(b), stream=st.cuda_stream)
+        moe.moe_quantize_experts_u8(tmp, shape.stride, shape.E, shape.H, shape.F,
+                                    blob.data_ptr() + b * shape.E * ust, ust, st)
+    torch.cuda.synchronize()
+    del tmp
+    return blob, ust
+
+
+def stage_times(layer, x, y, T, steps, warm):
+    """Per-stage device times (ms) of eager forwards, from the library's events."""
+    import torch
+
+    import mixture_experts_amd as moe
+    st = torch.cuda.current_stream()
+    nst = moe.MOE_NUM_STAGES
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(steps)]
+    for row in evs:
+        for e in row:
+            e.record(st)
+    for _ in range(warm):
+        moe.moe_forward(layer.handle, x, T, y, st)
+    for i in range(steps):
+        moe.moe_forward_ev(layer.handle, x, T, y, st, [e.cuda_event for e in evs[i]])
+    torch.cuda.synchronize()
+    return [sum(evs[i][s].elapsed_time(evs[i][s + 1]) for i in range(steps)) / steps
+            for s in range(nst)]
+
+
+def bench_decode(shape, x, y, K, W, u8=False):
     """The Mixtral-shaped layer on decode batches T = 1, 4, 16, 64.  Four
-    copies of the layer's experts (4 x 2.8 GB, far beyond the 256 MB of
-    Infinity Cache) are visited in turn, one HIP-graph replay = one forward of
-    each copy, so no repeat is served from a cache; the step time is the
-    replay time / 4.  Stage times come from a separate eager pass with the
-    library's per-stage events (they include the event overhead)."""
+    copies of the layer's experts (4 x 2.8 GB bf16 or 4 x 1.4 GB uint8, far
+    beyond the 256 MB of Infinity Cache) are visited in turn, one HIP-graph
+    replay = one forward of each copy, so no repeat is served from a cache;
+    the step time is the replay time / 4.  Stage times come from a separate
+    eager pass with the library's per-stage events (they include the event
+    overhead)."""
     import numpy as np
     import torch
 
@@ -82,23 +132,22 @@ def bench_decode(shape, x, y, K, W, run_ev):
     import mixture_experts_amd as moe
     NCOPY = 4
     st = torch.cuda.current_stream()
-    blob = torch.empty(NCOPY * shape.E * shape.stride, dtype=torch.uint8, device="cuda")
+    blob, stride = expert_blob(shape, NCOPY, u8)
     wr = torch.from_numpy(gen.gen_router(shape).view(np.int16)).cuda()
-    layers = []
-    for c in range(NCOPY):
-        base = blob.data_ptr() + c * shape.E * shape.stride
-        gen.experts_device(shape, base, layer=0, stream=st.cuda_stream)
-        layers.append(moe.MoELayer(shape.H, shape.F, shape.E, shape.k, 64, moe.MOE_BF16, wr,
-                                   base, shape.stride))
+    fmt = moe.MOE_EXPERT_U8 if u8 else moe.MOE_EXPERT_DTYPE
+    layers = [moe.MoELayer(shape.H, shape.F, shape.E, shape.k, 64, moe.MOE_BF16, wr,
+                           blob.data_ptr() + c * shape.E * stride, stride, expert_format=fmt)
+              for c in range(NCOPY)]
     torch.cuda.synchronize()
-    eb = 3 * shape.H * shape.F * 2
-    res = {"weight_copies": NCOPY}
+    wbytes = 1 if u8 else 2  # per weight
+    eb = 3 * shape.H * shape.F * wbytes + (64 if u8 else 0)
+    res = {"weight_copies": NCOPY, "expert_weights": "uint8 (affine per matrix)" if u8 else "bf16"}
     for Td in (1, 4, 16, 64):
         xd, yd = x[:Td], y[:Td]
         r = layers[0].route(xd, Td)
         torch.cuda.synchronize()
         touched = int((r["counts"] > 0).sum().item())
-        _, st_d, _ = run_ev(xd, yd, Td, 20, W)
+        st_d = stage_times(layers[0], xd, yd, Td, 20, W)
         side = torch.cuda.Stream()
         side.wait_stream(st)
         with torch.cuda.stream(side):
@@ -123,7 +172,7 @@ def bench_decode(shape, x, y, K, W, run_ev):
         wall = (time.perf_counter() - t0) / (K * NCOPY)
         dev_s = e0.elapsed_time(e1) * 1e-3 / (K * NCOPY)
         bytes_step = touched * eb + shape.H * shape.E * 2 + Td * shape.H * (2 + 4)
-        gu_bytes = touched * 2 * shape.H * shape.F * 2
+        gu_bytes = touched * 2 * shape.H * shape.F * wbytes
         res[f"T{Td}"] = {
             "tokens_per_s": round(Td / wall, 1),
             "ms_per_step": round(wall * 1e3, 4),
@@ -141,7 +190,7 @@ def bench_decode(shape, x, y, K, W, run_ev):
     return res
 
 
-def bench_stack(K, W):
+def bench_stack(K, W, u8=False):
     """32 Mixtral-shaped layers, experts in one contiguous buffer (layer l,
     expert e at blob + (l*E + e)*stride), residual stream h <- h + MoE(norm(h));
     one step = all 32 layers on a decode batch, replayed as one HIP graph."""
@@ -152,18 +201,20 @@ def bench_stack(K, W):
     import mixture_experts_amd as moe
     shape, NL = gen.MIXTRAL, 32
     st = torch.cuda.current_stream()
-    blob = torch.empty(NL * shape.E * shape.stride, dtype=torch.uint8, device="cuda")
+    blob, stride = expert_blob(shape, NL, u8, layer_of=lambda b: b)
+    fmt = moe.MOE_EXPERT_U8 if u8 else moe.MOE_EXPERT_DTYPE
     layers, keep = [], []
     for l in range(NL):
-        base = blob.data_ptr() + l * shape.E * shape.stride
-        gen.experts_device(shape, base, layer=l, stream=st.cuda_stream)
+        base = blob.data_ptr() + l * shape.E * stride
         wr = torch.from_numpy(gen.gen_router(shape, layer=l).view(np.int16)).cuda()
         keep.append(wr)
         layers.append(moe.MoELayer(shape.H, shape.F, shape.E, shape.k, 64, moe.MOE_BF16, wr,
-                                   base, shape.stride, flags=moe.MOE_FLAG_RESIDUAL_PRENORM))
+                                   base, stride, flags=moe.MOE_FLAG_RESIDUAL_PRENORM,
+                                   expert_format=fmt))
     torch.cuda.synchronize()
-    eb = 3 * shape.H * shape.F * 2
-    res = {"layers": NL, "expert_buffer_GB": round(blob.numel() / 1e9, 2)}
+    eb = 3 * shape.H * shape.F * (1 if u8 else 2) + (64 if u8 else 0)
+    res = {"layers": NL, "expert_buffer_GB": round(blob.numel() / 1e9, 2),
+           "expert_weights": "uint8 (affine per matrix)" if u8 else "bf16"}
     for T in (1, 4, 16, 64):
         x0 = torch.from_numpy(gen.normal(0, 0, gen.T_X, T * shape.H, 1.0, "f32")).cuda()
         x0 = x0.view(T, shape.H)
@@ -297,11 +348,15 @@ def main():
     }
 
     if not args.no_decode and args.workload == "mixtral_prefill":
-        out["decode"] = bench_decode(shape, x, y, max(K, 50), W, run)
+        print("[bench] decode batches, bf16 and uint8 experts", file=sys.stderr, flush=True)
+        out["decode"] = bench_decode(shape, x, y, max(K, 50), W)
+        out["decode_u8"] = bench_decode(shape, x, y, max(K, 50), W, u8=True)
 
     if not args.no_stack and args.workload == "mixtral_prefill":
-        print("[bench] 32-layer stacked decode", file=sys.stderr, flush=True)
+        print("[bench] 32-layer stacked decode, bf16 and uint8 experts", file=sys.stderr,
+              flush=True)
         out["stack_decode"] = bench_stack(max(K, 20), W)
+        out["stack_decode_u8"] = bench_stack(max(K, 20), W, u8=True)
 
     if not args.no_cpu_baseline:
         import oracle

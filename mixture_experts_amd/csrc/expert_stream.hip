@@ -25,8 +25,8 @@
 //
 // uint8 experts (weights (q - zero) * scale, one map per matrix
 // [www.pnsm.cn/news/1892388.html sec. 3.1 and sec. 5.2]): the weight runs
-// hold one byte per weight, so a chunk moves half the bytes; an item is 32
-// weight rows in both kernels.  In registers each group of 4 codes becomes
+// hold one byte per weight, and an item is 16, 32 or 64 weight rows (QNA
+// blocks of 16) as the batch size suits.  In registers each group of 4 codes becomes
 // two fp16 pairs by a byte permute with 0x64 (fp16 1024 + q) and one packed
 // fp16 add of -(1024 + zero), exactly (q - zero); the bf16 token operand
 // becomes fp16 exactly (bf16 values in fp16's normal range are fp16
@@ -87,15 +87,16 @@ __device__ __forceinline__ h8_t bf16_to_h8(u32x4 v) {
 template <int SPR>
 __device__ __forceinline__ int run_slot(int r, int c) { return c ^ (r & ((SPR < 16 ? SPR : 16) - 1)); }
 
-template <bool GATED, bool Q8, int TR, int NS, int CK>
+template <bool GATED, bool Q8, int QNA, int TR, int NS, int CK>
 __global__ __launch_bounds__(256) void stream_kernel(
     const uint8_t* __restrict__ experts, uint64_t stride_elems,
     const uint16_t* __restrict__ tok, const int32_t* __restrict__ perm, int k_top,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ active, int E, int H,
     int F, int T, void* __restrict__ out) {
   constexpr int WE = Q8 ? 1 : 2;                // bytes per weight
-  constexpr int NA = (GATED || Q8) ? 2 : 1;     // weight row blocks of 16 (gate, up)
+  constexpr int NA = Q8 ? QNA : (GATED ? 2 : 1);  // weight row blocks of 16 per item
   constexpr int WR = 16 * NA;                   // weight rows per item
+  constexpr int OB = GATED ? NA / 2 : NA;       // output row blocks of 16 per item
   constexpr int NB = (TR + 15) / 16;            // token column blocks of the MFMA
   constexpr int RBW = WE * CK, RBT = 2 * CK;    // bytes per weight / token row run
   constexpr int SPRW = RBW / 16, SPRT = RBT / 16;  // 16-byte slots per run
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(256) void stream_kernel(
   __shared__ f32x4 red[4][NA * NB][64];
 
   const int K = GATED ? H : F;
-  const int NWT = GATED ? F / 16 : H / WR;
+  const int NWT = GATED ? F / (16 * OB) : H / WR;
   const int NC = K / CK;
   const int n_items = active[E] * NWT;
   const int G = gridDim.x;
@@ -137,8 +138,8 @@ __global__ __launch_bounds__(256) void stream_kernel(
     for (int i = 0; i < IW; ++i) {
       const int r = (wave * IW + i) * RPIW + lane / SPRW;  // weight row of the item
       size_t w;  // weight index of the row's first element
-      if (GATED)
-        w = (size_t)(r < 16 ? 0 : F) * H + (size_t)(wt * 16 + (r & 15)) * H;
+      if (GATED)  // rows 0 .. 16 OB - 1 gate, then the same f rows of up
+        w = (size_t)(r < 16 * OB ? 0 : F) * H + (size_t)(wt * 16 * OB + r % (16 * OB)) * H;
       else
         w = 2 * (size_t)F * H + (size_t)(wt * WR + r) * F;
       wsrc[i] = eb + w * WE + run_slot<SPRW>(r, lane % SPRW) * 16;
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(256) void stream_kernel(
       const uint8_t* pb = experts + (size_t)stride_elems * e + 3 * (size_t)F * H;
 #pragma unroll
       for (int i = 0; i < NA; ++i) {
-        const int m = GATED ? i : 2;
+        const int m = GATED ? (i < OB ? 0 : 1) : 2;
         c_scale[i] = reinterpret_cast<const float*>(pb)[m];
         const _Float16 b = (_Float16)(-(1024 + reinterpret_cast<const int32_t*>(pb)[3 + m]));
         c_bias[i] = h2_t{b, b};
@@ -312,32 +313,28 @@ __global__ __launch_bounds__(256) void stream_kernel(
         const int t = c_pass * TR + col;
         if (col < TR && t < c_ne) {
           const int p = c_pbeg + t;
-          const int r0 = c_wt * (GATED ? 16 : WR) + 4 * (l >> 4);
-          f32x4 g = red[0][n][l];
-          g += red[1][n][l];
-          g += red[2][n][l];
-          g += red[3][n][l];
-          if (Q8) g *= c_scale[0];
-          if (GATED) {
-            f32x4 u = red[0][NB + n][l];
-            u += red[1][NB + n][l];
-            u += red[2][NB + n][l];
-            u += red[3][NB + n][l];
-            if (Q8) u *= c_scale[1];
-            const bf16x2 lo = {(__bf16)(silu_f32(g[0]) * u[0]), (__bf16)(silu_f32(g[1]) * u[1])};
-            const bf16x2 hi = {(__bf16)(silu_f32(g[2]) * u[2]), (__bf16)(silu_f32(g[3]) * u[3])};
-            uint2 pk;
-            pk.x = __builtin_bit_cast(uint32_t, lo);
-            pk.y = __builtin_bit_cast(uint32_t, hi);
-            *reinterpret_cast<uint2*>((uint16_t*)out + (size_t)p * F + r0) = pk;
-          } else {
-            *reinterpret_cast<f32x4*>((float*)out + (size_t)p * H + r0) = g;
-            if (NA == 2) {  // uint8 experts: the item's second block of 16 rows
-              f32x4 g2 = red[0][NB + n][l];
-              g2 += red[1][NB + n][l];
-              g2 += red[2][NB + n][l];
-              g2 += red[3][NB + n][l];
-              *reinterpret_cast<f32x4*>((float*)out + (size_t)p * H + r0 + 16) = g2 * c_scale[1];
+          const int r0 = c_wt * 16 * OB + 4 * (l >> 4);
+          auto block = [&](int i) {  // the waves' partials of row block i, in wave order
+            f32x4 v = red[0][i * NB + n][l];
+            v += red[1][i * NB + n][l];
+            v += red[2][i * NB + n][l];
+            v += red[3][i * NB + n][l];
+            if (Q8) v *= c_scale[i];
+            return v;
+          };
+#pragma unroll
+          for (int i = 0; i < OB; ++i) {
+            const f32x4 g = block(i);
+            if (GATED) {
+              const f32x4 u = block(OB + i);
+              const bf16x2 lo = {(__bf16)(silu_f32(g[0]) * u[0]), (__bf16)(silu_f32(g[1]) * u[1])};
+              const bf16x2 hi = {(__bf16)(silu_f32(g[2]) * u[2]), (__bf16)(silu_f32(g[3]) * u[3])};
+              uint2 pk;
+              pk.x = __builtin_bit_cast(uint32_t, lo);
+              pk.y = __builtin_bit_cast(uint32_t, hi);
+              *reinterpret_cast<uint2*>((uint16_t*)out + (size_t)p * F + r0 + 16 * i) = pk;
+            } else {
+              *reinterpret_cast<f32x4*>((float*)out + (size_t)p * H + r0 + 16 * i) = g;
             }
           }
         }
@@ -353,18 +350,19 @@ __global__ __launch_bounds__(256) void stream_kernel(
   WAIT_VMCNT(0);
 }
 
-template <bool GATED, bool Q8, int TR, int NS, int CK>
+template <bool GATED, bool Q8, int QNA, int TR, int NS, int CK>
 int launch_tr(const ExpertArgs& a, hipStream_t st) {
-  constexpr int NA = (GATED || Q8) ? 2 : 1, NB = (TR + 15) / 16;
+  constexpr int NA = Q8 ? QNA : (GATED ? 2 : 1), NB = (TR + 15) / 16;
+  constexpr int OB = GATED ? NA / 2 : NA;
   constexpr int lds = NS * (16 * NA * (Q8 ? 1 : 2) + TR * 2) * CK + 4 * NA * NB * 64 * 16;
   const int per_cu = (160 * 1024) / lds;
-  const int nwt = GATED ? a.F / 16 : a.H / (16 * NA);
+  const int nwt = GATED ? a.F / (16 * OB) : a.H / (16 * NA);
   const int slots = a.E < a.S ? a.E : a.S;
   int grid = cu_count() * (per_cu < 1 ? 1 : per_cu);
   if (grid > nwt * slots) grid = nwt * slots;
   const uint16_t* tok = GATED ? (const uint16_t*)a.x : (const uint16_t*)a.act;
   void* out = GATED ? a.act : (void*)a.yp;
-  stream_kernel<GATED, Q8, TR, NS, CK><<<grid, 256, 0, st>>>(
+  stream_kernel<GATED, Q8, QNA, TR, NS, CK><<<grid, 256, 0, st>>>(
       (const uint8_t*)a.experts, a.stride_elems, tok, a.perm, a.k, a.offsets, a.active, a.E,
       a.H, a.F, a.T, out);
   return hipGetLastError() == hipSuccess ? 0 : -1;
@@ -377,17 +375,33 @@ int launch_stream_q(const ExpertArgs& a, hipStream_t st) {
   // K allows it (bf16 layers have H % 256 == 0 and F % 128 == 0), else 128
   const int rows = a.rows_hint;
   const int K = GATED ? a.H : a.F;
+  if constexpr (Q8) {
+    // uint8 weights: a chunk holds half the bytes of a bf16 one, so small
+    // batches take items of 64 weight rows (the bytes of a bf16 item, and
+    // the token operand converted once for 4 row blocks); the down
+    // projection of single tokens keeps 16-row items so that every
+    // workgroup has one, with a deeper ring
+    if (K % 512 == 0) {
+      if (GATED) {
+        if (rows <= 8) return launch_tr<GATED, Q8, 4, 8, 3, 256>(a, st);
+        if (rows <= 16) return launch_tr<GATED, Q8, 4, 16, 2, 256>(a, st);
+      } else {
+        if (rows <= 2) return launch_tr<GATED, Q8, 1, 8, 4, 512>(a, st);
+        if (rows > 8 && rows <= 16) return launch_tr<GATED, Q8, 4, 16, 2, 256>(a, st);
+      }
+    }
+  }
   if (!GATED && K % 512 == 0 && rows <= 16) {  // down: 1 KB row runs
-    if (rows <= 8) return launch_tr<GATED, Q8, 8, 3, 512>(a, st);
-    return launch_tr<GATED, Q8, 16, 3, 512>(a, st);
+    if (rows <= 8) return launch_tr<GATED, Q8, 2, 8, 3, 512>(a, st);
+    return launch_tr<GATED, Q8, 2, 16, 3, 512>(a, st);
   }
   if (K % 256 == 0) {
-    if (rows <= 8) return launch_tr<GATED, Q8, 8, GATED ? 3 : 4, 256>(a, st);
-    if (rows <= 16) return launch_tr<GATED, Q8, 16, GATED ? 3 : 4, 256>(a, st);
-    return launch_tr<GATED, Q8, 32, GATED ? 2 : 3, 256>(a, st);
+    if (rows <= 8) return launch_tr<GATED, Q8, 2, 8, GATED ? 3 : 4, 256>(a, st);
+    if (rows <= 16) return launch_tr<GATED, Q8, 2, 16, GATED ? 3 : 4, 256>(a, st);
+    return launch_tr<GATED, Q8, 2, 32, GATED ? 2 : 3, 256>(a, st);
   }
-  if (rows <= 16) return launch_tr<GATED, Q8, 16, 4, 128>(a, st);
-  return launch_tr<GATED, Q8, 32, GATED ? 3 : 4, 128>(a, st);
+  if (rows <= 16) return launch_tr<GATED, Q8, 2, 16, 4, 128>(a, st);
+  return launch_tr<GATED, Q8, 2, 32, GATED ? 3 : 4, 128>(a, st);
 }
 
 template <bool GATED>

@@ -81,9 +81,15 @@ static orc_mat_t expert_matrix(const orc_layer_t* L, const unsigned char* blk, i
   return M;
 }
 
-static double mat_at(const orc_mat_t* M, size_t i) {
-  if (M->u8) return ((double)M->base[i] - M->zero) * M->scale;
-  return widen(M->base, M->dtype, i);
+/* sum_i x[i] * M[off + i], i ascending (one row of a weight matrix) */
+static double row_dot(const orc_mat_t* M, size_t off, const double* x, int32_t n) {
+  double s = 0.0;
+  if (M->u8) {
+    for (int32_t i = 0; i < n; ++i) s += x[i] * (((double)M->base[off + i] - M->zero) * M->scale);
+  } else {
+    for (int32_t i = 0; i < n; ++i) s += x[i] * widen(M->base, M->dtype, off + i);
+  }
+  return s;
 }
 
 /* Round a double to the nearest bfloat16 value (8 significant bits), ties to
@@ -223,16 +229,13 @@ int orc_expert_ffn(const orc_layer_t* L, int32_t e, const double* xrow, double* 
   double* a = (double*)malloc(sizeof(double) * (size_t)F);
   if (!a) return -1;
   for (int32_t f = 0; f < F; ++f) {
-    double g = 0.0, u = 0.0;
-    for (int32_t h = 0; h < H; ++h) g += xrow[h] * mat_at(&Wg, (size_t)f * H + h);
-    for (int32_t h = 0; h < H; ++h) u += xrow[h] * mat_at(&Wu, (size_t)f * H + h);
+    const double g = row_dot(&Wg, (size_t)f * H, xrow, H);
+    const double u = row_dot(&Wu, (size_t)f * H, xrow, H);
     double act = g / (1.0 + exp(-g)) * u;
     a[f] = (L->dtype == ORC_BF16) ? orc_bf16_round(act) : act;
   }
   for (int32_t h = 0; h < H; ++h) {
-    double s = 0.0;
-    for (int32_t f = 0; f < F; ++f) s += a[f] * mat_at(&Wd, (size_t)h * F + f);
-    yrow[h] = s;
+    yrow[h] = row_dot(&Wd, (size_t)h * F, a, F);
   }
   free(a);
   return 0;

@@ -104,6 +104,11 @@ U8_SMALL = [
     (256, 128, 64, 8, 60, 0),
     (512, 256, 8, 2, 40, moe.MOE_FLAG_GATE_RAW),
     (768, 256, 3, 1, 1100, 0),         # a large batch on the streaming kernels
+    # K % 512 == 0: the item sizes chosen per batch (1, 4, 16 rows per expert)
+    (512, 512, 8, 2, 1, 0),
+    (512, 512, 8, 2, 4, 0),
+    (512, 512, 8, 2, 16, 0),
+    (512, 512, 8, 2, 64, 0),
 ]
 
 
