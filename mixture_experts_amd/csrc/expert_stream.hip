@@ -26,12 +26,14 @@
 // uint8 experts (weights (q - zero) * scale, one map per matrix
 // [www.pnsm.cn/news/1892388.html sec. 3.1 and sec. 5.2]): the weight runs
 // hold one byte per weight, and an item is 16, 32 or 64 weight rows (QNA
-// blocks of 16) as the batch size suits.  In registers each group of 4 codes becomes
-// two fp16 pairs by a byte permute with 0x64 (fp16 1024 + q) and one packed
-// fp16 add of -(1024 + zero), exactly (q - zero); the bf16 token operand
-// becomes fp16 exactly (bf16 values in fp16's normal range are fp16
-// values), the MFMA is v_mfma_f32_16x16x32_f16, and the scale multiplies
-// the reduced sums once per output.
+// blocks of 16) as the batch size suits.  In registers each group of 4
+// codes becomes two fp16 pairs by a byte permute with 0x64 (fp16 1024 + q)
+// and one packed fp16 add of -(1024 + zero), exactly (q - zero).  The token
+// rows arrive in fp16: the layer input is copied to fp16 before the gate/up
+// kernel, whose epilogue stores the bf16-rounded activation as fp16 (bf16
+// values in fp16's normal range are fp16 values).  The MFMA is
+// v_mfma_f32_16x16x32_f16 and the scale multiplies the reduced sums once
+// per output.
 #include "common.h"
 #include "kernels.h"
 
@@ -66,21 +68,6 @@ __device__ __forceinline__ h8_t dequant8(uint2 w, h2_t bias) {
   return h8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
-// 8 bf16 -> 8 fp16 (exact for magnitudes in fp16's normal range)
-__device__ __forceinline__ h8_t bf16_to_h8(u32x4 v) {
-  const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-  h8_t r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const auto p = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(d[i] << 16),
-                                              __uint_as_float(d[i] & 0xFFFF0000u));
-    const h2_t h = __builtin_bit_cast(h2_t, p);
-    r[2 * i] = h.x;
-    r[2 * i + 1] = h.y;
-  }
-  return r;
-}
-
 // One LDS row run holds its chunks of 16 bytes with chunk c of run r at slot
 // c ^ (r % SPR) (SPR = chunks per run, at most 16), so the 16 lanes of an
 // MFMA operand read (16 runs, one chunk) spread over the bank groups.
@@ -110,7 +97,11 @@ __global__ __launch_bounds__(256) void stream_kernel(
                 "chunk width and token rows per pass");
   static_assert(NS >= 2 && NS <= 4, "ring depth");
   __shared__ __attribute__((aligned(16))) uint8_t ring[NS][STAGE];
-  __shared__ f32x4 red[4][NA * NB][64];
+  // the waves' partial sums at the end of a pass, [4 waves][NA*NB][64 lanes],
+  // in the ring stage just computed when it is large enough
+  constexpr int RED = 4 * NA * NB * 64;
+  constexpr bool RED_IN_RING = RED * 16 <= STAGE;
+  __shared__ f32x4 red_own[RED_IN_RING ? 1 : RED];
 
   const int K = GATED ? H : F;
   const int NWT = GATED ? F / (16 * OB) : H / WR;
@@ -284,7 +275,7 @@ __global__ __launch_bounds__(256) void stream_kernel(
         const int r = n * 16 + r16 < TR ? n * 16 + r16 : 0;
         const u32x4 v =
             *reinterpret_cast<const u32x4*>(sb + WR * RBW + r * RBT + run_slot<SPRT>(r, c) * 16);
-        if constexpr (Q8) b[n] = bf16_to_h8(v);
+        if constexpr (Q8) b[n] = __builtin_bit_cast(h8_t, v);  // fp16 token rows
         else b[n] = as_bf16x8(v);
       }
 #pragma unroll
@@ -292,15 +283,20 @@ __global__ __launch_bounds__(256) void stream_kernel(
 #pragma unroll
         for (int i = 0; i < NA; ++i) acc[i][n] = mfma16(a[i], b[n], acc[i][n]);
     }
+    const int cst = st;  // the stage just computed
     st = st == NS - 1 ? 0 : st + 1;
 
     if (++c_c == NC) {  // end of a token pass: reduce the 4 K partial sums
       c_c = 0;
+      f32x4* red = RED_IN_RING ? reinterpret_cast<f32x4*>(&ring[cst][0]) : red_own;
+      // every wave's reads of that stage are done (its next loads are issued
+      // only after the next chunk barrier, when the sums below have been read)
+      if (RED_IN_RING) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
       for (int i = 0; i < NA; ++i)
 #pragma unroll
         for (int n = 0; n < NB; ++n) {
-          red[wave][i * NB + n][lane] = acc[i][n];
+          red[(wave * NA * NB + i * NB + n) * 64 + lane] = acc[i][n];
           acc[i][n] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
       // LDS writes done, then the barrier; no wait on the loads in flight
@@ -315,10 +311,12 @@ __global__ __launch_bounds__(256) void stream_kernel(
           const int p = c_pbeg + t;
           const int r0 = c_wt * 16 * OB + 4 * (l >> 4);
           auto block = [&](int i) {  // the waves' partials of row block i, in wave order
-            f32x4 v = red[0][i * NB + n][l];
-            v += red[1][i * NB + n][l];
-            v += red[2][i * NB + n][l];
-            v += red[3][i * NB + n][l];
+            constexpr int WS = NA * NB * 64;  // one wave's partials
+            const int o = (i * NB + n) * 64 + l;
+            f32x4 v = red[o];
+            v += red[WS + o];
+            v += red[2 * WS + o];
+            v += red[3 * WS + o];
             if (Q8) v *= c_scale[i];
             return v;
           };
@@ -332,6 +330,12 @@ __global__ __launch_bounds__(256) void stream_kernel(
               uint2 pk;
               pk.x = __builtin_bit_cast(uint32_t, lo);
               pk.y = __builtin_bit_cast(uint32_t, hi);
+              if (Q8) {  // the bf16-rounded activation, stored as fp16 for the down kernel
+                pk.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(
+                    __uint_as_float(pk.x << 16), __uint_as_float(pk.x & 0xFFFF0000u)));
+                pk.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(
+                    __uint_as_float(pk.y << 16), __uint_as_float(pk.y & 0xFFFF0000u)));
+              }
               *reinterpret_cast<uint2*>((uint16_t*)out + (size_t)p * F + r0 + 16 * i) = pk;
             } else {
               *reinterpret_cast<f32x4*>((float*)out + (size_t)p * H + r0 + 16 * i) = g;
@@ -354,7 +358,8 @@ template <bool GATED, bool Q8, int QNA, int TR, int NS, int CK>
 int launch_tr(const ExpertArgs& a, hipStream_t st) {
   constexpr int NA = Q8 ? QNA : (GATED ? 2 : 1), NB = (TR + 15) / 16;
   constexpr int OB = GATED ? NA / 2 : NA;
-  constexpr int lds = NS * (16 * NA * (Q8 ? 1 : 2) + TR * 2) * CK + 4 * NA * NB * 64 * 16;
+  constexpr int stage = (16 * NA * (Q8 ? 1 : 2) + TR * 2) * CK, red = 4 * NA * NB * 64 * 16;
+  constexpr int lds = NS * stage + (red <= stage ? 16 : red);
   const int per_cu = (160 * 1024) / lds;
   const int nwt = GATED ? a.F / (16 * OB) : a.H / (16 * NA);
   const int slots = a.E < a.S ? a.E : a.S;
@@ -376,9 +381,8 @@ int launch_stream_q(const ExpertArgs& a, hipStream_t st) {
   const int rows = a.rows_hint;
   const int K = GATED ? a.H : a.F;
   if constexpr (Q8) {
-    // uint8 weights: a chunk holds half the bytes of a bf16 one, so small
-    // batches take items of 64 weight rows (the bytes of a bf16 item, and
-    // the token operand converted once for 4 row blocks); the down
+    // uint8 weights: a chunk holds half the bytes of a bf16 one, so batches
+    // take items of 64 weight rows (the bytes of a bf16 item); the down
     // projection of single tokens keeps 16-row items so that every
     // workgroup has one, with a deeper ring
     if (K % 512 == 0) {
@@ -389,6 +393,7 @@ int launch_stream_q(const ExpertArgs& a, hipStream_t st) {
         if (rows <= 2) return launch_tr<GATED, Q8, 1, 8, 4, 512>(a, st);
         if (rows > 8 && rows <= 16) return launch_tr<GATED, Q8, 4, 16, 2, 256>(a, st);
       }
+      if (rows > 16) return launch_tr<GATED, Q8, 4, 32, 2, 256>(a, st);
     }
   }
   if (!GATED && K % 512 == 0 && rows <= 16) {  // down: 1 KB row runs

@@ -48,7 +48,8 @@ struct ExpertArgs {
   const void* x;            // [T][H] layer input (bf16 or fp32)
   const void* experts;      // expert blocks
   uint64_t stride_elems;    // expert stride in elements (bytes for uint8 experts)
-  int u8;                   // experts are uint8 codes + parameter blocks
+  int u8;                   // experts are uint8 codes + parameter blocks; then x
+                            // holds fp16 values and act is stored in fp16
   int T, H, F, E, k, S;
   int rows_hint;            // rows per expert one streaming pass should cover
   const int32_t* perm;      // [S]
@@ -84,6 +85,10 @@ int launch_stream_down(const ExpertArgs& a, hipStream_t st);
 // fp32 expert FFN (plain FMA)
 int launch_f32_gate_up(const ExpertArgs& a, hipStream_t st);
 int launch_f32_down(const ExpertArgs& a, hipStream_t st);
+
+// fp16 copy of n bf16 values (exact in fp16's normal range; round toward
+// zero beyond it and below it)
+int launch_to_f16(const uint16_t* src, size_t n, uint16_t* dst, hipStream_t st);
 
 // uint8 expert weights from bf16 ones (parameter blocks of dst as scratch)
 int launch_quantize_u8(const void* src, uint64_t src_stride, int E, int H, int F, void* dst,

@@ -22,6 +22,7 @@ struct moe_layer {
   size_t ws_bytes;
   // workspace pieces
   uint16_t* xt;       // [maxT][H] bf16 branch input (RESIDUAL_PRENORM)
+  uint16_t* x16;      // [maxT][H] fp16 copy of the expert input (uint8 experts)
   int32_t* idx;       // [S]
   float* w;           // [S]
   float* part;        // partial router logits
@@ -105,6 +106,8 @@ void carve(moe_layer* L, Arena& A) {
   const size_t nrun = (S + DISPATCH_RUN - 1) / DISPATCH_RUN;
   L->xt = (uint16_t*)arena_alloc(A, (d.flags & MOE_FLAG_RESIDUAL_PRENORM)
                                         ? (size_t)d.max_tokens * d.hidden * 2 : 0);
+  L->x16 = (uint16_t*)arena_alloc(A, d.expert_format == MOE_EXPERT_U8
+                                         ? (size_t)d.max_tokens * d.hidden * 2 : 0);
   L->idx = (int32_t*)arena_alloc(A, S * 4);
   L->w = (float*)arena_alloc(A, S * 4);
   size_t part = 0;
@@ -333,6 +336,10 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
     ea.rows_hint = T < hint ? T : hint;
   }
   if (!mark(MOE_STAGE_GATE_UP)) return MOE_ERR_DEVICE;
+  if (ea.u8) {  // the uint8 kernels take fp16 token operands
+    if (launch_to_f16((const uint16_t*)xin, (size_t)T * d.hidden, L->x16, st)) return MOE_ERR_DEVICE;
+    ea.x = L->x16;
+  }
   int r1 = f32 ? launch_f32_gate_up(ea, st)
                : stream_path ? launch_stream_gate_up(ea, st) : launch_grouped_gate_up(ea, st);
   if (r1 || !mark(MOE_STAGE_DOWN)) return MOE_ERR_DEVICE;

@@ -1,6 +1,7 @@
 // quantize.hip -- conversion of bf16 expert weights to uint8 codes with one
 // affine map per weight matrix (a one-time step before MOE_EXPERT_U8 layers
-// run, not part of the forward pass).
+// run, not part of the forward pass); and the fp16 copy of a uint8 layer's
+// input that its expert kernels read.
 //
 // The pages quantise each expert matrix after training from its minimum and
 // maximum into 255 levels and read it back as (q - zero point) * scale
@@ -130,7 +131,35 @@ __global__ __launch_bounds__(256) void q_codes(const uint8_t* src, uint64_t sstr
   }
 }
 
+// 8 bf16 -> 8 fp16 per thread (round toward zero: exact where bf16 values
+// are fp16 values)
+__global__ __launch_bounds__(256) void to_f16_kernel(const uint16_t* __restrict__ src, size_t n,
+                                                     uint16_t* __restrict__ dst) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i + 8 <= n) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src + i);
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(d[j] << 16),
+                                                                     __uint_as_float(d[j] & 0xFFFF0000u)));
+    *reinterpret_cast<u32x4*>(dst + i) = u32x4{o[0], o[1], o[2], o[3]};
+  } else {
+    for (size_t j = i; j < n; ++j) {
+      const auto h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float((uint32_t)src[j] << 16), 0.0f);
+      dst[j] = (uint16_t)__builtin_bit_cast(uint32_t, h);
+    }
+  }
+}
+
 }  // namespace
+
+int launch_to_f16(const uint16_t* src, size_t n, uint16_t* dst, hipStream_t st) {
+  const size_t threads = (n + 7) / 8;
+  to_f16_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(src, n, dst);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
 
 int launch_quantize_u8(const void* src, uint64_t src_stride, int E, int H, int F, void* dst,
                        uint64_t dst_stride, hipStream_t st) {
