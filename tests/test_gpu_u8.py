@@ -62,11 +62,12 @@ def test_quantizer_bit_exact_mixtral_expert():
 class U8Case:
     """A uint8-expert layer on the GPU and the oracle's layer on the same codes."""
 
-    def __init__(self, shape, max_tokens, flags=0):
+    def __init__(self, shape, max_tokens, flags=0, layer=0):
         self.shape = shape
-        self.router, self.bias = gen.gen_router(shape), gen.gen_bias(shape)
+        self.router, self.bias = gen.gen_router(shape, layer), gen.gen_bias(shape)
         d_src = torch.empty(shape.E * shape.stride, dtype=torch.uint8, device="cuda")
-        gen.experts_device(shape, d_src.data_ptr(), stream=torch.cuda.current_stream().cuda_stream)
+        gen.experts_device(shape, d_src.data_ptr(), layer=layer,
+                           stream=torch.cuda.current_stream().cuda_stream)
         self.d_u8, self.st = quantize_on_gpu(shape, d_src)
         del d_src
         self.u8 = self.d_u8.cpu().numpy()
@@ -146,6 +147,29 @@ def test_u8_mixtral_decode(T, nsample):
     st = check_rows(c, x, toks, y[toks], idx[toks])
     _log("  ", st)
     c.close()
+
+
+def test_u8_residual_stack_teacher_forced():
+    """Three stacked uint8 layers in place (RESIDUAL_PRENORM: the normalised
+    bf16 branch input is what the uint8 kernels read in fp16), each checked
+    against the oracle fed with the GPU's residual stream at that layer."""
+    shape = gen.LayerShape("u8stack", H=512, F=512, E=8, k=2, dtype="bf16")
+    T = 24
+    cases = [U8Case(shape, T, moe.MOE_FLAG_RESIDUAL_PRENORM, layer=l) for l in range(3)]
+    h = torch.from_numpy(gen.normal(0, 0, gen.T_X, T * shape.H, 1.0, "f32").reshape(T, shape.H)).cuda()
+    for c in cases:
+        h_in = h.cpu().numpy()
+        c.layer.forward(h, h)
+        torch.cuda.synchronize()
+        h_out = h.cpu().numpy()
+        xt = oracle.prenorm_bf16(h_in)
+        r = c.layer.route(torch.from_numpy(h_in).cuda(), T)
+        torch.cuda.synchronize()
+        branch = h_out.astype(np.float64) - h_in.astype(np.float64)
+        st = check_rows(c, xt, np.arange(T), branch, r["idx"].cpu().numpy())
+        _log("  ", st)
+    for c in cases:
+        c.close()
 
 
 def test_u8_close_to_the_bf16_layer():
