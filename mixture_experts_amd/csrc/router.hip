@@ -453,15 +453,24 @@ __global__ __launch_bounds__(256) void route_small_kernel(
 // rows), wave w takes the hidden slice [w H/16, (w+1) H/16) for all tokens
 // (tokens as the A operand, read from global memory), the 16 partial logit
 // tiles are added in wave order (+ bias), then top-k and the dispatch.
+// MULTI: one workgroup per 16 tokens (the token rows of a larger batch are
+// then read through several CUs); each routes its tokens, and the last to
+// finish (a device-scope atomic after a release fence, as in the split-H
+// kernel) reads every token's experts back and dispatches them all, then
+// resets the counter for the next launch.
 constexpr int R1_HMAX = 4096;
 constexpr int R1_LDW = R1_HMAX + 8;  // padded router row (bf16)
-template <int MB, int EV>
+template <int MB, int EV, bool MULTI>
 __global__ __launch_bounds__(1024) void route_one_kernel(
-    const uint16_t* __restrict__ x, int T, int H, int E, int k, int raw,
+    const uint16_t* __restrict__ x, int T_all, int H, int E, int k, int raw,
     const uint16_t* __restrict__ wr, const float* __restrict__ bias, int tile_rows, int cap,
-    int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off,
+    int32_t* __restrict__ counter, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off,
     int32_t* __restrict__ active, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  static_assert(!MULTI || MB == 1, "one token block per workgroup");
+  const int tok0 = MULTI ? (int)blockIdx.x * 16 : 0;  // this workgroup's first token
+  const int T = MULTI ? min(16, T_all - tok0) : T_all;
+  x += (size_t)tok0 * H;
   // the staged router, later the 16 partial logit tiles [16][RT_TOK][17]
   __shared__ __attribute__((aligned(16))) uint16_t wt[16 * R1_LDW];
   __shared__ float lg[RT_TOK * 17];
@@ -567,10 +576,25 @@ __global__ __launch_bounds__(1024) void route_one_kernel(
     lg[t * 17 + e] = s;
   }
   __syncthreads();
-  topk_rows16(lg, 17, 0, T, E, k, raw, idx_out, w_out, 16, idx_l, RT_TOK);
-  __syncthreads();
-  dispatch_small(idx_l, T * k, E, tile_rows, cap, cnt, off_l, rank_l, counts, offsets, tile_off,
-                 active, perm, inv);
+  if (MULTI) {
+    topk_rows16(lg, 17, 0, T, E, k, raw, idx_out + (size_t)tok0 * k, w_out + (size_t)tok0 * k,
+                16, nullptr, RT_TOK);
+    __shared__ int s_last;
+    __threadfence();  // release this block's experts and weights
+    __syncthreads();
+    if (tid == 0) s_last = (atomicAdd(counter, 1) == (int)gridDim.x - 1);
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();  // acquire every block's
+    for (int i = tid; i < T_all * k; i += 1024) idx_l[i] = idx_out[i];
+    __syncthreads();
+    if (tid == 0) *counter = 0;  // ready for the next launch
+  } else {
+    topk_rows16(lg, 17, 0, T, E, k, raw, idx_out, w_out, 16, idx_l, RT_TOK);
+    __syncthreads();
+  }
+  dispatch_small(idx_l, T_all * k, E, tile_rows, cap, cnt, off_l, rank_l, counts, offsets,
+                 tile_off, active, perm, inv);
 }
 
 }  // namespace
@@ -626,13 +650,13 @@ int launch_route_small(const RouterArgs& a, const DispatchArgs& d, int32_t* coun
   if (a.E <= 16 && a.H <= R1_HMAX && a.H % 512 == 0 && a.T <= RT_TOK) {
     auto* xx = (const uint16_t*)a.x;
     auto* ww = (const uint16_t*)a.wr;
-#define R1_ARGS xx, a.T, a.H, a.E, a.k, a.raw_gate, ww, a.bias, d.tile_rows, d.capacity, a.idx, a.w, d.counts, \
-                d.offsets, d.tile_off, d.active, d.perm, d.inv
+#define R1_ARGS xx, a.T, a.H, a.E, a.k, a.raw_gate, ww, a.bias, d.tile_rows, d.capacity, counter, a.idx, \
+                a.w, d.counts, d.offsets, d.tile_off, d.active, d.perm, d.inv
     const int mb = (a.T + 15) / 16;
-#define R1_MB(EV)                                                         \
-    if (mb <= 1) route_one_kernel<1, EV><<<1, 1024, 0, st>>>(R1_ARGS);    \
-    else if (mb <= 2) route_one_kernel<2, EV><<<1, 1024, 0, st>>>(R1_ARGS); \
-    else route_one_kernel<4, EV><<<1, 1024, 0, st>>>(R1_ARGS);
+    // one workgroup up to 16 tokens, one per 16 tokens beyond
+#define R1_MB(EV)                                                                \
+    if (mb <= 1) route_one_kernel<1, EV, false><<<1, 1024, 0, st>>>(R1_ARGS);    \
+    else route_one_kernel<1, EV, true><<<mb, 1024, 0, st>>>(R1_ARGS);
     if (a.E == 8) { R1_MB(8) }
     else { R1_MB(0) }
 #undef R1_MB
