@@ -376,8 +376,9 @@ int launch_tr(const ExpertArgs& a, hipStream_t st) {
 template <bool GATED, bool Q8>
 int launch_stream_q(const ExpertArgs& a, hipStream_t st) {
   // token rows per pass (experts with more rows take several passes) and the
-  // chunk width: 512 for the down projection of small batches, else 256 when
-  // K allows it (bf16 layers have H % 256 == 0 and F % 128 == 0), else 128
+  // chunk width: 512 for batches of up to 8 rows per expert (16 for the down
+  // projection), else 256 when K allows it (bf16 layers have H % 256 == 0
+  // and F % 128 == 0), else 128
   const int rows = a.rows_hint;
   const int K = GATED ? a.H : a.F;
   if constexpr (Q8) {
@@ -396,8 +397,10 @@ int launch_stream_q(const ExpertArgs& a, hipStream_t st) {
       if (rows > 16) return launch_tr<GATED, Q8, 4, 32, 2, 256>(a, st);
     }
   }
+  if (GATED && K % 512 == 0 && rows <= 8)  // 1 KB row runs, one deep ring per CU
+    return launch_tr<GATED, Q8, 2, 8, 3, 512>(a, st);
   if (!GATED && K % 512 == 0 && rows <= 16) {  // down: 1 KB row runs
-    if (rows <= 8) return launch_tr<GATED, Q8, 2, 8, 3, 512>(a, st);
+    if (rows <= 8) return launch_tr<GATED, Q8, 2, 8, Q8 ? 3 : 4, 512>(a, st);
     return launch_tr<GATED, Q8, 2, 16, 3, 512>(a, st);
   }
   if (K % 256 == 0) {
