@@ -69,10 +69,16 @@ __global__ __launch_bounds__(MOE_MAX_EXPERTS) void dispatch_scan_kernel(
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
-    for (int r = 0; r < nrun; ++r) {
-      const int h = hist[(size_t)r * E + e];
-      base[(size_t)r * E + e] = run;
-      run += h;
+    // runs in groups of 16 whose loads are all in flight together
+    for (int r0 = 0; r0 < nrun; r0 += 16) {
+      int h[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) h[j] = r0 + j < nrun ? hist[(size_t)(r0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (r0 + j < nrun) base[(size_t)(r0 + j) * E + e] = run;
+        run += h[j];
+      }
     }
     if (cap > 0 && run > cap) run = cap;
     counts[e] = run;

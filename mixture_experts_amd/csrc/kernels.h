@@ -25,6 +25,7 @@ struct RouterArgs {
   int32_t* idx;           // [T][k]
   float* w;               // [T][k]
   float* part;            // [router_splits(T, H)][T][E] partial logits (bf16 layers)
+  uint16_t* wrt;          // [E][H] workspace for the transposed router (bf16 layers)
   int raw_gate;           // 1: gate weights = the selected logits (no softmax)
 };
 

@@ -26,6 +26,7 @@ struct moe_layer {
   int32_t* idx;       // [S]
   float* w;           // [S]
   float* part;        // partial router logits
+  uint16_t* wrt;      // [E][H] transposed router (bf16 layers)
   int32_t* counts;    // [E]
   int32_t* offsets;   // [E+1]
   int32_t* tile_off;  // [E+1]
@@ -119,6 +120,7 @@ void carve(moe_layer* L, Arena& A) {
     }
   }
   L->part = (float*)arena_alloc(A, part);
+  L->wrt = (uint16_t*)arena_alloc(A, d.dtype == MOE_BF16 ? E * (size_t)d.hidden * 2 : 0);
   L->counts = (int32_t*)arena_alloc(A, E * 4);
   L->offsets = (int32_t*)arena_alloc(A, (E + 1) * 4);
   L->tile_off = (int32_t*)arena_alloc(A, (E + 1) * 4);
@@ -172,7 +174,7 @@ int run_route(moe_layer* L, const void* x_route, int T, const float* logits_in,
               int tile_rows, hipStream_t st) {
   const moe_layer_desc& d = L->d;
   RouterArgs ra{x_route, T, d.hidden, d.num_experts, d.top_k, d.dtype == MOE_F32 ? 1 : 0,
-                d.router_w, d.router_b, logits_in, L->idx, L->w, L->part,
+                d.router_w, d.router_b, logits_in, L->idx, L->w, L->part, L->wrt,
                 (d.flags & MOE_FLAG_GATE_RAW) ? 1 : 0};
   DispatchArgs da{L->idx, T * d.top_k, d.num_experts, tile_rows, L->hist, L->rank, L->base,
                   L->counts, L->offsets, L->tile_off, L->active, L->perm, L->inv,
@@ -299,7 +301,7 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
   {
     const moe_layer_desc& dd = L->d;
     RouterArgs ra{xin, T, dd.hidden, dd.num_experts, dd.top_k, f32 ? 1 : 0, dd.router_w,
-                  dd.router_b, nullptr, L->idx, L->w, L->part,
+                  dd.router_b, nullptr, L->idx, L->w, L->part, L->wrt,
                   (dd.flags & MOE_FLAG_GATE_RAW) ? 1 : 0};
     DispatchArgs da{L->idx, S, dd.num_experts, GG_BT, L->hist, L->rank, L->base, L->counts,
                     L->offsets, L->tile_off, L->active, L->perm, L->inv, dd.expert_capacity};

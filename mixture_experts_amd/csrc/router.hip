@@ -218,52 +218,85 @@ __device__ void dispatch_small(const int32_t* idx_lds, int S, int E, int tile_ro
 // 32 KB); each chunk of the router is staged in LDS transposed ([e][h]) so
 // that the MFMA B operand is a 16-byte read, and all token loads of a chunk
 // are issued before the staging, so their latency overlaps it.
-constexpr int RP_MAXCH = 512;  // largest staged chunk (hidden units)
+// Wr [H][E] -> WrT [E][H] (64 x 64 tiles through LDS), so that the router
+// operand of the logits GEMM is K-contiguous like the tokens.  Rows move as
+// 16-byte runs of 8 values (E a multiple of 8; else element by element).
+__global__ __launch_bounds__(256) void router_transpose_kernel(const uint16_t* __restrict__ wr,
+                                                               int H, int E,
+                                                               uint16_t* __restrict__ wrt) {
+  constexpr int P = 72;  // row pitch (elements): 16-byte aligned rows, spread banks
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * P];  // [h][e]
+  const int h0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  if (E % 8 == 0) {
+#pragma unroll
+    for (int i = threadIdx.x; i < 64 * 8; i += 256) {
+      const int r = i >> 3, c = (i & 7) * 8;  // hidden unit, first of 8 experts
+      u32x4 v{0u, 0u, 0u, 0u};
+      if (h0 + r < H && e0 + c < E) v = ldg16(wr + (size_t)(h0 + r) * E + e0 + c);
+      *reinterpret_cast<u32x4*>(tile + r * P + c) = v;
+    }
+  } else {
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+      const int r = i >> 6, c = i & 63;
+      tile[r * P + c] = (h0 + r < H && e0 + c < E) ? wr[(size_t)(h0 + r) * E + e0 + c] : (uint16_t)0;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
+    const int r = i >> 3, c = (i & 7) * 8;  // expert, first of 8 hidden units
+    if (e0 + r >= E || h0 + c >= H) continue;  // H is a multiple of 8
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = (uint32_t)tile[(c + 2 * q) * P + r] | ((uint32_t)tile[(c + 2 * q + 1) * P + r] << 16);
+    *reinterpret_cast<u32x4*>(wrt + (size_t)(e0 + r) * H + h0 + c) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// Partial logits of one hidden slice for 64 tokens: tokens as the A operand
+// and the transposed router as the B operand of v_mfma_f32_16x16x32_bf16,
+// both read straight from global memory (the router is L2-resident).
 template <int NT>
 __global__ __launch_bounds__(256) void router_partial_kernel(
-    const uint16_t* __restrict__ x, int T, int H, int E, const uint16_t* __restrict__ wr,
+    const uint16_t* __restrict__ x, int T, int H, int E, const uint16_t* __restrict__ wrt,
     int hslice, float* __restrict__ part) {
-  constexpr int EP = NT * 16;
-  constexpr int MAXCH = EP <= 32 ? RP_MAXCH : RT_HC;
-  constexpr int LDW = MAXCH + RT_PAD;
-  __shared__ __attribute__((aligned(16))) uint16_t wt[EP * LDW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile0 = blockIdx.x * RT_TOK;
   const int split = blockIdx.y;
   const int hb = split * hslice;
-  const int ch = (hslice % MAXCH == 0) ? MAXCH : RT_HC;  // hslice is a multiple of RT_HC
   f32x4 acc[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int my_tok = tile0 + wave * 16 + (lane & 15);
   const bool tok_ok = my_tok < T;
-  const uint16_t* xrow = x + (size_t)(tok_ok ? my_tok : 0) * H;
   const int kq = (lane >> 4) * 8;
-  for (int h0 = hb; h0 < hb + hslice; h0 += ch) {
-    u32x4 av[MAXCH / 32];
+  const uint16_t* xrow = x + (size_t)(tok_ok ? my_tok : 0) * H + hb + kq;
+  const uint16_t* wrow[NT];  // this lane's expert row of WrT per column block
 #pragma unroll
-    for (int s = 0; s < MAXCH / 32; ++s)
-      if (s * 32 < ch) av[s] = tok_ok ? ldg16(xrow + h0 + s * 32 + kq) : u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
-#pragma unroll 8
-    for (int i = tid; i < ch * EP; i += 256) {
-      const int r = i / EP, e = i % EP;
-      wt[e * LDW + r] = (e < E) ? wr[(size_t)(h0 + r) * E + e] : (uint16_t)0;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < MAXCH / 32; ++s) {
-      if (s * 32 >= ch) break;
-      const bf16x8 a = as_bf16x8(av[s]);
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const uint16_t* bp = wt + (n * 16 + (lane & 15)) * LDW + s * 32 + kq;
-        const bf16x8 b = as_bf16x8(*reinterpret_cast<const u32x4*>(bp));
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[n], 0, 0, 0);
-      }
-    }
+  for (int n = 0; n < NT; ++n) {
+    const int e = n * 16 + (lane & 15);
+    wrow[n] = wrt + (size_t)(e < E ? e : 0) * H + hb + kq;
   }
-  // C layout: lane holds column (expert) lane%16, rows 4*(lane/16) + j
+  for (int h = 0; h < hslice; h += 4 * 32) {  // hslice is a multiple of RT_HC (64)
+    u32x4 av[4], bv[4][NT];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      if (h + s * 32 < hslice) {
+        av[s] = tok_ok ? ldg16(xrow + h + s * 32) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int n = 0; n < NT; ++n) bv[s][n] = ldg16(wrow[n] + h + s * 32);
+      }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      if (h + s * 32 < hslice)
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[s]), as_bf16x8(bv[s][n]),
+                                                           acc[n], 0, 0, 0);
+  }
+  // C layout: lane holds column (expert) lane%16, rows 4*(lane/16) + j;
+  // experts beyond E (rows of WrT clamped to 0) are not stored
   float* out = part + (size_t)split * T * E;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
@@ -629,17 +662,19 @@ int launch_router(const RouterArgs& a, hipStream_t st) {
   const dim3 g2(grid, ns);
   const int nt = (a.E + 15) / 16;
   auto* xx = (const uint16_t*)a.x;
-  auto* ww = (const uint16_t*)a.wr;
+  const dim3 gt((a.H + 63) / 64, (a.E + 63) / 64);
+  router_transpose_kernel<<<gt, 256, 0, st>>>((const uint16_t*)a.wr, a.H, a.E, a.wrt);
+  const uint16_t* wt = a.wrt;
   if (nt <= 1)
-    router_partial_kernel<1><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, ww, hs, a.part);
+    router_partial_kernel<1><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, wt, hs, a.part);
   else if (nt <= 2)
-    router_partial_kernel<2><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, ww, hs, a.part);
+    router_partial_kernel<2><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, wt, hs, a.part);
   else if (nt <= 4)
-    router_partial_kernel<4><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, ww, hs, a.part);
+    router_partial_kernel<4><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, wt, hs, a.part);
   else if (nt <= 8)
-    router_partial_kernel<8><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, ww, hs, a.part);
+    router_partial_kernel<8><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, wt, hs, a.part);
   else
-    router_partial_kernel<16><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, ww, hs, a.part);
+    router_partial_kernel<16><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, wt, hs, a.part);
   router_topk_kernel<<<kgrid, 256, 0, st>>>(a.part, ns, a.T, a.E, a.k, a.raw_gate, a.bias, a.idx,
                                             a.w);
   return hipGetLastError() == hipSuccess ? 0 : -1;
