@@ -88,7 +88,7 @@ typedef struct {
 enum {
   /* Stacked-layer mode: x is the fp32 residual stream h [T][H]; the branch
    * input is bf16(h[t] / sqrt(mean_h h[t]^2 + 1e-6)) and y = h + MoE(.).
-   * y may alias x.  bf16 layers only. */
+   * y may alias x.  bf16 layers with H <= 16384 only. */
   MOE_FLAG_RESIDUAL_PRENORM = 1u << 0,
   /* Kernel path for the expert FFN of bf16 layers.  By default a call with
    * T*k <= 32*E (few rows per expert: decode batches, many small experts)
@@ -103,7 +103,14 @@ enum {
    * Without it the weights are the softmax over the k selected logits.
    * (Soft routing, every expert weighted, is top_k == num_experts with the
    * softmax gate.) */
-  MOE_FLAG_GATE_RAW = 1u << 3
+  MOE_FLAG_GATE_RAW = 1u << 3,
+  /* On the streaming path the down projection folds step 5 in when one
+   * workgroup can own every expert's rows of a hidden slice (H/16 slices at
+   * least as many as compute units, T*k <= 256): it sums the k expert rows of
+   * each token in the same fixed slot order with the same fp32 operations as
+   * the separate combine, so the results are bit-identical.  This flag keeps
+   * the combine a kernel of its own (for profiling and testing). */
+  MOE_FLAG_COMBINE_SEPARATE = 1u << 4
 };
 
 typedef struct {

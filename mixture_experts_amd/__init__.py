@@ -23,6 +23,7 @@ MOE_FLAG_RESIDUAL_PRENORM = 1 << 0
 MOE_FLAG_PATH_GROUPED = 1 << 1
 MOE_FLAG_PATH_STREAM = 1 << 2
 MOE_FLAG_GATE_RAW = 1 << 3
+MOE_FLAG_COMBINE_SEPARATE = 1 << 4
 MOE_EXPERT_DTYPE = 0
 MOE_EXPERT_U8 = 1
 U8_PARAMS_BYTES = 64

@@ -74,12 +74,17 @@ __device__ __forceinline__ h8_t dequant8(uint2 w, h2_t bias) {
 template <int SPR>
 __device__ __forceinline__ int run_slot(int r, int c) { return c ^ (r & ((SPR < 16 ? SPR : 16) - 1)); }
 
-template <bool GATED, bool Q8, int QNA, int TR, int NS, int CK>
+// FC (down projection only): the items of one 16-row hidden slice, every
+// non-empty expert's, run back to back in one workgroup, which keeps their
+// outputs in LDS and then writes y for that slice (step 5, the combine's
+// arithmetic in the combine's order) instead of storing per-row outputs.
+template <bool GATED, bool Q8, int QNA, int TR, int NS, int CK, bool FC = false>
 __global__ __launch_bounds__(256) void stream_kernel(
     const uint8_t* __restrict__ experts, uint64_t stride_elems,
     const uint16_t* __restrict__ tok, const int32_t* __restrict__ perm, int k_top,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ active, int E, int H,
-    int F, int T, void* __restrict__ out) {
+    int F, int T, void* __restrict__ out, const float* __restrict__ cw,
+    const int32_t* __restrict__ cinv, const float* cres, float* cy) {
   constexpr int WE = Q8 ? 1 : 2;                // bytes per weight
   constexpr int NA = Q8 ? QNA : (GATED ? 2 : 1);  // weight row blocks of 16 per item
   constexpr int WR = 16 * NA;                   // weight rows per item
@@ -102,12 +107,32 @@ __global__ __launch_bounds__(256) void stream_kernel(
   constexpr int RED = 4 * NA * NB * 64;
   constexpr bool RED_IN_RING = RED * 16 <= STAGE;
   __shared__ f32x4 red_own[RED_IN_RING ? 1 : RED];
+  static_assert(!FC || (!GATED && WR == 16), "combine folded into 16-row down items");
+  // FC: the down outputs of the slice, [pair t*k + j][16 rows], pairs < 256
+  __shared__ f32x4 comb[FC ? 256 * 16 / 4 : 1];
 
   const int K = GATED ? H : F;
   const int NWT = GATED ? F / (16 * OB) : H / WR;
   const int NC = K / CK;
-  const int n_items = active[E] * NWT;
+  const int n_act = active[E];
+  const int n_items = n_act * NWT;
   const int G = gridDim.x;
+  // item j of this workgroup: (expert slot, weight row block); without FC
+  // items are numbered slot-major and dealt round-robin, with FC the
+  // workgroup takes hidden slices b, b + G, ... with every slot of each
+  auto item_of = [&](int j, int& slot, int& wt) -> bool {
+    if (FC) {
+      if (n_act <= 0) return false;
+      const int q = j / n_act;
+      slot = j - q * n_act;
+      wt = blockIdx.x + q * G;
+      return wt < NWT;
+    }
+    const int item = blockIdx.x + j * G;
+    slot = item / NWT;
+    wt = item - slot * NWT;
+    return item < n_items;
+  };
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -117,10 +142,9 @@ __global__ __launch_bounds__(256) void stream_kernel(
   const uint8_t* wsrc[IW];
   const uint16_t* tsrc[IT];
   auto l_item = [&]() {  // sets l_ok, l_npass and the weight sources for item l_j
-    const int item = blockIdx.x + l_j * G;
-    l_ok = item < n_items;
+    int slot, wt;
+    l_ok = item_of(l_j, slot, wt);
     if (!l_ok) return;
-    const int slot = item / NWT, wt = item - slot * NWT;
     const int e = active[slot];
     const int n_e = offsets[e + 1] - offsets[e];
     l_npass = (n_e + TR - 1) / TR;
@@ -141,8 +165,9 @@ __global__ __launch_bounds__(256) void stream_kernel(
   // no vector load the compiler would have to wait for joins the loads in
   // flight.
   auto l_pass_rows = [&]() {
-    const int item = blockIdx.x + l_j * G;
-    const int e = active[item / NWT];
+    int slot, wt;
+    (void)item_of(l_j, slot, wt);
+    const int e = active[slot];
     const int p_beg = offsets[e], n_e = offsets[e + 1] - p_beg;
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
@@ -196,11 +221,9 @@ __global__ __launch_bounds__(256) void stream_kernel(
   float c_scale[NA];  // uint8 experts: scale of each weight row block
   h2_t c_bias[NA];    // and -(1024 + zero point) for the dequantisation
   auto c_item = [&]() {
-    const int item = blockIdx.x + c_j * G;
-    c_ok = item < n_items;
+    int slot;
+    c_ok = item_of(c_j, slot, c_wt);
     if (!c_ok) return;
-    const int slot = item / NWT;
-    c_wt = item - slot * NWT;
     const int e = active[slot];
     c_pbeg = offsets[e];
     c_ne = offsets[e + 1] - c_pbeg;
@@ -217,6 +240,14 @@ __global__ __launch_bounds__(256) void stream_kernel(
     }
   };
 
+  if (FC && n_act <= 0) {  // no pair reached an expert: y = resid (+ nothing)
+    for (int wt = blockIdx.x; wt < NWT; wt += G)
+      for (int u = threadIdx.x; u < T * 16; u += 256) {
+        const size_t o = (size_t)(u >> 4) * H + wt * 16 + (u & 15);
+        cy[o] = cres ? cres[o] + 0.0f : 0.0f;
+      }
+    return;
+  }
   l_item();
   if (l_ok) l_pass_rows();
   c_item();
@@ -337,6 +368,8 @@ __global__ __launch_bounds__(256) void stream_kernel(
                     __uint_as_float(pk.y << 16), __uint_as_float(pk.y & 0xFFFF0000u)));
               }
               *reinterpret_cast<uint2*>((uint16_t*)out + (size_t)p * F + r0 + 16 * i) = pk;
+            } else if (FC) {  // pair perm[p], rows 4 (l / 16) .. + 3 of the slice
+              comb[(perm[p] * 16 + 4 * (l >> 4)) >> 2] = g;
             } else {
               *reinterpret_cast<f32x4*>((float*)out + (size_t)p * H + r0 + 16 * i) = g;
             }
@@ -346,8 +379,28 @@ __global__ __launch_bounds__(256) void stream_kernel(
       // red is written again only after at least one more chunk barrier
       if (++c_pass == c_npass) {
         c_pass = 0;
+        const int wt_done = c_wt;
         ++c_j;
         c_item();
+        if (FC && (!c_ok || c_wt != wt_done)) {
+          // every expert's rows of slice wt_done are in comb: y for the slice,
+          // y[t] = (resid[t] +) sum_j w[t][j] * out_j in slot order, pairs
+          // dropped by the capacity (slot -1) skipped
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          const float* cs = reinterpret_cast<const float*>(comb);
+          const int h0 = wt_done * 16;
+          for (int u = threadIdx.x; u < T * 16; u += 256) {
+            const int t = u >> 4, hh = u & 15;
+            float acc = 0.0f;
+            for (int j = 0; j < k_top; ++j) {
+              if (cinv[t * k_top + j] < 0) continue;
+              acc = fmaf(cw[t * k_top + j], cs[(t * k_top + j) * 16 + hh], acc);
+            }
+            const size_t o = (size_t)t * H + h0 + hh;
+            cy[o] = cres ? cres[o] + acc : acc;
+          }
+          // comb is written again only after at least one more chunk barrier
+        }
       }
     }
   }
@@ -355,26 +408,42 @@ __global__ __launch_bounds__(256) void stream_kernel(
 }
 
 template <bool GATED, bool Q8, int QNA, int TR, int NS, int CK>
-int launch_tr(const ExpertArgs& a, hipStream_t st) {
+int launch_tr(const ExpertArgs& a, hipStream_t st, bool* combined = nullptr) {
   constexpr int NA = Q8 ? QNA : (GATED ? 2 : 1), NB = (TR + 15) / 16;
   constexpr int OB = GATED ? NA / 2 : NA;
   constexpr int stage = (16 * NA * (Q8 ? 1 : 2) + TR * 2) * CK, red = 4 * NA * NB * 64 * 16;
   constexpr int lds = NS * stage + (red <= stage ? 16 : red);
-  const int per_cu = (160 * 1024) / lds;
   const int nwt = GATED ? a.F / (16 * OB) : a.H / (16 * NA);
   const int slots = a.E < a.S ? a.E : a.S;
+  const uint16_t* tok = GATED ? (const uint16_t*)a.x : (const uint16_t*)a.act;
+  // the down projection folds the combine in when each of the 16-row hidden
+  // slices can go to a workgroup of its own with every CU busy, and the
+  // slice's outputs of all T*k pairs fit the LDS buffer
+  if constexpr (!GATED && NA == 1) {
+    constexpr int lds_fc = lds + 256 * 16 * 4;
+    if (combined && a.cy && a.S <= 256 && nwt >= cu_count() && lds_fc <= 160 * 1024) {
+      const int per_cu = (160 * 1024) / lds_fc;
+      int grid = cu_count() * per_cu;
+      if (grid > nwt) grid = nwt;
+      stream_kernel<GATED, Q8, QNA, TR, NS, CK, true><<<grid, 256, 0, st>>>(
+          (const uint8_t*)a.experts, a.stride_elems, tok, a.perm, a.k, a.offsets, a.active, a.E,
+          a.H, a.F, a.T, nullptr, a.cw, a.cinv, a.cres, a.cy);
+      *combined = true;
+      return hipGetLastError() == hipSuccess ? 0 : -1;
+    }
+  }
+  const int per_cu = (160 * 1024) / lds;
   int grid = cu_count() * (per_cu < 1 ? 1 : per_cu);
   if (grid > nwt * slots) grid = nwt * slots;
-  const uint16_t* tok = GATED ? (const uint16_t*)a.x : (const uint16_t*)a.act;
   void* out = GATED ? a.act : (void*)a.yp;
   stream_kernel<GATED, Q8, QNA, TR, NS, CK><<<grid, 256, 0, st>>>(
       (const uint8_t*)a.experts, a.stride_elems, tok, a.perm, a.k, a.offsets, a.active, a.E,
-      a.H, a.F, a.T, out);
+      a.H, a.F, a.T, out, nullptr, nullptr, nullptr, nullptr);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 template <bool GATED, bool Q8>
-int launch_stream_q(const ExpertArgs& a, hipStream_t st) {
+int launch_stream_q(const ExpertArgs& a, hipStream_t st, bool* combined) {
   // token rows per pass (experts with more rows take several passes) and the
   // chunk width: 512 for batches of up to 8 rows per expert (16 for the down
   // projection), else 256 when K allows it (bf16 layers have H % 256 == 0
@@ -388,33 +457,35 @@ int launch_stream_q(const ExpertArgs& a, hipStream_t st) {
     // workgroup has one, with a deeper ring
     if (K % 512 == 0) {
       if (GATED) {
-        if (rows <= 8) return launch_tr<GATED, Q8, 4, 8, 3, 256>(a, st);
-        if (rows <= 16) return launch_tr<GATED, Q8, 4, 16, 2, 256>(a, st);
+        if (rows <= 8) return launch_tr<GATED, Q8, 4, 8, 3, 256>(a, st, combined);
+        if (rows <= 16) return launch_tr<GATED, Q8, 4, 16, 2, 256>(a, st, combined);
       } else {
-        if (rows <= 2) return launch_tr<GATED, Q8, 1, 8, 4, 512>(a, st);
-        if (rows > 8 && rows <= 16) return launch_tr<GATED, Q8, 4, 16, 2, 256>(a, st);
+        if (rows <= 2) return launch_tr<GATED, Q8, 1, 8, 4, 512>(a, st, combined);
+        if (rows > 8 && rows <= 16) return launch_tr<GATED, Q8, 4, 16, 2, 256>(a, st, combined);
       }
-      if (rows > 16) return launch_tr<GATED, Q8, 4, 32, 2, 256>(a, st);
+      if (rows > 16) return launch_tr<GATED, Q8, 4, 32, 2, 256>(a, st, combined);
     }
   }
   if (GATED && K % 512 == 0 && rows <= 8)  // 1 KB row runs, one deep ring per CU
-    return launch_tr<GATED, Q8, 2, 8, 3, 512>(a, st);
+    return launch_tr<GATED, Q8, 2, 8, 3, 512>(a, st, combined);
   if (!GATED && K % 512 == 0 && rows <= 16) {  // down: 1 KB row runs
-    if (rows <= 8) return launch_tr<GATED, Q8, 2, 8, Q8 ? 3 : 4, 512>(a, st);
-    return launch_tr<GATED, Q8, 2, 16, 3, 512>(a, st);
+    if (rows <= 8) return launch_tr<GATED, Q8, 2, 8, Q8 ? 3 : 4, 512>(a, st, combined);
+    return launch_tr<GATED, Q8, 2, 16, 3, 512>(a, st, combined);
   }
   if (K % 256 == 0) {
-    if (rows <= 8) return launch_tr<GATED, Q8, 2, 8, GATED ? 3 : 4, 256>(a, st);
-    if (rows <= 16) return launch_tr<GATED, Q8, 2, 16, GATED ? 3 : 4, 256>(a, st);
-    return launch_tr<GATED, Q8, 2, 32, GATED ? 2 : 3, 256>(a, st);
+    if (rows <= 8) return launch_tr<GATED, Q8, 2, 8, GATED ? 3 : 4, 256>(a, st, combined);
+    if (rows <= 16) return launch_tr<GATED, Q8, 2, 16, GATED ? 3 : 4, 256>(a, st, combined);
+    return launch_tr<GATED, Q8, 2, 32, GATED ? 2 : 3, 256>(a, st, combined);
   }
-  if (rows <= 16) return launch_tr<GATED, Q8, 2, 16, 4, 128>(a, st);
-  return launch_tr<GATED, Q8, 2, 32, GATED ? 3 : 4, 128>(a, st);
+  if (rows <= 16) return launch_tr<GATED, Q8, 2, 16, 4, 128>(a, st, combined);
+  return launch_tr<GATED, Q8, 2, 32, GATED ? 3 : 4, 128>(a, st, combined);
 }
 
 template <bool GATED>
-int launch_stream(const ExpertArgs& a, hipStream_t st) {
-  return a.u8 ? launch_stream_q<GATED, true>(a, st) : launch_stream_q<GATED, false>(a, st);
+int launch_stream(const ExpertArgs& a, hipStream_t st, bool* combined) {
+  if (combined) *combined = false;
+  return a.u8 ? launch_stream_q<GATED, true>(a, st, combined)
+              : launch_stream_q<GATED, false>(a, st, combined);
 }
 
 }  // namespace
@@ -433,5 +504,9 @@ int cu_count() {
   return cached[dev];
 }
 
-int launch_stream_gate_up(const ExpertArgs& a, hipStream_t st) { return launch_stream<true>(a, st); }
-int launch_stream_down(const ExpertArgs& a, hipStream_t st) { return launch_stream<false>(a, st); }
+int launch_stream_gate_up(const ExpertArgs& a, hipStream_t st) {
+  return launch_stream<true>(a, st, nullptr);
+}
+int launch_stream_down(const ExpertArgs& a, bool* combined, hipStream_t st) {
+  return launch_stream<false>(a, st, combined);
+}

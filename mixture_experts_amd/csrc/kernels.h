@@ -59,6 +59,13 @@ struct ExpertArgs {
   const int32_t* active;    // [E+1]
   void* act;                // [S][F] bf16 or fp32
   float* yp;                // [S][H] fp32
+  // step 5 inputs for a down projection that folds the combine in (cy null:
+  // it may not): gate weights [T][k], slot of each pair [T][k] (-1: dropped),
+  // residual [T][H] or null, output [T][H]
+  const float* cw = nullptr;
+  const int32_t* cinv = nullptr;
+  const float* cres = nullptr;
+  float* cy = nullptr;
 };
 
 int router_splits(int T, int H);
@@ -82,7 +89,8 @@ int launch_grouped_down(const ExpertArgs& a, int ksplit, hipStream_t st);
 // bf16 expert FFN, weight-streaming MFMA kernels (few rows per expert; every
 // batch for uint8 experts)
 int launch_stream_gate_up(const ExpertArgs& a, hipStream_t st);
-int launch_stream_down(const ExpertArgs& a, hipStream_t st);
+// *combined: set when the launch also wrote y (step 5 folded in)
+int launch_stream_down(const ExpertArgs& a, bool* combined, hipStream_t st);
 // fp32 expert FFN (plain FMA)
 int launch_f32_gate_up(const ExpertArgs& a, hipStream_t st);
 int launch_f32_down(const ExpertArgs& a, hipStream_t st);

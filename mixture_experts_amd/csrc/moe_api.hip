@@ -44,7 +44,8 @@ struct moe_layer {
 namespace {
 
 constexpr uint32_t kKnownFlags = MOE_FLAG_RESIDUAL_PRENORM | MOE_FLAG_PATH_GROUPED |
-                                 MOE_FLAG_PATH_STREAM | MOE_FLAG_GATE_RAW;
+                                 MOE_FLAG_PATH_STREAM | MOE_FLAG_GATE_RAW |
+                                 MOE_FLAG_COMBINE_SEPARATE;
 
 struct Arena {
   char* base;
@@ -91,7 +92,8 @@ int validate_desc(const moe_layer_desc* d) {
   if (d->num_experts > MOE_MAX_EXPERTS || d->top_k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   if (d->dtype == MOE_BF16 && (H % 256 || F % 128)) return MOE_ERR_UNSUPPORTED;
   if (d->dtype == MOE_F32 && (H % 4 || F % 4)) return MOE_ERR_UNSUPPORTED;
-  if ((d->flags & MOE_FLAG_RESIDUAL_PRENORM) && d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if ((d->flags & MOE_FLAG_RESIDUAL_PRENORM) && (d->dtype != MOE_BF16 || H > 16384))
+    return MOE_ERR_UNSUPPORTED;
   const uint64_t S = (uint64_t)d->max_tokens * (uint64_t)d->top_k;
   const uint64_t lim = 1ull << 31;
   if (S * (H > F ? H : F) >= lim || 3 * H * F >= lim || (uint64_t)d->max_tokens * H >= lim)
@@ -347,10 +349,21 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
   if (r1 || !mark(MOE_STAGE_DOWN)) return MOE_ERR_DEVICE;
   const float* resid = prenorm ? (const float*)x : nullptr;
   const int planes = (f32 || stream_path) ? 1 : grouped_down_ksplit(ea);
+  // the streaming down projection may take step 5 over (then the combine
+  // stage below is empty)
+  bool combined = false;
+  if (stream_path && !(d.flags & MOE_FLAG_COMBINE_SEPARATE)) {
+    ea.cw = L->w;
+    ea.cinv = L->inv;
+    ea.cres = resid;
+    ea.cy = (float*)y;
+  }
   int r2 = f32 ? launch_f32_down(ea, st)
-               : stream_path ? launch_stream_down(ea, st) : launch_grouped_down(ea, planes, st);
+               : stream_path ? launch_stream_down(ea, &combined, st)
+                             : launch_grouped_down(ea, planes, st);
   if (r2 || !mark(MOE_STAGE_COMBINE)) return MOE_ERR_DEVICE;
-  if (launch_combine(L->yp, planes, L->w, L->inv, resid, T, d.hidden, d.top_k, y, st))
+  if (!combined &&
+      launch_combine(L->yp, planes, L->w, L->inv, resid, T, d.hidden, d.top_k, y, st))
     return MOE_ERR_DEVICE;
   if (!mark(MOE_NUM_STAGES)) return MOE_ERR_DEVICE;
   return MOE_OK;

@@ -368,22 +368,45 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
 }
 
 // Branch input of a stacked layer: xt[t] = bf16(h[t] / sqrt(mean(h[t]^2) + 1e-6)).
-// One workgroup per token; fixed-order reduction.
+// One workgroup per token.  Thread i holds the 4-float groups i, i + 256, ...
+// of the row in registers (NV of them, all loads in flight together), sums
+// their squares in that order, the waves reduce with a butterfly and the four
+// wave sums are added in wave order, so the reduction order is fixed.
+template <int NV>
 __global__ __launch_bounds__(256) void prenorm_kernel(const float* __restrict__ h, int H,
                                                       uint16_t* __restrict__ xt) {
-  __shared__ float part[256];
+  __shared__ float wsum[4];
   const int t = blockIdx.x, tid = threadIdx.x;
-  const float* row = h + (size_t)t * H;
-  float ss = 0.0f;
-  for (int i = tid; i < H; i += 256) ss = fmaf(row[i], row[i], ss);
-  part[tid] = ss;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (tid < s) part[tid] += part[tid + s];
-    __syncthreads();
+  const f32x4* row = reinterpret_cast<const f32x4*>(h + (size_t)t * H);
+  const int n4 = H >> 2;
+  f32x4 v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = tid + i * 256;
+    v[i] = c < n4 ? row[c] : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const float r = sqrtf(part[0] / (float)H + 1e-6f);
-  for (int i = tid; i < H; i += 256) xt[(size_t)t * H + i] = f32_to_bf16(row[i] / r);
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ss = fmaf(v[i][j], v[i][j], ss);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+  const float r = sqrtf(tot / (float)H + 1e-6f);
+  uint2* out = reinterpret_cast<uint2*>(xt + (size_t)t * H);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = tid + i * 256;
+    if (c < n4) {
+      uint2 o;
+      o.x = (uint32_t)f32_to_bf16(v[i][0] / r) | ((uint32_t)f32_to_bf16(v[i][1] / r) << 16);
+      o.y = (uint32_t)f32_to_bf16(v[i][2] / r) | ((uint32_t)f32_to_bf16(v[i][3] / r) << 16);
+      out[c] = o;
+    }
+  }
 }
 
 // Small batches (T <= 64, one token tile): routing and dispatch in one
@@ -715,6 +738,14 @@ int launch_route_small(const RouterArgs& a, const DispatchArgs& d, int32_t* coun
 }
 
 int launch_prenorm(const float* h, int T, int H, uint16_t* xt, hipStream_t st) {
-  prenorm_kernel<<<T, 256, 0, st>>>(h, H, xt);
+  // H is a multiple of 4 (a multiple of 256 for bf16 layers, the only ones
+  // with a residual stream) and at most 64 K: up to 64 floats per thread
+  const int nv = (H / 4 + 255) / 256;
+  if (H % 4 || nv > 16) return -1;
+  if (nv <= 1) prenorm_kernel<1><<<T, 256, 0, st>>>(h, H, xt);
+  else if (nv <= 2) prenorm_kernel<2><<<T, 256, 0, st>>>(h, H, xt);
+  else if (nv <= 4) prenorm_kernel<4><<<T, 256, 0, st>>>(h, H, xt);
+  else if (nv <= 8) prenorm_kernel<8><<<T, 256, 0, st>>>(h, H, xt);
+  else prenorm_kernel<16><<<T, 256, 0, st>>>(h, H, xt);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -73,6 +73,9 @@ def _desc(**kw):
     (dict(dtype=moe.MOE_F32, flags=moe.MOE_FLAG_RESIDUAL_PRENORM,
           expert_stride=3 * 256 * 256 * 4), moe.MOE_ERR_UNSUPPORTED),
     (dict(hidden=65536, ffn=65536, expert_stride=3 * 65536 * 65536 * 2), moe.MOE_ERR_UNSUPPORTED),
+    # the residual stream's row is held in registers: H <= 16384
+    (dict(hidden=16640, ffn=256, flags=moe.MOE_FLAG_RESIDUAL_PRENORM,
+          expert_stride=3 * 16640 * 256 * 2), moe.MOE_ERR_UNSUPPORTED),
     (dict(expert_format=2), moe.MOE_ERR_INVALID_ARG),
     (dict(expert_format=-1), moe.MOE_ERR_INVALID_ARG),
     # uint8 experts: room for the 64-byte parameter block, bf16 layers, streaming path only
@@ -128,3 +131,17 @@ def test_null_handle_calls():
     st = ctypes.c_int(0)
     assert not lib.moe_layer_create(None, ctypes.byref(st))
     assert st.value == moe.MOE_ERR_INVALID_ARG
+
+
+def test_binding_constants_match_header():
+    """Every MOE_* enumerator of include/moe.h has the same value in the binding."""
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    found = 0
+    for name, val in re.findall(r"\b(MOE_[A-Z0-9_]+)\s*=\s*([^,\n}]+)", text):
+        v = val.strip()
+        m = re.fullmatch(r"1u?\s*<<\s*(\d+)", v)
+        num = (1 << int(m.group(1))) if m else int(v, 0)
+        assert getattr(moe, name) == num, name
+        found += 1
+    assert found >= 10
