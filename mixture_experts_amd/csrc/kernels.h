@@ -27,6 +27,11 @@ struct RouterArgs {
   float* part;            // [router_splits(T, H)][T][E] partial logits (bf16 layers)
   uint16_t* wrt;          // [E][H] workspace for the transposed router (bf16 layers)
   int raw_gate;           // 1: gate weights = the selected logits (no softmax)
+  // residual layers on the one-workgroup small-batch route: the fp32 stream
+  // [T][H], and the branch input [T][H] bf16 the route forms from it (x is
+  // then not read)
+  const float* hres = nullptr;
+  uint16_t* xt_out = nullptr;
 };
 
 struct DispatchArgs {
@@ -75,6 +80,8 @@ int launch_prenorm(const float* h, int T, int H, uint16_t* xt, hipStream_t st);
 // left zeroed by the kernel)
 int launch_route_small(const RouterArgs& a, const DispatchArgs& d, int32_t* counter,
                        hipStream_t st);
+// whether launch_route_small can form the prenorm branch input itself
+bool route_small_folds_prenorm(int T, int H, int E);
 int launch_dispatch(const DispatchArgs& a, hipStream_t st);
 
 // compute units of the current device (cached per device)

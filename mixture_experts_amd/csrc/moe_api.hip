@@ -294,8 +294,13 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
   const int S = T * d.top_k;
   const void* xin = x;
   if (!mark(MOE_STAGE_ROUTE)) return MOE_ERR_DEVICE;
+  // residual layers: the small-batch route forms the branch input itself
+  // when it runs in one workgroup per 16 tokens; otherwise a kernel of its own
+  const bool fold_pn = prenorm && small_route(L, T, nullptr) &&
+                       route_small_folds_prenorm(T, d.hidden, d.num_experts);
   if (prenorm) {
-    if (launch_prenorm((const float*)x, T, d.hidden, L->xt, st)) return MOE_ERR_DEVICE;
+    if (!fold_pn && launch_prenorm((const float*)x, T, d.hidden, L->xt, st))
+      return MOE_ERR_DEVICE;
     xin = L->xt;
   }
   const bool f32 = d.dtype == MOE_F32;
@@ -307,6 +312,10 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
                   (dd.flags & MOE_FLAG_GATE_RAW) ? 1 : 0};
     DispatchArgs da{L->idx, S, dd.num_experts, GG_BT, L->hist, L->rank, L->base, L->counts,
                     L->offsets, L->tile_off, L->active, L->perm, L->inv, dd.expert_capacity};
+    if (fold_pn) {
+      ra.hres = (const float*)x;
+      ra.xt_out = L->xt;
+    }
     if (small_route(L, T, nullptr)) {  // one launch: the dispatch stage is empty
       if (launch_route_small(ra, da, L->sync, st)) return MOE_ERR_DEVICE;
       if (!mark(MOE_STAGE_DISPATCH)) return MOE_ERR_DEVICE;

@@ -367,7 +367,8 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
   topk_rows(lg, ldl, tile0, T, E, k, raw, idx_out, w_out);
 }
 
-// Branch input of a stacked layer: xt[t] = bf16(h[t] / sqrt(mean(h[t]^2) + 1e-6)).
+// Branch input of a stacked layer: xt[t] = bf16(h[t] / sqrt(mean(h[t]^2) + 1e-6)),
+// the division taken as one fp32 reciprocal and a product per element.
 // One workgroup per token.  Thread i holds the 4-float groups i, i + 256, ...
 // of the row in registers (NV of them, all loads in flight together), sums
 // their squares in that order, the waves reduce with a butterfly and the four
@@ -395,16 +396,15 @@ __global__ __launch_bounds__(256) void prenorm_kernel(const float* __restrict__ 
   if ((tid & 63) == 0) wsum[tid >> 6] = ss;
   __syncthreads();
   const float tot = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
-  const float r = sqrtf(tot / (float)H + 1e-6f);
+  const float ri = 1.0f / sqrtf(tot / (float)H + 1e-6f);
   uint2* out = reinterpret_cast<uint2*>(xt + (size_t)t * H);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c = tid + i * 256;
     if (c < n4) {
-      uint2 o;
-      o.x = (uint32_t)f32_to_bf16(v[i][0] / r) | ((uint32_t)f32_to_bf16(v[i][1] / r) << 16);
-      o.y = (uint32_t)f32_to_bf16(v[i][2] / r) | ((uint32_t)f32_to_bf16(v[i][3] / r) << 16);
-      out[c] = o;
+      const bf16x2 lo = {(__bf16)(v[i][0] * ri), (__bf16)(v[i][1] * ri)};
+      const bf16x2 hi = {(__bf16)(v[i][2] * ri), (__bf16)(v[i][3] * ri)};
+      out[c] = uint2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
     }
   }
 }
@@ -516,17 +516,29 @@ __global__ __launch_bounds__(256) void route_small_kernel(
 // resets the counter for the next launch.
 constexpr int R1_HMAX = 4096;
 constexpr int R1_LDW = R1_HMAX + 8;  // padded router row (bf16)
-template <int MB, int EV, bool MULTI>
+// PN: the input is the fp32 residual stream h; the workgroup also forms the
+// branch input bf16(h / sqrt(mean h^2 + 1e-6)) of its tokens (written to xt
+// for the expert kernels) and routes on it.  Each lane loads the fp32 values
+// of exactly the bf16 operand fragments it feeds to the MFMA, so the norm
+// needs only a reduction: over the 4 lane groups of a wave (butterfly), then
+// over the 16 waves in wave order.
+template <int MB, int EV, bool MULTI, bool PN>
 __global__ __launch_bounds__(1024) void route_one_kernel(
     const uint16_t* __restrict__ x, int T_all, int H, int E, int k, int raw,
     const uint16_t* __restrict__ wr, const float* __restrict__ bias, int tile_rows, int cap,
     int32_t* __restrict__ counter, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off,
-    int32_t* __restrict__ active, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    int32_t* __restrict__ active, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+    const float* __restrict__ hres, uint16_t* __restrict__ xt_out) {
   static_assert(!MULTI || MB == 1, "one token block per workgroup");
+  static_assert(!PN || MB == 1, "prenorm: one token block per workgroup");
   const int tok0 = MULTI ? (int)blockIdx.x * 16 : 0;  // this workgroup's first token
   const int T = MULTI ? min(16, T_all - tok0) : T_all;
   x += (size_t)tok0 * H;
+  if (PN) {
+    hres += (size_t)tok0 * H;
+    xt_out += (size_t)tok0 * H;
+  }
   // the staged router, later the 16 partial logit tiles [16][RT_TOK][17]
   __shared__ __attribute__((aligned(16))) uint16_t wt[16 * R1_LDW];
   __shared__ float lg[RT_TOK * 17];
@@ -543,7 +555,18 @@ __global__ __launch_bounds__(1024) void route_one_kernel(
   const int hw = H / 16, hb = wave * hw, nks = hw / 32;  // nks <= 8
   constexpr int KS = R1_HMAX / 16 / 32;
   u32x4 xa[2][KS];
+  f32x4 hv[PN ? KS : 1][2];  // PN: this lane's 8 fp32 values per K step
   auto load_x = [&](int m0) {
+    if (PN) {
+      const float* hr = hres + (size_t)min(r16, T - 1) * H + hb + kg * 8;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        if (s < nks) {
+          hv[s][0] = *reinterpret_cast<const f32x4*>(hr + s * 32);
+          hv[s][1] = *reinterpret_cast<const f32x4*>(hr + s * 32 + 4);
+        }
+      return;
+    }
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm) {
       const uint16_t* xr = x + (size_t)min((m0 + mm) * 16 + r16, T - 1) * H + hb + kg * 8;
@@ -553,6 +576,7 @@ __global__ __launch_bounds__(1024) void route_one_kernel(
     }
   };
   load_x(0);
+  __shared__ float pn_ss[PN ? 16 * 16 : 1];  // [wave][token] sums of squares
   // stage Wr^T (EV = 8: E is 8 and a router row is one 16-byte load)
   if (EV > 0) {
     // thread i < H/8 takes router rows 8i .. 8i+7 (8 experts per 16-byte
@@ -595,7 +619,42 @@ __global__ __launch_bounds__(1024) void route_one_kernel(
       for (int e = 0; e < 16; ++e) wt[e * R1_LDW + h] = wv[e];
     }
   }
+  if (PN) {  // this lane's part of its token's sum of squares, in K order
+    float ss = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      if (s < nks)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ss = fmaf(hv[s][hf][j], hv[s][hf][j], ss);
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    if (kg == 0) pn_ss[wave * 16 + r16] = ss;
+  }
   __syncthreads();
+  if (PN) {
+    float tot = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) tot += pn_ss[w * 16 + r16];
+    const float ri = 1.0f / sqrtf(tot / (float)H + 1e-6f);
+    const bool own = r16 < T;  // rows past T repeat the last token: no store
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      if (s < nks) {
+        uint32_t q[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 v = hv[s][j >> 1];
+          const int o = (j & 1) * 2;
+          const bf16x2 b2 = {(__bf16)(v[o] * ri), (__bf16)(v[o + 1] * ri)};
+          q[j] = __builtin_bit_cast(uint32_t, b2);
+        }
+        xa[0][s] = u32x4{q[0], q[1], q[2], q[3]};
+        if (own)
+          *reinterpret_cast<u32x4*>(xt_out + (size_t)r16 * H + hb + s * 32 + kg * 8) = xa[0][s];
+      }
+  }
 
   f32x4 acc[MB];
 #pragma unroll
@@ -703,20 +762,30 @@ int launch_router(const RouterArgs& a, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+bool route_small_folds_prenorm(int T, int H, int E) {
+  return E <= 16 && H <= R1_HMAX && H % 512 == 0 && T <= RT_TOK;
+}
+
 int launch_route_small(const RouterArgs& a, const DispatchArgs& d, int32_t* counter,
                        hipStream_t st) {
-  if (a.E <= 16 && a.H <= R1_HMAX && a.H % 512 == 0 && a.T <= RT_TOK) {
+  if (a.hres && !route_small_folds_prenorm(a.T, a.H, a.E)) return -1;
+  if (route_small_folds_prenorm(a.T, a.H, a.E)) {
     auto* xx = (const uint16_t*)a.x;
     auto* ww = (const uint16_t*)a.wr;
 #define R1_ARGS xx, a.T, a.H, a.E, a.k, a.raw_gate, ww, a.bias, d.tile_rows, d.capacity, counter, a.idx, \
-                a.w, d.counts, d.offsets, d.tile_off, d.active, d.perm, d.inv
+                a.w, d.counts, d.offsets, d.tile_off, d.active, d.perm, d.inv, a.hres, a.xt_out
     const int mb = (a.T + 15) / 16;
     // one workgroup up to 16 tokens, one per 16 tokens beyond
-#define R1_MB(EV)                                                                \
-    if (mb <= 1) route_one_kernel<1, EV, false><<<1, 1024, 0, st>>>(R1_ARGS);    \
-    else route_one_kernel<1, EV, true><<<mb, 1024, 0, st>>>(R1_ARGS);
-    if (a.E == 8) { R1_MB(8) }
-    else { R1_MB(0) }
+#define R1_MB(EV, PN)                                                                \
+    if (mb <= 1) route_one_kernel<1, EV, false, PN><<<1, 1024, 0, st>>>(R1_ARGS);    \
+    else route_one_kernel<1, EV, true, PN><<<mb, 1024, 0, st>>>(R1_ARGS);
+    if (a.hres) {
+      if (a.E == 8) { R1_MB(8, true) }
+      else { R1_MB(0, true) }
+    } else {
+      if (a.E == 8) { R1_MB(8, false) }
+      else { R1_MB(0, false) }
+    }
 #undef R1_MB
 #undef R1_ARGS
     return hipGetLastError() == hipSuccess ? 0 : -1;
