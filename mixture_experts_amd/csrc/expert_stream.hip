@@ -416,25 +416,24 @@ int launch_tr(const ExpertArgs& a, hipStream_t st, bool* combined = nullptr) {
   const int nwt = GATED ? a.F / (16 * OB) : a.H / (16 * NA);
   const int slots = a.E < a.S ? a.E : a.S;
   const uint16_t* tok = GATED ? (const uint16_t*)a.x : (const uint16_t*)a.act;
-  // the down projection folds the combine in when each of the 16-row hidden
-  // slices can go to a workgroup of its own with every CU busy, and the
-  // slice's outputs of all T*k pairs fit the LDS buffer
+  const int per_cu = (160 * 1024) / lds;
+  int grid = cu_count() * (per_cu < 1 ? 1 : per_cu);
+  if (grid > nwt * slots) grid = nwt * slots;
+  // the down projection folds the combine in when the slice's outputs of all
+  // T*k pairs fit the LDS buffer and one workgroup per 16-row hidden slice is
+  // as many workgroups as the plain launch would run (then no CU idles)
   if constexpr (!GATED && NA == 1) {
     constexpr int lds_fc = lds + 256 * 16 * 4;
-    if (combined && a.cy && a.S <= 256 && nwt >= cu_count() && lds_fc <= 160 * 1024) {
-      const int per_cu = (160 * 1024) / lds_fc;
-      int grid = cu_count() * per_cu;
-      if (grid > nwt) grid = nwt;
-      stream_kernel<GATED, Q8, QNA, TR, NS, CK, true><<<grid, 256, 0, st>>>(
+    const int grid_fc = nwt < cu_count() * ((160 * 1024) / lds_fc) ? nwt
+                                                                   : cu_count() * ((160 * 1024) / lds_fc);
+    if (combined && a.cy && a.S <= 256 && lds_fc <= 160 * 1024 && grid_fc >= grid) {
+      stream_kernel<GATED, Q8, QNA, TR, NS, CK, true><<<grid_fc, 256, 0, st>>>(
           (const uint8_t*)a.experts, a.stride_elems, tok, a.perm, a.k, a.offsets, a.active, a.E,
           a.H, a.F, a.T, nullptr, a.cw, a.cinv, a.cres, a.cy);
       *combined = true;
       return hipGetLastError() == hipSuccess ? 0 : -1;
     }
   }
-  const int per_cu = (160 * 1024) / lds;
-  int grid = cu_count() * (per_cu < 1 ? 1 : per_cu);
-  if (grid > nwt * slots) grid = nwt * slots;
   void* out = GATED ? a.act : (void*)a.yp;
   stream_kernel<GATED, Q8, QNA, TR, NS, CK><<<grid, 256, 0, st>>>(
       (const uint8_t*)a.experts, a.stride_elems, tok, a.perm, a.k, a.offsets, a.active, a.E,
