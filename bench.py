@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the 32-layer stacked decode (90 GB of experts)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-batches", default="1,4,16,64",
+                    help="decode / stacked-decode batch sizes to run (comma-separated, "
+                         "from 1,4,16,64; a subset isolates one batch size in a kernel trace)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (reference "
@@ -117,7 +120,10 @@ def stage_times(layer, x, y, T, steps, warm):
             for s in range(nst)]
 
 
-def bench_decode(shape, x, y, K, W, u8=False):
+DECODE_BATCHES = (1, 4, 16, 64)
+
+
+def bench_decode(shape, x, y, K, W, u8=False, batches=DECODE_BATCHES):
     """The Mixtral-shaped layer on decode batches T = 1, 4, 16, 64.  Four
     copies of the layer's experts (4 x 2.8 GB bf16 or 4 x 1.4 GB uint8, far
     beyond the 256 MB of Infinity Cache) are visited in turn, one HIP-graph
@@ -142,7 +148,7 @@ def bench_decode(shape, x, y, K, W, u8=False):
     wbytes = 1 if u8 else 2  # per weight
     eb = 3 * shape.H * shape.F * wbytes + (64 if u8 else 0)
     res = {"weight_copies": NCOPY, "expert_weights": "uint8 (affine per matrix)" if u8 else "bf16"}
-    for Td in (1, 4, 16, 64):
+    for Td in batches:
         xd, yd = x[:Td], y[:Td]
         r = layers[0].route(xd, Td)
         torch.cuda.synchronize()
@@ -190,7 +196,7 @@ def bench_decode(shape, x, y, K, W, u8=False):
     return res
 
 
-def bench_stack(K, W, u8=False):
+def bench_stack(K, W, u8=False, batches=DECODE_BATCHES):
     """32 Mixtral-shaped layers, experts in one contiguous buffer (layer l,
     expert e at blob + (l*E + e)*stride), residual stream h <- h + MoE(norm(h));
     one step = all 32 layers on a decode batch, replayed as one HIP graph."""
@@ -215,7 +221,7 @@ def bench_stack(K, W, u8=False):
     eb = 3 * shape.H * shape.F * (1 if u8 else 2) + (64 if u8 else 0)
     res = {"layers": NL, "expert_buffer_GB": round(blob.numel() / 1e9, 2),
            "expert_weights": "uint8 (affine per matrix)" if u8 else "bf16"}
-    for T in (1, 4, 16, 64):
+    for T in batches:
         x0 = torch.from_numpy(gen.normal(0, 0, gen.T_X, T * shape.H, 1.0, "f32")).cuda()
         x0 = x0.view(T, shape.H)
         h = torch.empty_like(x0)
@@ -269,6 +275,10 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr, flush=True)
+        sys.exit(2)
+    batches = tuple(int(b) for b in args.decode_batches.split(","))
+    if not set(batches) <= set(DECODE_BATCHES):
+        print(f"--decode-batches: choose from {DECODE_BATCHES}", file=sys.stderr, flush=True)
         sys.exit(2)
     import numpy as np
     import torch
@@ -350,14 +360,14 @@ def main():
 
     if not args.no_decode and args.workload == "mixtral_prefill":
         print("[bench] decode batches, bf16 and uint8 experts", file=sys.stderr, flush=True)
-        out["decode"] = bench_decode(shape, x, y, max(K, 50), W)
-        out["decode_u8"] = bench_decode(shape, x, y, max(K, 50), W, u8=True)
+        out["decode"] = bench_decode(shape, x, y, max(K, 50), W, batches=batches)
+        out["decode_u8"] = bench_decode(shape, x, y, max(K, 50), W, u8=True, batches=batches)
 
     if not args.no_stack and args.workload == "mixtral_prefill":
         print("[bench] 32-layer stacked decode, bf16 and uint8 experts", file=sys.stderr,
               flush=True)
-        out["stack_decode"] = bench_stack(max(K, 20), W)
-        out["stack_decode_u8"] = bench_stack(max(K, 20), W, u8=True)
+        out["stack_decode"] = bench_stack(max(K, 20), W, batches=batches)
+        out["stack_decode_u8"] = bench_stack(max(K, 20), W, u8=True, batches=batches)
 
     if not args.no_cpu_baseline:
         import oracle

@@ -762,14 +762,16 @@ int launch_router(const RouterArgs& a, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+// (one workgroup: with several, the workgroups' fp32 loads of the stream
+// lengthen the route more than a separate normalisation launch costs)
 bool route_small_folds_prenorm(int T, int H, int E) {
-  return E <= 16 && H <= R1_HMAX && H % 512 == 0 && T <= RT_TOK;
+  return E <= 16 && H <= R1_HMAX && H % 512 == 0 && T <= 16;
 }
 
 int launch_route_small(const RouterArgs& a, const DispatchArgs& d, int32_t* counter,
                        hipStream_t st) {
   if (a.hres && !route_small_folds_prenorm(a.T, a.H, a.E)) return -1;
-  if (route_small_folds_prenorm(a.T, a.H, a.E)) {
+  if (a.E <= 16 && a.H <= R1_HMAX && a.H % 512 == 0 && a.T <= RT_TOK) {
     auto* xx = (const uint16_t*)a.x;
     auto* ww = (const uint16_t*)a.wr;
 #define R1_ARGS xx, a.T, a.H, a.E, a.k, a.raw_gate, ww, a.bias, d.tile_rows, d.capacity, counter, a.idx, \
