@@ -11,7 +11,11 @@
 // and the tile schedule count the kept pairs, a dropped pair gets inv = -1,
 // perm is -1 beyond the kept pairs.
 //
-// Three kernels, all deterministic (no ordering depends on atomics):
+// Up to 8192 pairs, one workgroup does it all (dispatch_one_kernel: 16 waves
+// rank their share of the slots as below, the per-wave counts give each
+// wave's base per expert, one thread scans the experts, every thread
+// scatters); beyond that three kernels.  All deterministic (no ordering
+// depends on atomics):
 //   hist    one wave per run of 512 slots; the rank of a slot among the
 //           earlier slots of the same expert in its run comes from a
 //           bit-sliced ballot match (lanes holding the same expert id) and a
@@ -124,10 +128,105 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   }
 }
 
+// The whole dispatch of S <= D1_MAX pairs in one workgroup of 16 waves.
+// Wave w ranks slots [w SW, (w+1) SW) (SW a multiple of 64) within the wave
+// by the same ballot match; wh[w][e] then turns from that wave's count into
+// the pairs of expert e in waves before w.
+constexpr int D1_MAX = 8192;
+__global__ __launch_bounds__(1024) void dispatch_one_kernel(
+    const int32_t* __restrict__ idx, int S, int E, int nbits, int tile_rows, int cap,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off,
+    int32_t* __restrict__ active, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  __shared__ int32_t idx_l[D1_MAX];
+  __shared__ int32_t rank_l[D1_MAX];
+  __shared__ int32_t wh[16][MOE_MAX_EXPERTS];
+  __shared__ int32_t tot[MOE_MAX_EXPERTS];
+  __shared__ int32_t off_l[MOE_MAX_EXPERTS + 1];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < S; i += 1024) idx_l[i] = idx[i];
+  for (int i = tid; i < 16 * MOE_MAX_EXPERTS; i += 1024) wh[i / MOE_MAX_EXPERTS][i % MOE_MAX_EXPERTS] = 0;
+  __syncthreads();
+  const int SW = ((S + 1023) / 1024) * 64;  // slots per wave
+  int32_t* cnt = wh[wave];
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c = 0; c * 64 < SW; ++c) {
+    const int sl = wave * SW + c * 64 + lane;
+    const bool valid = sl < S;
+    const int e = valid ? idx_l[sl] : 0;
+    uint64_t match = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      match &= bit ? m : ~m;
+    }
+    const uint64_t earlier = match & below;
+    const int c0 = valid ? cnt[e] : 0;
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      rank_l[sl] = c0 + __popcll(earlier);
+      if (earlier == 0) cnt[e] = c0 + __popcll(match);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  if (tid < E) {  // per-wave bases of expert tid, its total kept
+    int run = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int h = wh[w][tid];
+      wh[w][tid] = run;
+      run += h;
+    }
+    tot[tid] = (cap > 0 && run > cap) ? cap : run;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int o = 0, t = 0, n = 0;
+    for (int e = 0; e < E; ++e) {
+      const int c = tot[e];
+      off_l[e] = o;
+      offsets[e] = o;
+      counts[e] = c;
+      tile_off[e] = t;
+      o += c;
+      t += (c + tile_rows - 1) / tile_rows;
+      if (c > 0) active[n++] = e;
+    }
+    off_l[E] = o;
+    offsets[E] = o;
+    tile_off[E] = t;
+    active[E] = n;
+  }
+  __syncthreads();
+  for (int sl = tid; sl < S; sl += 1024) {
+    const int e = idx_l[sl];
+    const int g = wh[sl / SW][e] + rank_l[sl];  // rank of the pair in its expert
+    if (sl >= off_l[E]) perm[sl] = -1;          // beyond the kept pairs
+    if (cap > 0 && g >= cap) {
+      inv[sl] = -1;  // dropped
+      continue;
+    }
+    const int p = off_l[e] + g;
+    if (p >= 0 && p < S) {  // by construction; kept as in the scatter kernel
+      perm[p] = sl;
+      inv[sl] = p;
+    } else {
+      inv[sl] = -1;
+    }
+  }
+}
+
 }  // namespace
 
 int launch_dispatch(const DispatchArgs& a, hipStream_t st) {
   const int S = a.S;
+  if (S <= D1_MAX) {
+    int nb = 0;
+    while ((1 << nb) < a.E) ++nb;
+    dispatch_one_kernel<<<1, 1024, 0, st>>>(a.idx, S, a.E, nb, a.tile_rows, a.capacity,
+                                            a.counts, a.offsets, a.tile_off, a.active, a.perm,
+                                            a.inv);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   const int nrun = (S + DISPATCH_RUN - 1) / DISPATCH_RUN;
   int nbits = 0;
   while ((1 << nbits) < a.E) ++nbits;

@@ -311,9 +311,9 @@ __global__ __launch_bounds__(256) void router_partial_kernel(
 
 // Sum of the partial logits in split order (+ bias), then top-k and softmax.
 // nsplit == 0: `part` holds caller-given logits [T][E], used as they are.
-// RK_TOK tokens per workgroup (4 per wave), so a prefill batch spreads over
-// the whole chip.
-constexpr int RK_TOK = 16;
+// RK_TOK tokens per workgroup, one per wave: the selection is a chain of
+// cross-lane steps, so many waves in flight, not many tokens per wave, hide it.
+constexpr int RK_TOK = 4;
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ part,
                                                           int nsplit, int T, int E, int k, int raw,
                                                           const float* __restrict__ bias,
