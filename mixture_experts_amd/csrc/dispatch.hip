@@ -13,7 +13,7 @@
 //
 // Up to 8192 pairs, one workgroup does it all (dispatch_one_kernel: 16 waves
 // rank their share of the slots as below, the per-wave counts give each
-// wave's base per expert, one thread scans the experts, every thread
+// wave's base per expert, the experts are scanned in parallel, every thread
 // scatters); beyond that three kernels.  All deterministic (no ordering
 // depends on atomics):
 //   hist    one wave per run of 512 slots; the rank of a slot among the
@@ -27,6 +27,66 @@
 #include "kernels.h"
 
 namespace {
+
+// Exclusive prefix over the experts, for a workgroup of at least 256
+// threads (E <= 256): offsets[e] = sum of sc[e'] for e' < e, tile_off[e] the
+// same over ceil(sc / tile_rows), active[] = the experts with sc > 0 in
+// ascending order, and the totals at [E].  Waves 0-3 scan 64 experts each
+// (shuffle-up steps), then add the earlier waves' totals.  off_l (LDS, E+1)
+// receives the offsets too.  Ends with a workgroup barrier.
+__device__ void expert_prefix(const int32_t* sc, int E, int tile_rows,
+                              int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off,
+                              int32_t* __restrict__ active, int32_t* off_l) {
+  __shared__ int32_t wsum[4][3];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int c = 0, t = 0, f = 0;
+  int ic = 0, it = 0, iff = 0;  // inclusive prefixes within the wave
+  if (tid < 256) {
+    c = tid < E ? sc[tid] : 0;
+    t = (c + tile_rows - 1) / tile_rows;
+    f = c > 0 ? 1 : 0;
+    ic = c;
+    it = t;
+    iff = f;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int uc = __shfl_up(ic, d), ut = __shfl_up(it, d), uf = __shfl_up(iff, d);
+      if (lane >= d) {
+        ic += uc;
+        it += ut;
+        iff += uf;
+      }
+    }
+    if (lane == 63) {
+      wsum[wave][0] = ic;
+      wsum[wave][1] = it;
+      wsum[wave][2] = iff;
+    }
+  }
+  __syncthreads();
+  if (tid < 256) {
+    int bc = 0, bt = 0, bf = 0;
+    for (int w = 0; w < wave; ++w) {
+      bc += wsum[w][0];
+      bt += wsum[w][1];
+      bf += wsum[w][2];
+    }
+    const int ec = bc + ic - c, et = bt + it - t, ef = bf + iff - f;  // exclusive
+    if (tid < E) {
+      offsets[tid] = ec;
+      tile_off[tid] = et;
+      off_l[tid] = ec;
+      if (f) active[ef] = tid;
+    }
+    if (tid == E - 1) {
+      offsets[E] = ec + c;
+      tile_off[E] = et + t;
+      off_l[E] = ec + c;
+      active[E] = ef + f;
+    }
+  }
+  __syncthreads();
+}
 
 __global__ __launch_bounds__(64) void dispatch_hist_kernel(const int32_t* __restrict__ idx,
                                                            int S, int E, int nbits,
@@ -60,48 +120,57 @@ __global__ __launch_bounds__(64) void dispatch_hist_kernel(const int32_t* __rest
   for (int e = lane; e < E; e += 64) hist[(size_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// One workgroup of MOE_MAX_EXPERTS threads.  base[r][e] = sum of hist[r'][e]
-// for r' < r (the expert's pairs in earlier runs).  counts[e] = the pairs
+// One workgroup of 1024 threads, thread (c, e) = (tid / 256, tid % 256):
+// base[r][e] = sum of hist[r'][e] for r' < r (the expert's pairs in earlier
+// runs), each thread summing one quarter of the runs (its loads in flight
+// together) and starting from the quarters before it.  counts[e] = the pairs
 // kept (capped at cap when cap > 0).  tile_off[e] = sum over e' < e of
 // ceil(counts[e'] / tile_rows).  active[0..n) = the experts with counts > 0,
 // ascending; active[E] = n.
-__global__ __launch_bounds__(MOE_MAX_EXPERTS) void dispatch_scan_kernel(
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(
     const int32_t* __restrict__ hist, int nrun, int E, int tile_rows, int cap,
     int32_t* __restrict__ base, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ tile_off, int32_t* __restrict__ active) {
+  __shared__ int32_t qs[4][MOE_MAX_EXPERTS];  // per-quarter sums
   __shared__ int32_t sc[MOE_MAX_EXPERTS];
-  const int e = threadIdx.x;
-  int run = 0;
+  __shared__ int32_t off_l[MOE_MAX_EXPERTS + 1];
+  const int tid = threadIdx.x, q = tid >> 8, e = tid & 255;
+  const int rq = (nrun + 3) / 4;  // runs per quarter
+  const int r_beg = q * rq, r_end = min(nrun, r_beg + rq);
+  int sum = 0;
   if (e < E) {
-    // runs in groups of 16 whose loads are all in flight together
-    for (int r0 = 0; r0 < nrun; r0 += 16) {
+    for (int r0 = r_beg; r0 < r_end; r0 += 16) {
       int h[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) h[j] = r0 + j < nrun ? hist[(size_t)(r0 + j) * E + e] : 0;
+      for (int j = 0; j < 16; ++j) h[j] = r0 + j < r_end ? hist[(size_t)(r0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sum += h[j];
+    }
+  }
+  qs[q][e] = sum;
+  __syncthreads();
+  if (e < E) {
+    int run = 0;
+    for (int p = 0; p < q; ++p) run += qs[p][e];
+    for (int r0 = r_beg; r0 < r_end; r0 += 16) {
+      int h[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) h[j] = r0 + j < r_end ? hist[(size_t)(r0 + j) * E + e] : 0;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        if (r0 + j < nrun) base[(size_t)(r0 + j) * E + e] = run;
+        if (r0 + j < r_end) base[(size_t)(r0 + j) * E + e] = run;
         run += h[j];
       }
     }
-    if (cap > 0 && run > cap) run = cap;
-    counts[e] = run;
-  }
-  sc[e] = (e < E) ? run : 0;
-  __syncthreads();
-  if (e == 0) {
-    int o = 0, t = 0, n = 0;
-    for (int i = 0; i < E; ++i) {
-      offsets[i] = o;
-      tile_off[i] = t;
-      o += sc[i];
-      t += (sc[i] + tile_rows - 1) / tile_rows;
-      if (sc[i] > 0) active[n++] = i;
+    if (q == 0) {
+      int tot = qs[0][e] + qs[1][e] + qs[2][e] + qs[3][e];
+      if (cap > 0 && tot > cap) tot = cap;
+      counts[e] = tot;
+      sc[e] = tot;
     }
-    offsets[E] = o;
-    tile_off[E] = t;
-    active[E] = n;
   }
+  __syncthreads();
+  expert_prefix(sc, E, tile_rows, offsets, tile_off, active, off_l);
 }
 
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
@@ -177,26 +246,10 @@ __global__ __launch_bounds__(1024) void dispatch_one_kernel(
       run += h;
     }
     tot[tid] = (cap > 0 && run > cap) ? cap : run;
+    counts[tid] = tot[tid];
   }
   __syncthreads();
-  if (tid == 0) {
-    int o = 0, t = 0, n = 0;
-    for (int e = 0; e < E; ++e) {
-      const int c = tot[e];
-      off_l[e] = o;
-      offsets[e] = o;
-      counts[e] = c;
-      tile_off[e] = t;
-      o += c;
-      t += (c + tile_rows - 1) / tile_rows;
-      if (c > 0) active[n++] = e;
-    }
-    off_l[E] = o;
-    offsets[E] = o;
-    tile_off[E] = t;
-    active[E] = n;
-  }
-  __syncthreads();
+  expert_prefix(tot, E, tile_rows, offsets, tile_off, active, off_l);
   for (int sl = tid; sl < S; sl += 1024) {
     const int e = idx_l[sl];
     const int g = wh[sl / SW][e] + rank_l[sl];  // rank of the pair in its expert
@@ -231,7 +284,7 @@ int launch_dispatch(const DispatchArgs& a, hipStream_t st) {
   int nbits = 0;
   while ((1 << nbits) < a.E) ++nbits;
   dispatch_hist_kernel<<<nrun, 64, 0, st>>>(a.idx, S, a.E, nbits, a.hist, a.rank);
-  dispatch_scan_kernel<<<1, MOE_MAX_EXPERTS, 0, st>>>(a.hist, nrun, a.E, a.tile_rows,
+  dispatch_scan_kernel<<<1, 1024, 0, st>>>(a.hist, nrun, a.E, a.tile_rows,
                                                       a.capacity, a.base, a.counts, a.offsets,
                                                       a.tile_off, a.active);
   dispatch_scatter_kernel<<<(S + 255) / 256, 256, 0, st>>>(a.idx, a.rank, a.base, a.offsets, S,

@@ -309,6 +309,82 @@ __global__ __launch_bounds__(256) void router_partial_kernel(
   }
 }
 
+// The same partial logits for many experts (E > 32): the transposed router
+// chunk of 128 hidden units is staged in LDS once per workgroup and shared by
+// its 4 waves (read straight from L2 every wave would fetch it four times),
+// double-buffered with the next chunk's loads in flight during the MFMAs.
+template <int NT>
+__global__ __launch_bounds__(256) void router_partial_lds_kernel(
+    const uint16_t* __restrict__ x, int T, int H, int E, const uint16_t* __restrict__ wrt,
+    int hslice, float* __restrict__ part) {
+  constexpr int CH = 128;      // hidden units per chunk
+  constexpr int LW = CH + 8;   // LDS row pitch (bf16): 16 rows of one read hit 16 bank groups
+  constexpr int NE = NT * 16;  // router rows staged (rows >= E are zeros)
+  __shared__ __attribute__((aligned(16))) uint16_t wl[2][NE * LW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tile0 = blockIdx.x * RT_TOK;
+  const int hb = blockIdx.y * hslice;
+  f32x4 acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int my_tok = tile0 + wave * 16 + (lane & 15);
+  const bool tok_ok = my_tok < T;
+  const int kq = (lane >> 4) * 8;
+  const uint16_t* xrow = x + (size_t)(tok_ok ? my_tok : 0) * H + hb + kq;
+  // staging: NE rows x 16 pieces of 16 bytes, NT pieces per thread
+  u32x4 r[NT];
+  auto stage_load = [&](int h) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int pc = tid + i * 256, row = pc >> 4, c = pc & 15;
+      r[i] = (row < E && h + c * 8 < hslice) ? ldg16(wrt + (size_t)row * H + hb + h + c * 8)
+                                             : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto stage_store = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int pc = tid + i * 256, row = pc >> 4, c = pc & 15;
+      *reinterpret_cast<u32x4*>(&wl[b][row * LW + c * 8]) = r[i];
+    }
+  };
+  stage_load(0);
+  stage_store(0);
+  __syncthreads();
+  int b = 0;
+  for (int h = 0; h < hslice; h += CH) {
+    const bool more = h + CH < hslice;
+    if (more) stage_load(h + CH);
+    u32x4 av[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      av[s] = (tok_ok && h + s * 32 < hslice) ? ldg16(xrow + h + s * 32) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      if (h + s * 32 < hslice)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const u32x4 bv =
+              *reinterpret_cast<const u32x4*>(&wl[b][(n * 16 + (lane & 15)) * LW + s * 32 + kq]);
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[s]), as_bf16x8(bv), acc[n],
+                                                           0, 0, 0);
+        }
+    if (more) stage_store(b ^ 1);  // its readers finished at the previous barrier
+    __syncthreads();
+    b ^= 1;
+  }
+  float* out = part + (size_t)blockIdx.y * T * E;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int e = n * 16 + (lane & 15);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = tile0 + wave * 16 + (lane >> 4) * 4 + j;
+      if (e < E && t < T) out[(size_t)t * E + e] = acc[n][j];
+    }
+  }
+}
+
 // Sum of the partial logits in split order (+ bias), then top-k and softmax.
 // nsplit == 0: `part` holds caller-given logits [T][E], used as they are.
 // RK_TOK tokens per workgroup, one per wave: the selection is a chain of
@@ -752,11 +828,11 @@ int launch_router(const RouterArgs& a, hipStream_t st) {
   else if (nt <= 2)
     router_partial_kernel<2><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, wt, hs, a.part);
   else if (nt <= 4)
-    router_partial_kernel<4><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, wt, hs, a.part);
+    router_partial_lds_kernel<4><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, wt, hs, a.part);
   else if (nt <= 8)
-    router_partial_kernel<8><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, wt, hs, a.part);
+    router_partial_lds_kernel<8><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, wt, hs, a.part);
   else
-    router_partial_kernel<16><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, wt, hs, a.part);
+    router_partial_lds_kernel<16><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, wt, hs, a.part);
   router_topk_kernel<<<kgrid, 256, 0, st>>>(a.part, ns, a.T, a.E, a.k, a.raw_gate, a.bias, a.idx,
                                             a.w);
   return hipGetLastError() == hipSuccess ? 0 : -1;
