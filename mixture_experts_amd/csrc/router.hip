@@ -32,10 +32,34 @@ struct Cand {
 };
 
 __device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
-  if (a.e == INT32_MAX) return false;
-  if (b.e == INT32_MAX) return true;
-  return a.v > b.v || (a.v == b.v && a.e < b.e);
+  // a is a candidate and either b is none or a beats it: larger value, or the
+  // same value and the lower index (bitwise operators: no branches)
+  return (a.e != INT32_MAX) &
+         ((b.e == INT32_MAX) | (a.v > b.v) | ((a.v == b.v) & (a.e < b.e)));
 }
+
+// The best candidate of the wave, in every lane: row-local steps (DPP
+// row_shr 1, 2, 4, 8 leave each row's best in its lane 15), then rows 0-1 and
+// 2-3 (row_bcast 15), then all four (row_bcast 31) into lane 63, read back as
+// a uniform value.  A lane whose DPP source lies outside its row, or whose row
+// is masked off, keeps its own candidate.  "better" is a total order on the
+// candidates, so the result does not depend on the reduction's shape.
+__device__ __forceinline__ Cand dpp_best_step(Cand c, Cand o) { return better(o, c) ? o : c; }
+#define DPP_CAND(c, ctrl, rmask)                                                                  \
+  Cand{__int_as_float(__builtin_amdgcn_update_dpp(__float_as_int((c).v), __float_as_int((c).v), \
+                                                  ctrl, rmask, 0xF, false)),                    \
+       __builtin_amdgcn_update_dpp((c).e, (c).e, ctrl, rmask, 0xF, false)}
+__device__ __forceinline__ Cand wave_best(Cand c) {
+  c = dpp_best_step(c, DPP_CAND(c, 0x111, 0xF));  // row_shr:1
+  c = dpp_best_step(c, DPP_CAND(c, 0x112, 0xF));  // row_shr:2
+  c = dpp_best_step(c, DPP_CAND(c, 0x114, 0xF));  // row_shr:4
+  c = dpp_best_step(c, DPP_CAND(c, 0x118, 0xF));  // row_shr:8
+  c = dpp_best_step(c, DPP_CAND(c, 0x142, 0xA));  // row_bcast:15 into rows 1, 3
+  c = dpp_best_step(c, DPP_CAND(c, 0x143, 0xC));  // row_bcast:31 into rows 2, 3
+  return Cand{__int_as_float(__builtin_amdgcn_readlane(__float_as_int(c.v), 63)),
+              __builtin_amdgcn_readlane(c.e, 63)};
+}
+#undef DPP_CAND
 
 // Top-k + softmax of tokens tile0 + wave, tile0 + wave + nwaves, ... below
 // tile0 + rows (interleaved so that small batches still spread over the
@@ -70,28 +94,27 @@ __device__ void topk_rows(const float* lg, int ldl, int tile0, int T, int E, int
         Cand cand{v[c], (avail >> c & 1u) ? lane + 64 * c : INT32_MAX};
         if (better(cand, best)) best = cand;
       }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        Cand o{__shfl_xor(best.v, off), __shfl_xor(best.e, off)};
-        if (better(o, best)) best = o;
-      }
+      best = wave_best(best);
       sel_v[j] = best.v;
       sel_e[j] = best.e;
       if ((best.e & 63) == lane) avail &= ~(1u << (best.e >> 6));
     }
-    // softmax over the k selected logits, in double (raw gate: the logits)
+    // softmax over the k selected logits, in double (raw gate: the logits):
+    // lane j < k evaluates pick j's exponential, z adds them in pick order
     const double m = (double)sel_v[0];
-    double z = 0.0;
-    double num = 0.0;
-    float vj = 0.0f;
-    int ej = 0;
+    float vj = sel_v[0];
+    int ej = sel_e[0];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j >= k) continue;
-      const double ex = raw ? 0.0 : exp((double)sel_v[j] - m);
-      z += ex;
-      if (j == lane) { num = ex; ej = sel_e[j]; vj = sel_v[j]; }
-    }
+    for (int j = 1; j < 8; ++j)
+      if (j < k && j == lane) {
+        vj = sel_v[j];
+        ej = sel_e[j];
+      }
+    const double num = (!raw && lane < k) ? exp((double)vj - m) : 0.0;
+    double z = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < k) z += __shfl(num, j);
     if (lane < k) {
       idx_out[(size_t)t * k + lane] = ej;
       w_out[(size_t)t * k + lane] = raw ? vj : (float)(num / z);
