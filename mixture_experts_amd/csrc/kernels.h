@@ -32,6 +32,9 @@ struct RouterArgs {
   // then not read)
   const float* hres = nullptr;
   uint16_t* xt_out = nullptr;
+  // uint8 expert layers on that route: the expert input [T][H] as fp16 (the
+  // route writes it; no separate conversion)
+  uint16_t* x16_out = nullptr;
 };
 
 struct DispatchArgs {
@@ -82,6 +85,8 @@ int launch_route_small(const RouterArgs& a, const DispatchArgs& d, int32_t* coun
                        hipStream_t st);
 // whether launch_route_small can form the prenorm branch input itself
 bool route_small_folds_prenorm(int T, int H, int E);
+// whether launch_route_small can write the fp16 copy of the expert input
+bool route_small_writes_x16(int T, int H, int E);
 int launch_dispatch(const DispatchArgs& a, hipStream_t st);
 
 // compute units of the current device (cached per device)

@@ -298,6 +298,9 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
   // when it runs in one workgroup per 16 tokens; otherwise a kernel of its own
   const bool fold_pn = prenorm && small_route(L, T, nullptr) &&
                        route_small_folds_prenorm(T, d.hidden, d.num_experts);
+  // uint8 layers: the same route writes the fp16 expert input
+  const bool fold_x16 = d.expert_format == MOE_EXPERT_U8 && small_route(L, T, nullptr) &&
+                        route_small_writes_x16(T, d.hidden, d.num_experts);
   if (prenorm) {
     if (!fold_pn && launch_prenorm((const float*)x, T, d.hidden, L->xt, st))
       return MOE_ERR_DEVICE;
@@ -316,6 +319,7 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
       ra.hres = (const float*)x;
       ra.xt_out = L->xt;
     }
+    if (fold_x16) ra.x16_out = L->x16;
     if (small_route(L, T, nullptr)) {  // one launch: the dispatch stage is empty
       if (launch_route_small(ra, da, L->sync, st)) return MOE_ERR_DEVICE;
       if (!mark(MOE_STAGE_DISPATCH)) return MOE_ERR_DEVICE;
@@ -350,7 +354,9 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
   }
   if (!mark(MOE_STAGE_GATE_UP)) return MOE_ERR_DEVICE;
   if (ea.u8) {  // the uint8 kernels take fp16 token operands
-    if (launch_to_f16((const uint16_t*)xin, (size_t)T * d.hidden, L->x16, st)) return MOE_ERR_DEVICE;
+    if (!fold_x16 &&
+        launch_to_f16((const uint16_t*)xin, (size_t)T * d.hidden, L->x16, st))
+      return MOE_ERR_DEVICE;
     ea.x = L->x16;
   }
   int r1 = f32 ? launch_f32_gate_up(ea, st)

@@ -628,7 +628,7 @@ __global__ __launch_bounds__(1024) void route_one_kernel(
     int32_t* __restrict__ counter, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off,
     int32_t* __restrict__ active, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
-    const float* __restrict__ hres, uint16_t* __restrict__ xt_out) {
+    const float* __restrict__ hres, uint16_t* __restrict__ xt_out, uint16_t* __restrict__ x16_out) {
   static_assert(!MULTI || MB == 1, "one token block per workgroup");
   static_assert(!PN || MB == 1, "prenorm: one token block per workgroup");
   const int tok0 = MULTI ? (int)blockIdx.x * 16 : 0;  // this workgroup's first token
@@ -638,6 +638,7 @@ __global__ __launch_bounds__(1024) void route_one_kernel(
     hres += (size_t)tok0 * H;
     xt_out += (size_t)tok0 * H;
   }
+  if (x16_out) x16_out += (size_t)tok0 * H;
   // the staged router, later the 16 partial logit tiles [16][RT_TOK][17]
   __shared__ __attribute__((aligned(16))) uint16_t wt[16 * R1_LDW];
   __shared__ float lg[RT_TOK * 17];
@@ -754,6 +755,24 @@ __global__ __launch_bounds__(1024) void route_one_kernel(
           *reinterpret_cast<u32x4*>(xt_out + (size_t)r16 * H + hb + s * 32 + kg * 8) = xa[0][s];
       }
   }
+  // uint8 expert layers take the expert input in fp16: this lane's operand
+  // values as fp16 (exact in fp16's normal range), one 16-byte store each
+  if (x16_out && r16 < T) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      if (s < nks) {
+        const u32x4 v = xa[0][s];
+        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          o[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(
+                                                  __uint_as_float(d[j] << 16),
+                                                  __uint_as_float(d[j] & 0xFFFF0000u)));
+        *reinterpret_cast<u32x4*>(x16_out + (size_t)r16 * H + hb + s * 32 + kg * 8) =
+            u32x4{o[0], o[1], o[2], o[3]};
+      }
+  }
 
   f32x4 acc[MB];
 #pragma unroll
@@ -867,14 +886,20 @@ bool route_small_folds_prenorm(int T, int H, int E) {
   return E <= 16 && H <= R1_HMAX && H % 512 == 0 && T <= 16;
 }
 
+bool route_small_writes_x16(int T, int H, int E) {
+  return E <= 16 && H <= R1_HMAX && H % 512 == 0 && T <= RT_TOK;
+}
+
 int launch_route_small(const RouterArgs& a, const DispatchArgs& d, int32_t* counter,
                        hipStream_t st) {
-  if (a.hres && !route_small_folds_prenorm(a.T, a.H, a.E)) return -1;
+  if ((a.hres && !route_small_folds_prenorm(a.T, a.H, a.E)) ||
+      (a.x16_out && !route_small_writes_x16(a.T, a.H, a.E)))
+    return -1;
   if (a.E <= 16 && a.H <= R1_HMAX && a.H % 512 == 0 && a.T <= RT_TOK) {
     auto* xx = (const uint16_t*)a.x;
     auto* ww = (const uint16_t*)a.wr;
 #define R1_ARGS xx, a.T, a.H, a.E, a.k, a.raw_gate, ww, a.bias, d.tile_rows, d.capacity, counter, a.idx, \
-                a.w, d.counts, d.offsets, d.tile_off, d.active, d.perm, d.inv, a.hres, a.xt_out
+                a.w, d.counts, d.offsets, d.tile_off, d.active, d.perm, d.inv, a.hres, a.xt_out, a.x16_out
     const int mb = (a.T + 15) / 16;
     // one workgroup up to 16 tokens, one per 16 tokens beyond
 #define R1_MB(EV, PN)                                                                \
