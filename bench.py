@@ -276,7 +276,7 @@ def bench_stack(K, W, u8=False, batches=DECODE_BATCHES):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr, flush=True)
         sys.exit(2)
     batches = tuple(int(b) for b in args.decode_batches.split(","))
