@@ -44,7 +44,10 @@ def f32_shape(E, k, H=8, F=8):
 
 @pytest.mark.parametrize("E,k,T", [(8, 2, 1), (8, 2, 64), (8, 2, 65), (3, 3, 100), (17, 4, 333),
                                    (64, 2, 1000), (128, 4, 2500), (200, 8, 129), (256, 8, 700),
-                                   (1, 1, 40), (256, 1, 3)])
+                                   (1, 1, 40), (256, 1, 3),
+                                   # 8192 pairs: the one-workgroup dispatch at its largest;
+                                   # 8194: the three dispatch kernels
+                                   (256, 8, 1024), (16, 2, 4097)])
 def test_route_given_logits_bit_exact(E, k, T):
     _log("route given logits", E, k, T)
     rng = np.random.default_rng(E * 1000 + T)
@@ -271,9 +274,11 @@ def test_grouped_path_matches_stream_path_on_every_row(name, shape, T):
 
 
 @pytest.mark.parametrize("E,k,T,cap", [(8, 2, 300, 40), (8, 2, 1000, 100), (64, 2, 777, 10),
-                                       (3, 3, 100, 1), (128, 4, 2500, 60), (8, 2, 20, 100)])
+                                       (3, 3, 100, 1), (128, 4, 2500, 60), (8, 2, 20, 100),
+                                       (256, 8, 1024, 20), (16, 2, 4097, 300)])
 def test_route_capacity_given_logits_bit_exact(E, k, T, cap):
-    """Capacity on the multi-run dispatch kernels: counts capped, the first
+    """Capacity on the dispatch kernels (one workgroup up to 8192 pairs, the
+    multi-run kernels beyond): counts capped, the first
     pairs of each expert in slot order kept, dropped pairs inv = -1, perm -1
     beyond the kept pairs; bit-exact against the oracle."""
     _log("route capacity", E, k, T, cap)
