@@ -830,6 +830,134 @@ __global__ __launch_bounds__(1024) void route_one_kernel(
                  tile_off, active, perm, inv);
 }
 
+// Decode batches of up to 4 tokens (E = 8 or 16, H a multiple of 1024 up to
+// R1_HMAX): routing
+// and dispatch without matrix instructions or a staged router.  Thread i
+// holds hidden units i, i + 1024, ... of every token and of the router rows
+// (coalesced loads, all in flight at once), forms its partial logits in that
+// order, and each wave adds its lanes' partials with DPP steps (row shifts,
+// then row broadcasts: a fixed tree); the 16 wave sums are added in wave
+// order.  With hres (residual layers) the workgroup first forms the branch
+// input bf16(h / sqrt(mean h^2 + 1e-6)) the same way (squares, then the same
+// reductions) and writes it for the expert kernels; with x16_out it writes
+// the fp16 copy of the expert input.  Top-k and dispatch as in route_one.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+#define DPP_ADD(ctrl, rmask) \
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, rmask, 0xF, false))
+  DPP_ADD(0x111, 0xF);  // row_shr:1
+  DPP_ADD(0x112, 0xF);  // row_shr:2
+  DPP_ADD(0x114, 0xF);  // row_shr:4
+  DPP_ADD(0x118, 0xF);  // row_shr:8: lane 15 of each row holds the row's sum
+  DPP_ADD(0x142, 0xA);  // row_bcast:15: lanes 31, 63 hold rows 0-1, 2-3
+  DPP_ADD(0x143, 0xC);  // row_bcast:31: lane 63 holds all four
+#undef DPP_ADD
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+template <int TT, int EV>  // tokens (at most), experts per router row (8 or 16)
+__global__ __launch_bounds__(1024) void route_tiny_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ hres, int T, int H, int E, int k,
+    int raw, const uint16_t* __restrict__ wr, const float* __restrict__ bias, int tile_rows,
+    int cap, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off,
+    int32_t* __restrict__ active, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+    uint16_t* __restrict__ xt_out, uint16_t* __restrict__ x16_out) {
+  constexpr int HPT = R1_HMAX / 1024;  // hidden units per thread, at most
+  __shared__ float red[16][TT * 16];  // per-wave partial logits
+  __shared__ float ssq[16][TT];
+  __shared__ float lg[16 * 17];        // [token][expert], row pitch 17
+  __shared__ int32_t idx_l[16 * MOE_MAX_TOPK];
+  __shared__ int32_t cnt[16];
+  __shared__ int32_t off_l[17];
+  __shared__ int32_t rank_l[16 * MOE_MAX_TOPK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hpt = H >> 10;
+  float xv[TT][HPT];
+  u32x4 wv[HPT][EV / 8];
+#pragma unroll
+  for (int i = 0; i < HPT; ++i)
+    if (i < hpt) {
+      const int h = tid + (i << 10);
+#pragma unroll
+      for (int q = 0; q < EV / 8; ++q)
+        wv[i][q] = ldg16(wr + (size_t)h * EV + q * 8);  // E == EV
+#pragma unroll
+      for (int t = 0; t < TT; ++t)
+        if (t < T) xv[t][i] = hres ? hres[(size_t)t * H + h] : bf16_to_f32(x[(size_t)t * H + h]);
+    }
+  if (hres) {  // branch input: the same reduction order for the squares
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int i = 0; i < HPT; ++i)
+        if (i < hpt && t < T) ss = fmaf(xv[t][i], xv[t][i], ss);
+      ss = wave_sum_dpp(ss);
+      if (lane == 0) ssq[wave][t] = ss;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      if (t >= T) continue;
+      float tot = 0.0f;
+      for (int w = 0; w < 16; ++w) tot += ssq[w][t];
+      const float ri = 1.0f / sqrtf(tot / (float)H + 1e-6f);
+#pragma unroll
+      for (int i = 0; i < HPT; ++i)
+        if (i < hpt) {
+          const __bf16 b = (__bf16)(xv[t][i] * ri);
+          xv[t][i] = (float)b;
+          xt_out[(size_t)t * H + tid + (i << 10)] = __builtin_bit_cast(uint16_t, b);
+        }
+    }
+  }
+  if (x16_out) {  // the expert input in fp16 (exact in fp16's normal range)
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+      for (int i = 0; i < HPT; ++i)
+        if (i < hpt && t < T) {
+          const auto f = __builtin_amdgcn_cvt_pkrtz(xv[t][i], 0.0f);
+          x16_out[(size_t)t * H + tid + (i << 10)] =
+              (uint16_t)(__builtin_bit_cast(uint32_t, f) & 0xFFFFu);
+        }
+  }
+  // partial logits of this thread's hidden units, in unit order
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    if (t >= T) continue;
+#pragma unroll
+    for (int e = 0; e < EV; ++e) {
+      if (e >= E) continue;
+      float acc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < HPT; ++i)
+        if (i < hpt) {
+          const uint32_t w2 = wv[i][e >> 3][(e & 7) >> 1];
+          const float wf = __uint_as_float((e & 1) ? (w2 & 0xFFFF0000u) : (w2 << 16));
+          acc = fmaf(xv[t][i], wf, acc);
+        }
+      acc = wave_sum_dpp(acc);
+      if (lane == 0) red[wave][t * 16 + e] = acc;
+    }
+  }
+  __syncthreads();
+  if (tid < T * 16) {  // waves added in order, then the bias
+    const int t = tid >> 4, e = tid & 15;
+    if (e < E) {
+      float sum = 0.0f;
+      for (int w = 0; w < 16; ++w) sum += red[w][t * 16 + e];
+      if (bias) sum += bias[e];
+      lg[t * 17 + e] = sum;
+    }
+  }
+  __syncthreads();
+  topk_rows16(lg, 17, 0, T, E, k, raw, idx_out, w_out, 16, idx_l, 16);
+  __syncthreads();
+  dispatch_small(idx_l, T * k, E, tile_rows, cap, cnt, off_l, rank_l, counts, offsets,
+                 tile_off, active, perm, inv);
+}
+
 }  // namespace
 
 int router_splits(int T, int H) {
@@ -895,6 +1023,22 @@ int launch_route_small(const RouterArgs& a, const DispatchArgs& d, int32_t* coun
   if ((a.hres && !route_small_folds_prenorm(a.T, a.H, a.E)) ||
       (a.x16_out && !route_small_writes_x16(a.T, a.H, a.E)))
     return -1;
+  if ((a.E == 8 || a.E == 16) && a.H <= R1_HMAX && a.H % 1024 == 0 && a.T <= 4) {
+    auto* xx = (const uint16_t*)a.x;
+    auto* ww = (const uint16_t*)a.wr;
+#define RT_ARGS xx, a.hres, a.T, a.H, a.E, a.k, a.raw_gate, ww, a.bias, d.tile_rows, d.capacity, \
+                a.idx, a.w, d.counts, d.offsets, d.tile_off, d.active, d.perm, d.inv, a.xt_out, a.x16_out
+    // a router row is one (E = 8) or two (E = 16) 16-byte loads
+    if (a.T <= 1) {
+      if (a.E == 8) route_tiny_kernel<1, 8><<<1, 1024, 0, st>>>(RT_ARGS);
+      else route_tiny_kernel<1, 16><<<1, 1024, 0, st>>>(RT_ARGS);
+    } else {
+      if (a.E == 8) route_tiny_kernel<4, 8><<<1, 1024, 0, st>>>(RT_ARGS);
+      else route_tiny_kernel<4, 16><<<1, 1024, 0, st>>>(RT_ARGS);
+    }
+#undef RT_ARGS
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
   if (a.E <= 16 && a.H <= R1_HMAX && a.H % 512 == 0 && a.T <= RT_TOK) {
     auto* xx = (const uint16_t*)a.x;
     auto* ww = (const uint16_t*)a.wr;
