@@ -830,8 +830,8 @@ __global__ __launch_bounds__(1024) void route_one_kernel(
                  tile_off, active, perm, inv);
 }
 
-// Decode batches of up to 4 tokens (E = 8 or 16, H a multiple of 1024 up to
-// R1_HMAX): routing
+// Single-token decode (E = 8 or 16, H a multiple of 1024 up to R1_HMAX; the
+// kernel takes up to TT tokens): routing
 // and dispatch without matrix instructions or a staged router.  Thread i
 // holds hidden units i, i + 1024, ... of every token and of the router rows
 // (coalesced loads, all in flight at once), forms its partial logits in that
@@ -1023,19 +1023,15 @@ int launch_route_small(const RouterArgs& a, const DispatchArgs& d, int32_t* coun
   if ((a.hres && !route_small_folds_prenorm(a.T, a.H, a.E)) ||
       (a.x16_out && !route_small_writes_x16(a.T, a.H, a.E)))
     return -1;
-  if ((a.E == 8 || a.E == 16) && a.H <= R1_HMAX && a.H % 1024 == 0 && a.T <= 4) {
+  // (at T = 4 the one-token-per-row MFMA route below is the faster one)
+  if ((a.E == 8 || a.E == 16) && a.H <= R1_HMAX && a.H % 1024 == 0 && a.T == 1) {
     auto* xx = (const uint16_t*)a.x;
     auto* ww = (const uint16_t*)a.wr;
 #define RT_ARGS xx, a.hres, a.T, a.H, a.E, a.k, a.raw_gate, ww, a.bias, d.tile_rows, d.capacity, \
                 a.idx, a.w, d.counts, d.offsets, d.tile_off, d.active, d.perm, d.inv, a.xt_out, a.x16_out
     // a router row is one (E = 8) or two (E = 16) 16-byte loads
-    if (a.T <= 1) {
-      if (a.E == 8) route_tiny_kernel<1, 8><<<1, 1024, 0, st>>>(RT_ARGS);
-      else route_tiny_kernel<1, 16><<<1, 1024, 0, st>>>(RT_ARGS);
-    } else {
-      if (a.E == 8) route_tiny_kernel<4, 8><<<1, 1024, 0, st>>>(RT_ARGS);
-      else route_tiny_kernel<4, 16><<<1, 1024, 0, st>>>(RT_ARGS);
-    }
+    if (a.E == 8) route_tiny_kernel<1, 8><<<1, 1024, 0, st>>>(RT_ARGS);
+    else route_tiny_kernel<1, 16><<<1, 1024, 0, st>>>(RT_ARGS);
 #undef RT_ARGS
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }

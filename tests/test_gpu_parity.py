@@ -122,9 +122,10 @@ SMALL = [
     ("bf16", 256, 640, 16, 4, 300, moe.MOE_FLAG_PATH_GROUPED),
     ("bf16", 768, 256, 3, 1, 1100, 0),
     ("bf16", 256, 128, 64, 8, 97, 0),
-    # the tiny-batch route (T <= 4, E = 8 or 16, H % 1024 == 0)
-    ("bf16", 1024, 256, 16, 4, 3, 0),
+    # the single-token route (T = 1, E = 8 or 16, H % 1024 == 0)
+    ("bf16", 1024, 256, 16, 4, 1, 0),
     ("bf16", 4096, 128, 8, 2, 1, 0),
+    ("bf16", 2048, 128, 8, 2, 1, moe.MOE_FLAG_GATE_RAW),
     ("bf16", 2048, 128, 8, 2, 4, moe.MOE_FLAG_GATE_RAW),
     # raw-logit gates: fp32 router, each bf16 router kernel, both expert paths
     ("f32", 64, 128, 8, 2, 32, moe.MOE_FLAG_GATE_RAW),
@@ -305,7 +306,7 @@ CAP_CASES = [
     ("bf16", 256, 128, 64, 8, 60, 3, 0),                             # split-H small routing, stream
     ("bf16", 512, 384, 4, 2, 700, 200, moe.MOE_FLAG_PATH_GROUPED),   # dispatch kernels, grouped
     ("bf16", 512, 384, 4, 2, 700, 200, moe.MOE_FLAG_PATH_STREAM),    # dispatch kernels, stream
-    ("bf16", 1024, 256, 8, 2, 4, 1, 0),                              # tiny-batch route, stream
+    ("bf16", 1024, 256, 8, 2, 4, 1, 0),                              # one-workgroup route, T = 4
     ("f32", 64, 128, 8, 2, 32, 4, 0),
 ]
 
