@@ -24,7 +24,7 @@ struct RouterArgs {
   const float* logits_in; // [T][E] or null
   int32_t* idx;           // [T][k]
   float* w;               // [T][k]
-  float* part;            // [router_splits(T, H)][T][E] partial logits (bf16 layers)
+  float* part;            // [router_splits(T, H, E)][T][E] partial logits (bf16 layers)
   uint16_t* wrt;          // [E][H] workspace for the transposed router (bf16 layers)
   int raw_gate;           // 1: gate weights = the selected logits (no softmax)
   // residual layers on the one-workgroup small-batch route: the fp32 stream
@@ -76,7 +76,7 @@ struct ExpertArgs {
   float* cy = nullptr;
 };
 
-int router_splits(int T, int H);
+int router_splits(int T, int H, int E);
 int launch_router(const RouterArgs& a, hipStream_t st);
 int launch_prenorm(const float* h, int T, int H, uint16_t* xt, hipStream_t st);
 // bf16 routing + dispatch in one launch for T <= 64 (counter: zeroed int32,

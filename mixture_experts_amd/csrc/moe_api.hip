@@ -117,7 +117,7 @@ void carve(moe_layer* L, Arena& A) {
   if (d.dtype == MOE_BF16) {
     for (int tiles = 1; (tiles - 1) * 64 < d.max_tokens; ++tiles) {
       const int T = tiles * 64 < d.max_tokens ? tiles * 64 : d.max_tokens;
-      const size_t need = (size_t)router_splits(T, d.hidden) * T * E * 4;
+      const size_t need = (size_t)router_splits(T, d.hidden, E) * T * E * 4;
       if (need > part) part = need;
     }
   }

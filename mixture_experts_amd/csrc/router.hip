@@ -960,9 +960,12 @@ __global__ __launch_bounds__(1024) void route_tiny_kernel(
 
 }  // namespace
 
-int router_splits(int T, int H) {
+int router_splits(int T, int H, int E) {
   const int ntt = (T + RT_TOK - 1) / RT_TOK;
-  int ns = (512 + ntt - 1) / ntt;          // aim at >= 512 workgroups
+  // aim at >= 2048 workgroups when a workgroup's router share is small
+  // (E <= 16: the tokens dominate its loads), else >= 512
+  const int aim = E <= 16 ? 2048 : 512;
+  int ns = (aim + ntt - 1) / ntt;
   int max_ns = H / 256;                    // slices of at least 256
   if (max_ns > RT_MAX_SPLITS) max_ns = RT_MAX_SPLITS;
   if (ns > max_ns) ns = max_ns;
@@ -985,7 +988,7 @@ int launch_router(const RouterArgs& a, hipStream_t st) {
                                               a.w);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
-  const int ns = router_splits(a.T, a.H);
+  const int ns = router_splits(a.T, a.H, a.E);
   const int hs = a.H / ns;
   const dim3 g2(grid, ns);
   const int nt = (a.E + 15) / 16;
@@ -1056,7 +1059,7 @@ int launch_route_small(const RouterArgs& a, const DispatchArgs& d, int32_t* coun
 #undef R1_ARGS
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
-  const int ns = router_splits(a.T, a.H);
+  const int ns = router_splits(a.T, a.H, a.E);
   const int hs = a.H / ns;
   const int nt = (a.E + 15) / 16;
   auto* xx = (const uint16_t*)a.x;
