@@ -30,7 +30,8 @@
 // codes becomes two fp16 pairs by a byte permute with 0x64 (fp16 1024 + q)
 // and one packed fp16 add of -(1024 + zero), exactly (q - zero).  The token
 // rows arrive in fp16: the layer input is copied to fp16 before the gate/up
-// kernel, whose epilogue stores the bf16-rounded activation as fp16 (bf16
+// kernel (by the small-batch route itself, else by a conversion kernel), and
+// that kernel's epilogue stores the bf16-rounded activation as fp16 (bf16
 // values in fp16's normal range are fp16 values).  The MFMA is
 // v_mfma_f32_16x16x32_f16 and the scale multiplies the reduced sums once
 // per output.

@@ -6,16 +6,17 @@
 // (equal logits: lower expert index first) and a softmax over those k
 // [www.lmnt.cn/news/246575 sec. 2.2, route_tokens].
 //
-// bf16 layers: a first kernel computes partial logits of 64-token tiles over
-// slices of the hidden dimension (split so that even one token fills several
-// hundred workgroups) with v_mfma_f32_16x16x32_bf16 (tokens as the A operand,
-// the router slice staged transposed in LDS as the B operand, fp32
-// accumulation); a second kernel adds the slices in a fixed order (+ bias).
-// fp32 layers use one plain-FMA kernel.  The logits tile of 64 tokens sits in
-// LDS; each wave selects the top-k of its 16 tokens, one token at a time,
-// with the experts spread over the 64 lanes and a butterfly max-reduction
-// over (value desc, index asc).  The softmax over the k picks is evaluated in
-// fp64.
+// bf16 layers, batches beyond 64 tokens: the router is transposed once per
+// call; a first kernel computes partial logits of 64-token tiles over slices
+// of the hidden dimension (split so that the batch fills over a thousand
+// workgroups) with v_mfma_f32_16x16x32_bf16 (tokens as the A operand, the
+// transposed router as the B operand, read from L2 or, for many experts,
+// staged in LDS; fp32 accumulation); a second kernel adds the slices in a
+// fixed order (+ bias) and selects, one token per wave, with the experts
+// spread over the 64 lanes and a DPP max-reduction over (value desc, index
+// asc).  Batches of up to 64 tokens route and dispatch in one launch (the
+// one-workgroup kernels below).  fp32 layers use one plain-FMA kernel.  The
+// softmax over the k picks is evaluated in fp64.
 #include "common.h"
 #include "kernels.h"
 
