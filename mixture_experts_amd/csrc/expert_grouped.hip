@@ -30,7 +30,11 @@
 // tile lists on the device from the expert offsets (no host sync).  A
 // workgroup starts the first K steps of its next tile before it writes out
 // the current one, so tile boundaries cost little.  In a tile whose token
-// rows end early, waves skip the MFMAs of 32-row blocks past the end.
+// rows end early, waves skip the MFMAs of 32-row blocks past the end.  The
+// tiles of an XCD's last, partial round are cut along K into pieces run by
+// the workgroups that would otherwise idle; the pieces store fp32 partial
+// sums and a second, short launch adds them in piece order and writes those
+// tiles (no cross-workgroup waiting, and the same result on every call).
 #include "common.h"
 #include "kernels.h"
 
@@ -59,17 +63,159 @@ __device__ __forceinline__ int lds_slot(int row, int c) {
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0f70)
 #define GG_BARRIER() asm volatile("s_barrier" ::: "memory")
 
-// One tile: expert e, K slice ks, weight tile mt, token rows p0 .. p0+rows-1.
+// Tail split: the tiles that would leave most workgroups of an XCD idle in
+// its last round are cut along K into np pieces of at least kMinPiece steps.
+constexpr int kMaxPieces = 4;
+constexpr int kMinPiece = 16;
+constexpr int kPartFloats = 256 * 256;  // one piece's fp32 partial sums
+
+// One tile: expert e, K slice ks, weight tile mt, token rows p0 .. p0+rows-1,
+// K steps k0 .. k0+nk-1 of the slice.  np > 1: piece `piece` of np; the np
+// pieces of leftover tile l are taken by the workgroups l + p * nleft.
 struct Tile {
   int e, ks, mt, p0, rows;
+  int k0, nk, np, piece, l;
 };
+
+// Persistent schedule.  Tiles are numbered (K slice, weight group, expert,
+// token tile, weight tile), a weight group being a run of up to 8 weight
+// tiles; the tiles of one (K slice, weight group, expert) share weight rows
+// and token rows.  Each XCD (workgroup b runs on XCD b % 8) takes one
+// contiguous eighth of the numbering and its nw workgroups take those tiles
+// in turn, so tiles running together on an XCD share data in its L2, and
+// each XCD sees every expert, whatever the routing skew.  With split set,
+// the nleft tiles of a last, partial round are cut into np K pieces each
+// (np * nleft <= nw); each piece stores its fp32 partial sums and a second
+// launch adds the np partials in piece order and writes the tile.
+struct Plan {
+  int MW, ngpe, ntt, per_ks, nk_slice, q_beg, q_end, nfull, nleft, np;
+};
+
+__device__ Plan make_plan(bool gated, const int32_t* tile_off, int E, int H, int F, int ksplit,
+                          int xcd, int nw, bool split) {
+  Plan p;
+  p.MW = gated ? F / 128 : H / 256;  // weight tiles per expert
+  p.ngpe = (p.MW + kGroupW - 1) / kGroupW;
+  p.ntt = tile_off[E];               // token tiles over all experts
+  p.per_ks = p.ntt * p.MW;
+  p.nk_slice = (gated ? H : F) / ksplit / kBK;
+  const int ntiles = ksplit * p.per_ks;
+  p.q_beg = (int)(((int64_t)xcd * ntiles) >> 3);
+  p.q_end = (int)(((int64_t)(xcd + 1) * ntiles) >> 3);
+  p.nfull = (p.q_end - p.q_beg) / nw;
+  p.nleft = p.q_end - p.q_beg - p.nfull * nw;
+  p.np = 1;
+  if (split && p.nleft > 0)
+    p.np = max(1, min(min(nw / p.nleft, kMaxPieces), p.nk_slice / kMinPiece));
+  return p;
+}
+
+// Tile q of the numbering (whole K slice).
+__device__ void tile_at(const Plan& p, int q, const int32_t* tile_off, const int32_t* offsets,
+                        int E, Tile& t) {
+  const int ks = q / p.per_ks;
+  const int r = q - ks * p.per_ks;
+  const int fg = min(r / (p.ntt * kGroupW), p.ngpe - 1);
+  const int r2 = r - fg * p.ntt * kGroupW;
+  const int gsz = min(kGroupW, p.MW - fg * kGroupW);
+  const int u = r2 / gsz;  // token tile over all experts
+  const int e = upper_segment(tile_off, E, u);
+  t.e = e;
+  t.ks = ks;
+  t.mt = fg * kGroupW + (r2 - u * gsz);
+  t.p0 = offsets[e] + (u - tile_off[e]) * GG_BT;
+  t.rows = min(offsets[e + 1] - t.p0, GG_BT);
+  t.k0 = 0;
+  t.nk = p.nk_slice;
+  t.np = 1;
+  t.piece = 0;
+  t.l = 0;
+}
+
+// Output of one tile by the 4 waves of a workgroup.  Gate/up: lane (tcol,
+// rsub) of wave (wm, wn) holds 4 consecutive f for token tcol of each token
+// block and writes SiLU(g) * u as 8 bf16 bytes; the four waves together
+// write every 128-byte line of the tile's rows.  Down: the fp32 partial sums
+// go through the 64 KB of LDS at ob in four rounds, round j holding token
+// blocks 2j and 2j+1 as [64 tokens][256 h] 1 KB rows whose 16-byte chunks are
+// XOR-swizzled by the row (chunk c of row r at c ^ (r % 16)), written out as
+// 1 KB runs to plane t.ks.  get4(i, j, q) gives the lane's 4 sums of block
+// (i, j) at rows 8q + rsub; prep(j) runs before the blocks (., j) are read.
+// jsel >= 0: only the token blocks 2 jsel and 2 jsel + 1.
+template <bool GATED, class Prep, class Get>
+__device__ __forceinline__ void write_tile(const Tile& t, Prep prep, Get get4,
+                                           void* __restrict__ out, int F, int H, size_t plane,
+                                           uint8_t* ob, int wave, int jsel = -1) {
+  const int wm = wave & 1, wn = wave >> 1;
+  int tid;  // the thread id, opaque so that the addressing below is not kept live across tiles
+  asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
+  const int tcol = tid & 31;
+  const int rsub = 4 * ((tid >> 5) & 1);
+  if (GATED) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tl = (2 * j + wn) * 32 + tcol;
+      if (tl >= t.rows || (jsel >= 0 && j != jsel)) continue;
+      prep(j);
+      uint16_t* row = (uint16_t*)out + (size_t)(t.p0 + tl) * F + t.mt * 128 + wm * 64 + rsub;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 g = get4(i, j, q), u = get4(i + 2, j, q);
+          float o[4];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) o[jj] = silu_f32(g[jj]) * u[jj];
+          const bf16x2 lo = {(__bf16)o[0], (__bf16)o[1]}, hi = {(__bf16)o[2], (__bf16)o[3]};
+          uint2 pk;
+          pk.x = __builtin_bit_cast(uint32_t, lo);
+          pk.y = __builtin_bit_cast(uint32_t, hi);
+          *reinterpret_cast<uint2*>(row + 32 * i + 8 * q) = pk;
+        }
+    }
+  } else {
+    float* yp = (float*)out + (size_t)t.ks * plane;
+    const int c = tid & 63;
+    const int sr = wn * 32 + tcol;  // staging row of this lane's token
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (jsel >= 0 && j != jsel) continue;
+      if (j > 0) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      prep(j);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int hc = (wm * 128 + 32 * i + 8 * q + rsub) >> 2;
+          *reinterpret_cast<f32x4*>(ob + sr * 1024 + ((hc ^ (sr & 15)) << 4)) = get4(i, j, q);
+        }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll 4
+      for (int r0 = 0; r0 < 64; r0 += 4) {
+        const int row = r0 + (tid >> 6);
+        const int tl = (2 * j + (row >> 5)) * 32 + (row & 31);
+        if (tl < t.rows)
+          *reinterpret_cast<u32x4*>(yp + (size_t)(t.p0 + tl) * H + t.mt * 256 + ((c ^ (row & 15)) << 2)) =
+              *reinterpret_cast<const u32x4*>(ob + row * 1024 + (c << 4));
+      }
+    }
+  }
+}
+
+// A piece's partial sums, lane-major: wave, block (i, j), quad q, lane (the
+// lane id opaque, so that no address is formed before it is needed).
+__device__ __forceinline__ f32x4* part_base(float* ws, int slot, int wave) {
+  int ln;
+  asm volatile("v_and_b32 %0, 63, %1" : "=v"(ln) : "v"((int)threadIdx.x));
+  return reinterpret_cast<f32x4*>(ws + (size_t)slot * kPartFloats + wave * 16384) + ln;
+}
 
 template <bool GATED, int NS>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
     const uint16_t* __restrict__ experts, uint64_t stride_elems,
     const uint16_t* __restrict__ tok, const int32_t* __restrict__ perm, int k_top,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off, int E, int H,
-    int F, int T, int ksplit, size_t plane, void* __restrict__ out) {
+    int F, int T, int ksplit, size_t plane, void* __restrict__ out, float* __restrict__ ws) {
   // ring stage s at lds + s * kStage: [weight rows | token rows] x 256 x 4 chunks
   __shared__ u32x4 lds[GATED ? NS * kStage : kLdsDown];
   static_assert(GATED || (NS - 1) * kStage <= kStageOut, "LDS layout");
@@ -77,37 +223,26 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
   // ksplit > 1 (down projection only): the K range is cut into ksplit
   // slices, slice ks writes its partial sums to plane ks of the output.
   const int K = (GATED ? H : F) / ksplit;
-  const int nk = K / kBK;
-  const int MW = GATED ? F / 128 : H / 256;  // weight tiles per expert
-  const int ngpe = (MW + kGroupW - 1) / kGroupW;
-
-  // Persistent schedule.  Tiles are numbered (K slice, weight group, expert,
-  // token tile, weight tile), a weight group being a run of up to 8 weight
-  // tiles; the tiles of one (K slice, weight group, expert) share weight rows
-  // and token rows.  Each XCD (workgroup b runs on XCD b % 8) takes one
-  // contiguous eighth of the numbering and its workgroups take those tiles in
-  // turn, so tiles running together on an XCD share data in its L2, and each
-  // XCD sees every expert, whatever the routing skew.
   const int xcd = blockIdx.x & 7;
-  const int nw = gridDim.x >> 3;  // workgroups per XCD
-  const int ntt = tile_off[E];    // token tiles over all experts
-  const int per_ks = ntt * MW;
-  const int ntiles = ksplit * per_ks;
-  const int q_end = (int)(((int64_t)(xcd + 1) * ntiles) >> 3);
-  auto locate = [&](int q, Tile& t) -> bool {
-    if (q >= q_end) return false;
-    const int ks = q / per_ks;
-    const int r = q - ks * per_ks;
-    const int fg = min(r / (ntt * kGroupW), ngpe - 1);
-    const int r2 = r - fg * ntt * kGroupW;
-    const int gsz = min(kGroupW, MW - fg * kGroupW);
-    const int u = r2 / gsz;  // token tile over all experts
-    const int e = upper_segment(tile_off, E, u);
-    t.e = e;
-    t.ks = ks;
-    t.mt = fg * kGroupW + (r2 - u * gsz);
-    t.p0 = offsets[e] + (u - tile_off[e]) * GG_BT;
-    t.rows = min(offsets[e + 1] - t.p0, GG_BT);
+  const int nw = gridDim.x >> 3;   // workgroups per XCD
+  const int jw = blockIdx.x >> 3;  // this workgroup's place on its XCD
+  const Plan pl = make_plan(GATED, tile_off, E, H, F, ksplit, xcd, nw, ws != nullptr);
+  // work item w of this workgroup (rounds 0, 1, ...)
+  auto locate = [&](int w, Tile& t) -> bool {
+    if (pl.np < 2 || w < pl.nfull) {
+      const int q = pl.q_beg + jw + w * nw;
+      if (q >= pl.q_end) return false;
+      tile_at(pl, q, tile_off, offsets, E, t);
+      return true;
+    }
+    if (w > pl.nfull || jw >= pl.nleft * pl.np) return false;
+    const int l = jw % pl.nleft, piece = jw / pl.nleft;
+    tile_at(pl, pl.q_beg + pl.nfull * nw + l, tile_off, offsets, E, t);
+    t.l = l;
+    t.piece = piece;
+    t.np = pl.np;
+    t.k0 = piece * pl.nk_slice / pl.np;
+    t.nk = (piece + 1) * pl.nk_slice / pl.np - t.k0;
     return true;
   };
 
@@ -130,7 +265,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
   };
   auto set_tile = [&](const Tile& t, const int (&pv)[4]) {
     eb = experts + (size_t)stride_elems * t.e;
-    const int kbase = t.ks * K;
+    const int kbase = t.ks * K + t.k0 * kBK;
     int ln;  // the lane id, opaque as above
     asm volatile("v_and_b32 %0, 63, %1" : "=v"(ln) : "v"((int)threadIdx.x));
 #pragma unroll
@@ -162,8 +297,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
                  : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(src)
                  : "memory", "m0");
   };
-  // the first NS-1 K steps of a tile (ring stages 0 .. NS-2)
-  auto prologue = [&]() {
+  // the first NS-1 K steps of a tile of nk steps (ring stages 0 .. NS-2)
+  auto prologue = [&](int nk) {
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
       if (s < nk) {
@@ -177,7 +312,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
   // The K loop of one tile for a wave that computes its first NJ token
   // blocks (the others lie beyond the tile's rows).  Loads never depend on
   // NJ, so every wave keeps the same load and barrier sequence.
-  auto kloop = [&](auto NJc, f32x16 (&acc)[4][4]) {
+  auto kloop = [&](auto NJc, f32x16 (&acc)[4][4], int nk) {
     constexpr int NJ = decltype(NJc)::value;
     int ln;  // the lane id, opaque as above
     asm volatile("v_and_b32 %0, 63, %1" : "=v"(ln) : "v"((int)threadIdx.x));
@@ -248,83 +383,15 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
     for (; k < nk; ++k) step(k);
   };
 
-  // Output.  Gate/up, straight from the accumulators: lane (tcol, rsub) of
-  // wave (wm, wn) holds 4 consecutive f for token tcol of each token block
-  // and writes SiLU(g) * u as 8 bf16 bytes; the four waves together write
-  // every 128-byte line of the tile's rows.  Down: the fp32 partial sums go
-  // through LDS in four rounds, round j holding token blocks 2j and 2j+1 as
-  // [64 tokens][256 h] 1 KB rows whose 16-byte chunks are XOR-swizzled by
-  // the row (chunk c of row r at c ^ (r % 16)), written out as 1 KB runs.
-  auto epilogue = [&](const Tile& t, f32x16 (&acc)[4][4]) {
-    int tid;  // the thread id, opaque so that the addressing below is not kept live across tiles
-    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
-    const int tcol = tid & 31;
-    const int rsub = 4 * ((tid >> 5) & 1);
-    if (GATED) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tl = (2 * j + wn) * 32 + tcol;
-        if (tl >= t.rows) continue;
-        uint16_t* row = (uint16_t*)out + (size_t)(t.p0 + tl) * F + t.mt * 128 + wm * 64 + rsub;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float o[4];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              // read each accumulator where it is used: left to itself the
-              // compiler copies all of them to VGPRs at once and spills
-              float g, u;
-              asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(g) : "a"(acc[i][j][4 * q + jj]));
-              asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(u) : "a"(acc[i + 2][j][4 * q + jj]));
-              o[jj] = silu_f32(g) * u;
-            }
-            const bf16x2 lo = {(__bf16)o[0], (__bf16)o[1]}, hi = {(__bf16)o[2], (__bf16)o[3]};
-            uint2 pk;
-            pk.x = __builtin_bit_cast(uint32_t, lo);
-            pk.y = __builtin_bit_cast(uint32_t, hi);
-            *reinterpret_cast<uint2*>(row + 32 * i + 8 * q) = pk;
-          }
-      }
-    } else {
-      uint8_t* ob = (uint8_t*)&lds[kStageOut];
-      float* yp = (float*)out + (size_t)t.ks * plane;
-      const int c = tid & 63;
-      const int sr = wn * 32 + tcol;  // staging row of this lane's token
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (j > 0) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int hc = (wm * 128 + 32 * i + 8 * q + rsub) >> 2;
-            *reinterpret_cast<f32x4*>(ob + sr * 1024 + ((hc ^ (sr & 15)) << 4)) =
-                f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          }
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-#pragma unroll 4
-        for (int r0 = 0; r0 < 64; r0 += 4) {
-          const int row = r0 + (tid >> 6);
-          const int tl = (2 * j + (row >> 5)) * 32 + (row & 31);
-          if (tl < t.rows)
-            *reinterpret_cast<u32x4*>(yp + (size_t)(t.p0 + tl) * H + t.mt * 256 + ((c ^ (row & 15)) << 2)) =
-                *reinterpret_cast<const u32x4*>(ob + row * 1024 + (c << 4));
-        }
-      }
-    }
-  };
-
-  int q = (int)(((int64_t)xcd * ntiles) >> 3) + (int)(blockIdx.x >> 3);
+  int round = 0;
   Tile cur, nxt;
-  if (!locate(q, cur)) return;
+  if (!locate(round, cur)) return;
   {
     int pv[4];
     load_perm(cur, pv);
     set_tile(cur, pv);
   }
-  prologue();
+  prologue(cur.nk);
   // one tile for waves that compute NJ token blocks; returns whether a next
   // tile exists (then its first stages are in flight)
   auto tile = [&](auto NJc) -> bool {
@@ -337,18 +404,41 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
     // the next tile, located and its token rows looked up while this one
     // computes (those loads precede the K loop's and only strengthen its waits)
-    const bool more = locate(q + nw, nxt);
+    const bool more = locate(round + 1, nxt);
     int pn[4] = {0, 0, 0, 0};
     if (more) load_perm(nxt, pn);
-    kloop(NJc, acc);
+    kloop(NJc, acc, cur.nk);
     // every load of the tile has landed; end every wave's reads of the ring,
     // then start the next tile's first stages under this tile's epilogue
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (more) {
       set_tile(nxt, pn);
-      prologue();
+      prologue(nxt.nk);
     }
-    epilogue(cur, acc);
+    // read each accumulator where it is used: left to itself the compiler
+    // copies all of them to VGPRs at once and spills
+    auto from_acc = [&](int i, int j, int q) -> f32x4 {
+      f32x4 v;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float a;
+        asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(a) : "a"(acc[i][j][4 * q + u]));
+        v[u] = a;
+      }
+      return v;
+    };
+    if (cur.np < 2) {
+      write_tile<GATED>(cur, [](int) {}, from_acc, out, F, H, plane, (uint8_t*)&lds[kStageOut],
+                        wave);
+    } else {  // a piece: its partial sums, for the launch that finishes the tile
+      f32x4* dst = part_base(ws, xcd * nw + jw, wave);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) dst[((i * 4 + j) * 4 + q) * 64] = from_acc(i, j, q);
+    }
     return more;
   };
   for (;;) {
@@ -368,8 +458,52 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
     }
     if (!more) break;
     cur = nxt;
-    q += nw;
+    ++round;
   }
+}
+
+// The split tail tiles of a grouped_gemm_kernel launch: workgroup b finishes
+// token blocks 2 (b % 4) and 2 (b % 4) + 1 of leftover tile (b / 4) % nw of
+// XCD share b / (4 nw) (if there is one), adding the np pieces' partial sums
+// in piece order.
+template <bool GATED>
+__global__ __launch_bounds__(256) void grouped_fixup_kernel(
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off, int E, int H,
+    int F, int ksplit, size_t plane, void* __restrict__ out, float* __restrict__ ws, int nw) {
+  __shared__ u32x4 ob[GATED ? 1 : 64 * 1024 / 16];
+  const int jsel = blockIdx.x & 3, xcd = (blockIdx.x >> 2) / nw, l = (blockIdx.x >> 2) % nw;
+  const Plan pl = make_plan(GATED, tile_off, E, H, F, ksplit, xcd, nw, true);
+  if (pl.np < 2 || l >= pl.nleft) return;
+  Tile t;
+  tile_at(pl, pl.q_beg + pl.nfull * nw + l, tile_off, offsets, E, t);
+  if (64 * jsel >= t.rows) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const f32x4* src = part_base(ws, xcd * nw + l, wave);
+  const size_t pstep = (size_t)pl.nleft * kPartFloats / 4;  // between pieces
+  // the sums of token block column j, all loads of a column in flight at once
+  f32x4 col[4][4];
+  auto prep = [&](int j) {
+    f32x4 v[kMaxPieces][4][4];
+#pragma unroll
+    for (int p = 0; p < kMaxPieces; ++p)
+      if (p < pl.np)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[p][i][q] = src[p * pstep + ((i * 4 + j) * 4 + q) * 64];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 a = v[0][i][q];
+#pragma unroll
+        for (int p = 1; p < kMaxPieces; ++p)
+          if (p < pl.np) a += v[p][i][q];
+        col[i][q] = a;
+      }
+  };
+  write_tile<GATED>(t, prep, [&](int i, int, int q) -> f32x4 { return col[i][q]; }, out, F, H,
+                    plane, (uint8_t*)ob, wave, jsel);
 }
 
 // One workgroup per compute unit, a multiple of 8 (one share per XCD).
@@ -379,6 +513,8 @@ int persistent_grid() {
 }
 
 }  // namespace
+
+int grouped_grid() { return persistent_grid(); }
 
 int grouped_down_ksplit(const ExpertArgs& a) {
   // split the long K of the down projection in two when there are too few
@@ -390,13 +526,20 @@ int grouped_down_ksplit(const ExpertArgs& a) {
 int launch_grouped_gate_up(const ExpertArgs& a, hipStream_t st) {
   grouped_gemm_kernel<true, kNS><<<persistent_grid(), 256, 0, st>>>(
       (const uint16_t*)a.experts, a.stride_elems, (const uint16_t*)a.x, a.perm, a.k, a.offsets,
-      a.tile_off, a.E, a.H, a.F, a.T, 1, 0, a.act);
+      a.tile_off, a.E, a.H, a.F, a.T, 1, 0, a.act, a.gws);
+  if (a.gws)
+    grouped_fixup_kernel<true><<<4 * persistent_grid(), 256, 0, st>>>(
+        a.offsets, a.tile_off, a.E, a.H, a.F, 1, 0, a.act, a.gws, persistent_grid() / 8);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_grouped_down(const ExpertArgs& a, int ksplit, hipStream_t st) {
   grouped_gemm_kernel<false, kNS><<<persistent_grid(), 256, 0, st>>>(
       (const uint16_t*)a.experts, a.stride_elems, (const uint16_t*)a.act, a.perm, a.k,
-      a.offsets, a.tile_off, a.E, a.H, a.F, a.T, ksplit, (size_t)a.S * a.H, a.yp);
+      a.offsets, a.tile_off, a.E, a.H, a.F, a.T, ksplit, (size_t)a.S * a.H, a.yp, a.gws);
+  if (a.gws)
+    grouped_fixup_kernel<false><<<4 * persistent_grid(), 256, 0, st>>>(
+        a.offsets, a.tile_off, a.E, a.H, a.F, ksplit, (size_t)a.S * a.H, a.yp, a.gws,
+        persistent_grid() / 8);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -67,6 +67,9 @@ struct ExpertArgs {
   const int32_t* active;    // [E+1]
   void* act;                // [S][F] bf16 or fp32
   float* yp;                // [S][H] fp32
+  // grouped GEMMs: partial sums of split tail tiles, one 256 KB slot per
+  // workgroup (grouped_grid() of them), or null (no split)
+  float* gws = nullptr;
   // step 5 inputs for a down projection that folds the combine in (cy null:
   // it may not): gate weights [T][k], slot of each pair [T][k] (-1: dropped),
   // residual [T][H] or null, output [T][H]
@@ -97,6 +100,8 @@ int launch_grouped_gate_up(const ExpertArgs& a, hipStream_t st);
 // split-K factor the grouped down projection uses for this call (1 or 2);
 // with 2 it writes two partial planes yp[2][S][H]
 int grouped_down_ksplit(const ExpertArgs& a);
+// workgroups of a grouped GEMM launch on the current device
+int grouped_grid();
 int launch_grouped_down(const ExpertArgs& a, int ksplit, hipStream_t st);
 // bf16 expert FFN, weight-streaming MFMA kernels (few rows per expert; every
 // batch for uint8 experts)

@@ -39,6 +39,8 @@ struct moe_layer {
   void* act;          // [S][F] dtype
   float* yp;          // [2][S][H]
   int32_t* sync;      // [1] zeroed completion counter of the fused small-batch router
+  int gslots;         // workgroups of the grouped GEMMs (0: the layer never runs them)
+  float* gws;         // [gslots][256 x 256] partial sums of split tail tiles
 };
 
 namespace {
@@ -136,6 +138,12 @@ void carve(moe_layer* L, Arena& A) {
   // two planes: the grouped down projection may split its K range in two
   L->yp = (float*)arena_alloc(A, 2 * S * (size_t)d.hidden * 4);
   L->sync = (int32_t*)arena_alloc(A, 4);
+  // the grouped GEMMs run when T * k > 32 * E (or when pinned to them)
+  const bool grouped = d.dtype == MOE_BF16 && d.expert_format != MOE_EXPERT_U8 &&
+                       !(d.flags & MOE_FLAG_PATH_STREAM) &&
+                       ((d.flags & MOE_FLAG_PATH_GROUPED) || S > 32 * E);
+  L->gslots = grouped ? grouped_grid() : 0;
+  L->gws = (float*)arena_alloc(A, (size_t)L->gslots * 256 * 256 * 4);
 }
 
 // Keeps the layer's device current for the duration of a call.
@@ -346,6 +354,7 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
   ea.active = L->active;
   ea.act = L->act;
   ea.yp = L->yp;
+  if (L->gslots > 0 && L->gslots == grouped_grid()) ea.gws = L->gws;
   {
     // rows an expert is expected to see, for the width of a streaming pass
     const int avg = (S + d.num_experts - 1) / d.num_experts;
