@@ -30,11 +30,13 @@
 // tile lists on the device from the expert offsets (no host sync).  A
 // workgroup starts the first K steps of its next tile before it writes out
 // the current one, so tile boundaries cost little.  In a tile whose token
-// rows end early, waves skip the MFMAs of 32-row blocks past the end.  The
-// tiles of an XCD's last, partial round are cut along K into pieces run by
-// the workgroups that would otherwise idle; the pieces store fp32 partial
-// sums and a second, short launch adds them in piece order and writes those
-// tiles (no cross-workgroup waiting, and the same result on every call).
+// rows end early, waves skip the MFMAs of 32-row blocks past the end.  In
+// the down projection the tiles of an XCD's last, partial round are cut
+// along K into pieces run by the workgroups that would otherwise idle; the
+// pieces store fp32 partial sums and a second, short launch adds them in
+// piece order and writes those tiles (no cross-workgroup waiting, and the
+// same result on every call).  Gate/up tiles are shorter (K = H) and gain
+// nothing from it.
 #include "common.h"
 #include "kernels.h"
 
@@ -63,8 +65,9 @@ __device__ __forceinline__ int lds_slot(int row, int c) {
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0f70)
 #define GG_BARRIER() asm volatile("s_barrier" ::: "memory")
 
-// Tail split: the tiles that would leave most workgroups of an XCD idle in
-// its last round are cut along K into np pieces of at least kMinPiece steps.
+// Tail split (down projection): the tiles that would leave most workgroups
+// of an XCD idle in its last round are cut along K into np pieces of at
+// least kMinPiece steps.
 constexpr int kMaxPieces = 4;
 constexpr int kMinPiece = 16;
 constexpr int kPartFloats = 256 * 256;  // one piece's fp32 partial sums
@@ -226,7 +229,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
   const int xcd = blockIdx.x & 7;
   const int nw = gridDim.x >> 3;   // workgroups per XCD
   const int jw = blockIdx.x >> 3;  // this workgroup's place on its XCD
-  const Plan pl = make_plan(GATED, tile_off, E, H, F, ksplit, xcd, nw, ws != nullptr);
+  const Plan pl = make_plan(GATED, tile_off, E, H, F, ksplit, xcd, nw, !GATED && ws != nullptr);
   // work item w of this workgroup (rounds 0, 1, ...)
   auto locate = [&](int w, Tile& t) -> bool {
     if (pl.np < 2 || w < pl.nfull) {
@@ -526,10 +529,7 @@ int grouped_down_ksplit(const ExpertArgs& a) {
 int launch_grouped_gate_up(const ExpertArgs& a, hipStream_t st) {
   grouped_gemm_kernel<true, kNS><<<persistent_grid(), 256, 0, st>>>(
       (const uint16_t*)a.experts, a.stride_elems, (const uint16_t*)a.x, a.perm, a.k, a.offsets,
-      a.tile_off, a.E, a.H, a.F, a.T, 1, 0, a.act, a.gws);
-  if (a.gws)
-    grouped_fixup_kernel<true><<<4 * persistent_grid(), 256, 0, st>>>(
-        a.offsets, a.tile_off, a.E, a.H, a.F, 1, 0, a.act, a.gws, persistent_grid() / 8);
+      a.tile_off, a.E, a.H, a.F, a.T, 1, 0, a.act, nullptr);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
