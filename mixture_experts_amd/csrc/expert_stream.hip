@@ -9,7 +9,8 @@
 //
 // Work item: one non-empty expert x 16 output rows (gate AND up rows
 // f0..f0+15 for the first kernel, 32 weight rows; down rows h0..h0+15 for the
-// second), over all of the expert's token rows in passes of TR.  The grid is
+// second, h0..h0+63 when a pass covers 32 token rows), over all of the
+// expert's token rows in passes of TR.  The grid is
 // persistent: workgroup b takes items b, b + G, b + 2G, ... and treats the
 // K chunks of all its items as one sequence.  A chunk is CK (512, 256 or
 // 128, as K allows) K elements: the 2 CK-byte run of every
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(256) void stream_kernel(
     int F, int T, void* __restrict__ out, const float* __restrict__ cw,
     const int32_t* __restrict__ cinv, const float* cres, float* cy) {
   constexpr int WE = Q8 ? 1 : 2;                // bytes per weight
-  constexpr int NA = Q8 ? QNA : (GATED ? 2 : 1);  // weight row blocks of 16 per item
+  constexpr int NA = (Q8 || !GATED) ? QNA : 2;  // weight row blocks of 16 per item
   constexpr int WR = 16 * NA;                   // weight rows per item
   constexpr int OB = GATED ? NA / 2 : NA;       // output row blocks of 16 per item
   constexpr int NB = (TR + 15) / 16;            // token column blocks of the MFMA
@@ -410,7 +411,7 @@ __global__ __launch_bounds__(256) void stream_kernel(
 
 template <bool GATED, bool Q8, int QNA, int TR, int NS, int CK>
 int launch_tr(const ExpertArgs& a, hipStream_t st, bool* combined = nullptr) {
-  constexpr int NA = Q8 ? QNA : (GATED ? 2 : 1), NB = (TR + 15) / 16;
+  constexpr int NA = (Q8 || !GATED) ? QNA : 2, NB = (TR + 15) / 16;
   constexpr int OB = GATED ? NA / 2 : NA;
   constexpr int stage = (16 * NA * (Q8 ? 1 : 2) + TR * 2) * CK, red = 4 * NA * NB * 64 * 16;
   constexpr int lds = NS * stage + (red <= stage ? 16 : red);
@@ -466,19 +467,25 @@ int launch_stream_q(const ExpertArgs& a, hipStream_t st, bool* combined) {
       if (rows > 16) return launch_tr<GATED, Q8, 4, 32, 2, 256>(a, st, combined);
     }
   }
+  // bf16 down items: one 16-row block (A1) while a pass covers up to 16
+  // token rows; at 32 token rows a 16-row item would load twice as many
+  // token bytes as weight bytes per chunk, so items take 64 rows (A4).
+  // (bf16 gate/up items stay at 16 gate + 16 up rows: two workgroups per
+  // CU at 32 token rows were faster than one with 32 + 32-row items.)
+  constexpr int A1 = (GATED || Q8) ? 2 : 1, A4 = (GATED || Q8) ? 2 : 4;
   if (GATED && K % 512 == 0 && rows <= 8)  // 1 KB row runs, one deep ring per CU
     return launch_tr<GATED, Q8, 2, 8, 3, 512>(a, st, combined);
   if (!GATED && K % 512 == 0 && rows <= 16) {  // down: 1 KB row runs
-    if (rows <= 8) return launch_tr<GATED, Q8, 2, 8, Q8 ? 3 : 4, 512>(a, st, combined);
-    return launch_tr<GATED, Q8, 2, 16, 3, 512>(a, st, combined);
+    if (rows <= 8) return launch_tr<GATED, Q8, A1, 8, Q8 ? 3 : 4, 512>(a, st, combined);
+    return launch_tr<GATED, Q8, A1, 16, 3, 512>(a, st, combined);
   }
   if (K % 256 == 0) {
-    if (rows <= 8) return launch_tr<GATED, Q8, 2, 8, GATED ? 3 : 4, 256>(a, st, combined);
-    if (rows <= 16) return launch_tr<GATED, Q8, 2, 16, GATED ? 3 : 4, 256>(a, st, combined);
-    return launch_tr<GATED, Q8, 2, 32, GATED ? 2 : 3, 256>(a, st, combined);
+    if (rows <= 8) return launch_tr<GATED, Q8, A1, 8, GATED ? 3 : 4, 256>(a, st, combined);
+    if (rows <= 16) return launch_tr<GATED, Q8, A1, 16, GATED ? 3 : 4, 256>(a, st, combined);
+    return launch_tr<GATED, Q8, A4, 32, GATED ? 2 : 3, 256>(a, st, combined);
   }
-  if (rows <= 16) return launch_tr<GATED, Q8, 2, 16, 4, 128>(a, st, combined);
-  return launch_tr<GATED, Q8, 2, 32, GATED ? 3 : 4, 128>(a, st, combined);
+  if (rows <= 16) return launch_tr<GATED, Q8, A1, 16, 4, 128>(a, st, combined);
+  return launch_tr<GATED, Q8, A4, 32, GATED ? 3 : 4, 128>(a, st, combined);
 }
 
 template <bool GATED>
