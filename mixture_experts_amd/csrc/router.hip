@@ -157,9 +157,12 @@ __device__ void topk_rows16(const float* lg, int ldl, int tile0, int T, int E, i
     // softmax over the picks: lane j < k holds pick j; the maximum is pick 0
     const float m = __shfl(my_v, lane & ~15);
     const double ex = (el < k && !raw) ? exp((double)my_v - (double)m) : 0.0;
-    double z = ex;
+    // z adds the exponentials in pick order, as topk_rows does, so that every
+    // route kernel gives the same weights bit for bit
+    double z = 0.0;
 #pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+    for (int j = 0; j < MOE_MAX_TOPK; ++j)
+      if (j < k) z += __shfl(ex, (lane & ~15) + j);
     if (ok && el < k) {
       idx_out[(size_t)t * k + el] = my_e;
       w_out[(size_t)t * k + el] = raw ? my_v : (float)(ex / z);

@@ -86,44 +86,71 @@ def near_tie_gap(logits: np.ndarray, k: int) -> np.ndarray:
     return s[:, k - 1] - s[:, k]
 
 
-def check_rows(case: Case, x_np: np.ndarray, tokens, y_gpu_rows: np.ndarray,
-               gpu_idx_rows: np.ndarray, tol: float | None = None,
-               keep_rows: np.ndarray | None = None) -> dict:
-    """Compare GPU output rows of `tokens` with the oracle, near-tie rule applied.
+def reference_rows(case: Case, x_np: np.ndarray, tokens, gpu_idx_rows: np.ndarray,
+                   keep_rows: np.ndarray | None = None, chunk: int = 0, log=None):
+    """The oracle's output rows of `tokens` under the near-tie rule, and
+    routing statistics.  Returns (y_ref [n, H] float64, stats).
+
     keep_rows [len(tokens), k]: with an expert capacity, the slots that are
     kept under the GPU's routing of all tokens (which tokens an expert drops
     depends on the others); the reference then uses the GPU's experts for
-    every row, after the near-tie check has validated them."""
+    every row, after the near-tie check has validated them.
+    chunk > 0: the oracle is called on that many tokens at a time (log, if
+    given, is called after each chunk), so large workloads report progress."""
     k = case.shape.k
-    tol = TOL[case.shape.dtype] if tol is None else tol
     tokens = np.asarray(tokens, np.int32)
-    ref = case.orc.tokens(x_np, tokens)
-    gap = near_tie_gap(ref["logits"], k)
     gpu_idx_rows = np.asarray(gpu_idx_rows).reshape(len(tokens), k)
-    differs = np.any(gpu_idx_rows != ref["idx"], axis=1)
-    stats = dict(tokens=len(tokens), near_ties=int((gap < NEAR_TIE).sum()),
-                 routed_differently=int(differs.sum()))
-    y_ref = ref["y"].copy()
-    if differs.any():
-        kth = -np.sort(-ref["logits"], axis=1)[:, k - 1]
-        for n in np.nonzero(differs)[0]:
-            chosen = ref["logits"][n, gpu_idx_rows[n]]
-            # allowed only for near ties, and only as a valid top-k under a
-            # perturbation of at most NEAR_TIE (slot order: adjacent slots
-            # may swap only when their logits are that close)
-            assert len(set(gpu_idx_rows[n].tolist())) == k, (tokens[n], gpu_idx_rows[n])
-            assert np.all(chosen >= kth[n] - NEAR_TIE), (tokens[n], gpu_idx_rows[n], ref["idx"][n])
-            assert np.all(np.diff(chosen) <= NEAR_TIE), (tokens[n], chosen)
-        fix = np.nonzero(differs)[0]
-        r2 = case.orc.tokens(x_np, tokens[fix], idx_override=gpu_idx_rows[fix])
-        y_ref[fix] = r2["y"]
-    if keep_rows is not None:
-        y_ref = case.orc.tokens(x_np, tokens, idx_override=gpu_idx_rows,
-                                keep=np.asarray(keep_rows, np.int32).reshape(len(tokens), k))["y"]
-        stats["dropped_slots"] = int((np.asarray(keep_rows) == 0).sum())
-    rms = float(np.sqrt(np.mean(y_ref ** 2)))
-    err = float(np.abs(y_gpu_rows.astype(np.float64) - y_ref).max()) if len(tokens) else 0.0
-    stats.update(rms=rms, max_err=err, rel=err / rms if rms > 0 else err)
+    n = len(tokens)
+    step = n if chunk <= 0 else chunk
+    y_ref = np.empty((n, case.shape.H), np.float64)
+    stats = dict(tokens=n, near_ties=0, routed_differently=0)
+    for c0 in range(0, n, max(step, 1)):
+        sl = slice(c0, min(n, c0 + step))
+        tk, gi = tokens[sl], gpu_idx_rows[sl]
+        kp = None if keep_rows is None else np.asarray(keep_rows, np.int32).reshape(n, k)[sl]
+        ref = case.orc.tokens(x_np, tk)
+        gap = near_tie_gap(ref["logits"], k)
+        differs = np.any(gi != ref["idx"], axis=1)
+        stats["near_ties"] += int((gap < NEAR_TIE).sum())
+        stats["routed_differently"] += int(differs.sum())
+        yr = ref["y"]
+        if differs.any():
+            kth = -np.sort(-ref["logits"], axis=1)[:, k - 1]
+            for i in np.nonzero(differs)[0]:
+                chosen = ref["logits"][i, gi[i]]
+                # allowed only for near ties, and only as a valid top-k under a
+                # perturbation of at most NEAR_TIE (slot order: adjacent slots
+                # may swap only when their logits are that close)
+                assert len(set(gi[i].tolist())) == k, (tk[i], gi[i])
+                assert np.all(chosen >= kth[i] - NEAR_TIE), (tk[i], gi[i], ref["idx"][i])
+                assert np.all(np.diff(chosen) <= NEAR_TIE), (tk[i], chosen)
+            fix = np.nonzero(differs)[0]
+            yr[fix] = case.orc.tokens(x_np, tk[fix], idx_override=gi[fix])["y"]
+        if kp is not None:
+            yr = case.orc.tokens(x_np, tk, idx_override=gi, keep=kp)["y"]
+            stats["dropped_slots"] = stats.get("dropped_slots", 0) + int((kp == 0).sum())
+        y_ref[sl] = yr
+        if log is not None:
+            log(f"    oracle rows {sl.stop} / {n}")
+    return y_ref, stats
+
+
+def compare_rows(case: Case, y_gpu_rows: np.ndarray, y_ref: np.ndarray, stats: dict,
+                 tol: float | None = None) -> dict:
+    """max |y_gpu - y_ref| <= tol * RMS(y_ref), the RMS over all compared rows."""
+    tol = TOL[case.shape.dtype] if tol is None else tol
+    rms = float(np.sqrt(np.mean(y_ref ** 2))) if y_ref.size else 0.0
+    err = float(np.abs(y_gpu_rows.astype(np.float64) - y_ref).max()) if y_ref.size else 0.0
+    stats = dict(stats, rms=rms, max_err=err, rel=err / rms if rms > 0 else err)
     assert np.isfinite(y_gpu_rows).all()
     assert err <= tol * rms, stats
     return stats
+
+
+def check_rows(case: Case, x_np: np.ndarray, tokens, y_gpu_rows: np.ndarray,
+               gpu_idx_rows: np.ndarray, tol: float | None = None,
+               keep_rows: np.ndarray | None = None, chunk: int = 0, log=None) -> dict:
+    """Compare GPU output rows of `tokens` with the oracle, near-tie rule applied
+    (see reference_rows and compare_rows)."""
+    y_ref, stats = reference_rows(case, x_np, tokens, gpu_idx_rows, keep_rows, chunk, log)
+    return compare_rows(case, y_gpu_rows, y_ref, stats, tol)

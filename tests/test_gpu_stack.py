@@ -95,7 +95,7 @@ def test_stack_graph_replay_matches_eager():
     s.close()
 
 
-@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("T", [1, 4, 16, 64])
 def test_mixtral_stack_32_layers_teacher_forced(T):
     """The 32-layer Mixtral-shaped stack (90 GB of experts in one buffer):
     each sampled layer's branch output against the oracle fed with the GPU's
