@@ -202,6 +202,32 @@ enum {
 int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* stream,
                    void* const* stage_events);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * forward as moe_forward (steps 1-5, the same kernels) without a layer
+ * handle: *d describes the layer (its pointers are borrowed for the call,
+ * max_tokens bounds T), and the call's workspace is carved, for this T, from
+ * a file-scope device array of MOE_NOALLOC_SCRATCH_BYTES that each GPU the
+ * library runs on holds until the process ends.  Nothing is allocated.
+ *   - The first call on a device also queues, on `stream`, a one-time clear
+ *     of a completion counter in that array (every later launch leaves it at
+ *     zero).
+ *   - Every call on a GPU shares that GPU's array and leaves its contents
+ *     behind: calls that overlap on one GPU (any stream, any thread) race,
+ *     so the caller serialises them.
+ *   - Results equal moe_forward's bit for bit, except on calls that run the
+ *     grouped GEMMs (T*k > 32*E, or MOE_FLAG_PATH_GROUPED): there the down
+ *     projection does not split its last round of tiles along K (that needs
+ *     64 MB of partial sums), so the sums are added in another order
+ *     (deterministic, within rounding of moe_forward).
+ * Errors: those of moe_layer_create's validation of *d and of moe_forward's
+ * arguments; MOE_ERR_UNSUPPORTED when the workspace of this call does not
+ * fit the array (8 experts of H=4096, F=14336, k=2: up to about 540
+ * tokens); nothing is launched on an error. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_forward_noalloc(const moe_layer_desc* d, const void* x, int32_t T, float* y,
+                        void* stream);
+
 /* Quantises E bf16 experts (src: expert e at src + e*src_stride bytes, laid
  * out as in moe_layer_desc) into uint8 experts for MOE_EXPERT_U8 (dst, e at
  * dst + e*dst_stride).  Per matrix, in fp32 arithmetic with IEEE division

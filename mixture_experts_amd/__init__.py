@@ -33,7 +33,8 @@ MOE_NUM_STAGES = 5
 STAGE_NAMES = ("route", "dispatch", "gate_up", "down", "combine")
 
 EXPORTED = ("moe_layer_create", "moe_route", "moe_forward", "moe_forward_ev", "moe_layer_free",
-            "moe_quantize_experts_u8")
+            "moe_quantize_experts_u8", "moe_forward_noalloc")
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _ERRS = {MOE_ERR_INVALID_ARG: "invalid argument", MOE_ERR_NO_MEMORY: "out of device memory",
          MOE_ERR_DEVICE: "device error", MOE_ERR_UNSUPPORTED: "unsupported shape or mode"}
@@ -74,6 +75,8 @@ def lib():
         L.moe_forward.restype = ctypes.c_int
         L.moe_forward_ev.argtypes = [vp, vp, i32, vp, vp, vp]
         L.moe_forward_ev.restype = ctypes.c_int
+        L.moe_forward_noalloc.argtypes = [ctypes.POINTER(moe_layer_desc), vp, i32, vp, vp]
+        L.moe_forward_noalloc.restype = ctypes.c_int
         L.moe_layer_free.argtypes = [vp]
         L.moe_layer_free.restype = None
         L.moe_quantize_experts_u8.argtypes = [vp, ctypes.c_uint64, i32, i32, i32, vp,
@@ -152,6 +155,14 @@ def moe_forward_ev(layer, x, T, y, stream, stage_events):
     rc = lib().moe_forward_ev(layer, _ptr(x), T, _ptr(y), _stream(stream), arr)
     if rc != MOE_OK:
         raise MoeError(rc, "moe_forward_ev")
+
+
+def moe_forward_noalloc(desc: moe_layer_desc, x, T, y, stream=None):
+    """The forward that allocates nothing (workspace in the library's static
+    device array); desc as for moe_layer_create."""
+    rc = lib().moe_forward_noalloc(ctypes.byref(desc), _ptr(x), T, _ptr(y), _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_forward_noalloc")
 
 
 def moe_layer_free(layer):

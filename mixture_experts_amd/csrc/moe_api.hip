@@ -11,6 +11,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kernels.h"
 #include "moe.h"
 
@@ -104,7 +106,9 @@ int validate_desc(const moe_layer_desc* d) {
   return MOE_OK;
 }
 
-void carve(moe_layer* L, Arena& A) {
+// split_ws: also carve the grouped GEMMs' tail-split partial sums (64 MB on
+// 256 CUs) when the layer runs them
+void carve(moe_layer* L, Arena& A, bool split_ws = true) {
   const moe_layer_desc& d = L->d;
   const size_t S = (size_t)d.max_tokens * d.top_k;
   const size_t E = (size_t)d.num_experts;
@@ -139,7 +143,7 @@ void carve(moe_layer* L, Arena& A) {
   L->yp = (float*)arena_alloc(A, 2 * S * (size_t)d.hidden * 4);
   L->sync = (int32_t*)arena_alloc(A, 4);
   // the grouped GEMMs run when T * k > 32 * E (or when pinned to them)
-  const bool grouped = d.dtype == MOE_BF16 && d.expert_format != MOE_EXPERT_U8 &&
+  const bool grouped = split_ws && d.dtype == MOE_BF16 && d.expert_format != MOE_EXPERT_U8 &&
                        !(d.flags & MOE_FLAG_PATH_STREAM) &&
                        ((d.flags & MOE_FLAG_PATH_GROUPED) || S > 32 * E);
   L->gslots = grouped ? grouped_grid() : 0;
@@ -193,6 +197,42 @@ int run_route(moe_layer* L, const void* x_route, int T, const float* logits_in,
   if (launch_router(ra, st)) return MOE_ERR_DEVICE;
   if (launch_dispatch(da, st)) return MOE_ERR_DEVICE;
   return MOE_OK;
+}
+
+// ---- the entry point that allocates nothing (moe_forward_noalloc) ----------
+//
+// Its workspace is this file-scope array, one copy per GPU for the life of
+// the process.  The first 256 bytes hold the small-batch route's completion
+// counter (zero between calls: cleared once per device at set-up, and every
+// route launch leaves it at zero); the workspace of a call is carved after
+// them, sized for that call's T.
+constexpr size_t kScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+constexpr size_t kScratchHead = 256;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+__global__ void zero_i32_kernel(int32_t* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0;
+}
+
+std::mutex g_scratch_mu;
+unsigned char* g_scratch[64];  // device address of `scratch` per device
+
+// The device address of this device's scratch array (set-up on first use:
+// the address, then a fill kernel on `st` that clears the counter).
+unsigned char* scratch_base(int dev, hipStream_t st) {
+  if (dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    zero_i32_kernel<<<1, 64, 0, st>>>((int32_t*)p, (int)(kScratchHead / 4));
+    if (hipGetLastError() != hipSuccess) return nullptr;
+    g_scratch[dev] = (unsigned char*)p;
+  }
+  return g_scratch[dev];
 }
 
 }  // namespace
@@ -391,6 +431,33 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
     return MOE_ERR_DEVICE;
   if (!mark(MOE_NUM_STAGES)) return MOE_ERR_DEVICE;
   return MOE_OK;
+}
+
+int moe_forward_noalloc(const moe_layer_desc* d, const void* x, int32_t T, float* y,
+                        void* stream) {
+  int rc = validate_desc(d);
+  if (rc != MOE_OK) return rc;
+  if (T < 1 || T > d->max_tokens) return MOE_ERR_INVALID_ARG;
+  // a layer on the host stack whose workspace is carved from the scratch
+  // array for this call's T (no tail-split partial sums: they would take the
+  // whole array)
+  moe_layer L;
+  memset(&L, 0, sizeof L);
+  L.d = *d;
+  L.d.max_tokens = T;
+  L.esize = d->dtype == MOE_F32 ? 4 : 2;
+  Arena measure{nullptr, 0, 0};
+  carve(&L, measure, false);
+  if (align_up(measure.off, 256) > kScratchBytes - kScratchHead) return MOE_ERR_UNSUPPORTED;
+  if (hipGetDevice(&L.device) != hipSuccess) return MOE_ERR_DEVICE;
+  unsigned char* base = scratch_base(L.device, (hipStream_t)stream);
+  if (!base) return MOE_ERR_DEVICE;
+  Arena real{(char*)base + kScratchHead, kScratchBytes - kScratchHead, 0};
+  carve(&L, real, false);
+  L.sync = (int32_t*)base;
+  L.gslots = 0;
+  L.gws = nullptr;
+  return moe_forward_ev(&L, x, T, y, stream, nullptr);
 }
 
 void moe_layer_free(moe_layer_t* L) {
