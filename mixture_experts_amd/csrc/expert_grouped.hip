@@ -17,20 +17,29 @@
 // rows and the same 128 up rows, so SiLU(g)*u pairs accumulators that sit in
 // the same lane.
 //
-// Operands reach LDS through direct global->LDS loads (global_load_lds_dwordx4,
-// no register staging) into a ring of NS stages of one K step (32) each; the
-// 16-byte chunks of every 64-byte row are XOR-swizzled so that MFMA operand
-// reads are free of bank conflicts.  Each wave runs one instruction stream in
-// which the MFMAs of a half step (16 k) are interleaved with the LDS reads of
-// the next half step and with its share of the loads of a later K step, so
-// the matrix cores keep issuing while LDS and the load path work in their
-// shadow; one workgroup barrier per K step publishes a landed stage.
+// Operands reach LDS through direct global->LDS loads (global_load_lds_dwordx4
+// for weight rows, buffer_load_dwordx4 ... lds for token rows; no register
+// staging) in K steps of 64: one instruction moves 8 rows x 128 bytes, so
+// every request to L2 is a whole 128-byte line.  LDS holds three K steps of
+// weight rows and two of token rows (5 x 32 KB): weight rows, which come
+// from HBM on first touch, are loaded two steps ahead, token rows one step
+// ahead.  The 16-byte chunks of every 128-byte row are XOR-swizzled so that
+// MFMA operand reads are free of bank conflicts.  Each wave runs one
+// instruction stream in which the MFMAs of a slice (16 k) are interleaved
+// with the LDS reads of the next slice and with its share of the loads of
+// later K steps, spread over the slices so that the matrix cores keep
+// issuing; one workgroup barrier per K step publishes a landed step.
 //
 // The kernels are persistent (one workgroup per compute unit) and build their
-// tile lists on the device from the expert offsets (no host sync).  A
-// workgroup starts the first K steps of its next tile before it writes out
-// the current one, so tile boundaries cost little.  In a tile whose token
-// rows end early, waves skip the MFMAs of 32-row blocks past the end.  In
+// tile lists on the device from the expert offsets (no host sync).  In
+// gate/up a workgroup starts the first K steps of its next tile before it
+// writes out the current one, so tile boundaries cost little; the down
+// projection stages its fp32 output through LDS first.  In a tile whose
+// token rows end early, the loads of rows past the end fall outside the
+// token buffer's range, so they move no data (the hardware returns zeros
+// for them), and gate/up waves skip the MFMAs of 32-row blocks past the end
+// (the down projection computes them: with more than one variant of its K
+// loop the compiler no longer keeps the accumulators in place).  In
 // the down projection the tiles of an XCD's last, partial round are cut
 // along K into pieces run by the workgroups that would otherwise idle; the
 // pieces store fp32 partial sums and a second, short launch adds them in
@@ -45,31 +54,45 @@
 namespace {
 
 constexpr int kGroupW = 8;  // weight tiles per L2 group
-constexpr int kBK = 32;     // K step (elements): one 64-byte row slice
-constexpr int kCPR = 4;     // 16-byte chunks per LDS row
-constexpr int kNS = 4;      // LDS ring depth (4 x 32 KB)
-constexpr int kStage = 2 * 256 * kCPR;   // 16-byte chunks per ring stage (32 KB)
-// down projection: its output is staged in the 64 KB from kStageOut, clear of
-// ring stages 0-2 where the next tile's first K steps land meanwhile
-constexpr int kStageOut = 3 * kStage;
-constexpr int kLdsDown = kStageOut + 64 * 1024 / 16;  // 160 KB
+constexpr int kBK = 64;     // K step (elements): one 128-byte row slice
+constexpr int kCPR = 8;     // 16-byte chunks per LDS row
+// LDS: three buffers of one K step of the weight rows and two of the token
+// rows (256 rows x 128 bytes = 32 KB each), 160 KB in all; K step s takes
+// weight buffer s % 3 and token buffer 3 + s % 2
+constexpr int kBuf = 256 * kCPR;   // 16-byte chunks per buffer
 
-// Chunk c of row r sits at physical chunk c ^ ((r / 4) % 4): the 16 lanes of
+// Chunk c of row r sits at physical chunk c ^ ((r / 2) % 8): the 16 lanes of
 // one MFMA operand read take 16 consecutive rows at one logical chunk, and
-// those land in 16 distinct 16-byte slots of a 256-byte bank window.
+// those land in 16 distinct 16-byte slots of a 256-byte bank window (rows of
+// one parity share a half of the window; r / 2 spreads them over it).
 __device__ __forceinline__ int lds_slot(int row, int c) {
-  return row * kCPR + (c ^ ((row >> 2) & 3));
+  return row * kCPR + (c ^ ((row >> 1) & 7));
 }
 
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0f70)
 #define GG_BARRIER() asm volatile("s_barrier" ::: "memory")
 
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource of `bytes` bytes at base (a raw buffer: stride 0; word 3
+// as for every gfx9-family raw buffer).  A buffer load whose offset lies at
+// or beyond `bytes` reads nothing from memory and yields zeros.
+__device__ __forceinline__ i32x4 raw_buffer(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int32_t)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int32_t)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
 // Tail split (down projection): the tiles that would leave most workgroups
 // of an XCD idle in its last round are cut along K into np pieces of at
 // least kMinPiece steps.
 constexpr int kMaxPieces = 4;
-constexpr int kMinPiece = 16;
+constexpr int kMinPiece = 8;
 constexpr int kPartFloats = 256 * 256;  // one piece's fp32 partial sums
 
 // One tile: expert e, K slice ks, weight tile mt, token rows p0 .. p0+rows-1,
@@ -213,15 +236,15 @@ __device__ __forceinline__ f32x4* part_base(float* ws, int slot, int wave) {
   return reinterpret_cast<f32x4*>(ws + (size_t)slot * kPartFloats + wave * 16384) + ln;
 }
 
-template <bool GATED, int NS>
+template <bool GATED>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
     const uint16_t* __restrict__ experts, uint64_t stride_elems,
     const uint16_t* __restrict__ tok, const int32_t* __restrict__ perm, int k_top,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off, int E, int H,
     int F, int T, int ksplit, size_t plane, void* __restrict__ out, float* __restrict__ ws) {
-  // ring stage s at lds + s * kStage: [weight rows | token rows] x 256 x 4 chunks
-  __shared__ u32x4 lds[GATED ? NS * kStage : kLdsDown];
-  static_assert(GATED || (NS - 1) * kStage <= kStageOut, "LDS layout");
+  // weight buffers 0-2, token buffers 3-4 (the down projection's output is
+  // staged in the first 64 KB after the K loop)
+  __shared__ u32x4 lds[5 * kBuf];
 
   // ksplit > 1 (down projection only): the K range is cut into ksplit
   // slices, slice ks writes its partial sums to plane ks of the output.
@@ -231,7 +254,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
   const int jw = blockIdx.x >> 3;  // this workgroup's place on its XCD
   const Plan pl = make_plan(GATED, tile_off, E, H, F, ksplit, xcd, nw, !GATED && ws != nullptr);
   // work item w of this workgroup (rounds 0, 1, ...)
-  auto locate = [&](int w, Tile& t) -> bool {
+  auto locate = [&](int w, Tile& t) __attribute__((always_inline)) -> bool {
     if (pl.np < 2 || w < pl.nfull) {
       const int q = pl.q_beg + jw + w * nw;
       if (q >= pl.q_end) return false;
@@ -253,63 +276,101 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
   const int wm = wave & 1, wn = wave >> 1;
 
   // Loads: per K step each wave moves weight rows and token rows
-  // [64 wave, 64 wave + 64), 4 + 4 instructions of 16 rows x 64 bytes; lane l
-  // fills row l / 4, physical chunk l % 4, from the logical chunk stored there.
+  // [64 wave, 64 wave + 64), 8 + 8 instructions of 8 rows x 128 bytes; lane l
+  // fills row l / 8, physical chunk l % 8, from the logical chunk stored there.
   const uint16_t* eb = experts;
-  uint32_t aoff[4], boff[4];
-  // gate/up: the slot ids of this lane's 4 token rows (rows past the tile's
-  // end repeat its last row)
-  auto load_perm = [&](const Tile& t, int (&pv)[4]) {
+  // row group i of a lane is row group i & 1 plus 8 i rows (the swizzle of a
+  // row depends on (r / 2) % 8, which repeats every 16 rows): one base offset
+  // per parity, the rest uniform; gathered token rows (gate/up) take one each
+  uint32_t aoff[2], boff[GATED ? 8 : 2];
+  i32x4 brs = raw_buffer(tok, (uint32_t)T * H * 2u);
+  const bool tok_oob = (uint64_t)T * H * 2 <= 0x80000000ull;
+  // gate/up: the slot ids of this lane's 8 token rows (rows past the tile's
+  // end take its last row's)
+  auto load_perm = [&](const Tile& t, int (&pv)[8]) {
     if (!GATED) return;
     int ln;  // the lane id, opaque so that the addressing below is not kept live across tiles
     asm volatile("v_and_b32 %0, 63, %1" : "=v"(ln) : "v"((int)threadIdx.x));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pv[i] = perm[t.p0 + min(wave * 64 + i * 16 + (ln >> 2), t.rows - 1)];
+    for (int i = 0; i < 8; ++i) pv[i] = perm[t.p0 + min(wave * 64 + i * 8 + (ln >> 3), t.rows - 1)];
   };
-  auto set_tile = [&](const Tile& t, const int (&pv)[4]) {
+  auto set_tile = [&](const Tile& t, const int (&pv)[8]) {
     eb = experts + (size_t)stride_elems * t.e;
+    // the token buffer: all T tokens (gate/up, rows gathered through perm),
+    // or exactly this tile's rows of the activation (down projection)
+    if (!GATED) brs = raw_buffer(tok + (size_t)t.p0 * F, (uint32_t)t.rows * F * 2u);
     const int kbase = t.ks * K + t.k0 * kBK;
     int ln;  // the lane id, opaque as above
     asm volatile("v_and_b32 %0, 63, %1" : "=v"(ln) : "v"((int)threadIdx.x));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wave * 64 + i * 16 + (ln >> 2);
-      const int lc = (ln & 3) ^ ((r >> 2) & 3);
-      uint32_t a;
-      if (GATED) {
-        const int f0 = t.mt * 128;
-        a = (r < 128) ? (uint32_t)(f0 + r) * H : (uint32_t)F * H + (uint32_t)(f0 + r - 128) * H;
-      } else {
-        a = 2u * (uint32_t)F * H + (uint32_t)(t.mt * 256 + r) * F;
+    for (int i = 0; i < 8; ++i) {
+      const int r = wave * 64 + i * 8 + (ln >> 3);
+      const int lc = (ln & 7) ^ ((r >> 1) & 7);
+      if (i < 2) {
+        uint32_t a;
+        if (GATED) {  // waves 0-1 load gate rows, waves 2-3 the up rows
+          const int f0 = t.mt * 128;
+          a = (r < 128) ? (uint32_t)(f0 + r) * H : (uint32_t)F * H + (uint32_t)(f0 + r - 128) * H;
+        } else {
+          a = 2u * (uint32_t)F * H + (uint32_t)(t.mt * 256 + r) * F;
+        }
+        aoff[i] = a + lc * 8 + kbase;
       }
-      const int p = t.p0 + min(r, t.rows - 1);
-      const uint32_t b = GATED ? (uint32_t)min(max(pv[i], 0) / k_top, T - 1) * H : (uint32_t)p * F;
-      aoff[i] = a + lc * 8 + kbase;
-      boff[i] = b + lc * 8 + kbase;
+      // token rows, byte offsets in the token buffer (see brs); a row past the
+      // tile's end lies outside it, so its loads read nothing
+      if (GATED) {
+        // past the end: offset 2^31 (outside a token buffer of at most 2^31
+        // bytes), else the tile's last row again
+        const uint32_t o = ((uint32_t)min(max(pv[i], 0) / k_top, T - 1) * H + lc * 8 + kbase) * 2u;
+        boff[i] = (r >= t.rows && tok_oob) ? 0x80000000u : o;
+      } else if (i < 2) {
+        boff[i] = ((uint32_t)r * F + lc * 8 + kbase) * 2u;
+      }
     }
   };
   const uint32_t lds_base = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) u32x4*)&lds[0]);
-  // one 16-row load: operand op (0 weights, 1 tokens), row group i, K step s
-  auto dma = [&](int s, int op, int i) {
-    const uint16_t* src = (op == 0 ? eb + aoff[i] : tok + boff[i]) + s * kBK;
-    const uint32_t dst = lds_base + (uint32_t)(((s % NS) * kStage + op * 256 * kCPR) * 16) +
-                         (uint32_t)((wave * 64 + i * 16) * kCPR * 16);
+  // one 8-row load: operand op (0 weights, 1 tokens), row group i, K step s,
+  // into LDS buffer b
+  auto dma = [&](int s, int op, int i, int b) __attribute__((always_inline)) {
+    const uint32_t dst = lds_base + (uint32_t)(b * kBuf * 16) +
+                         (uint32_t)((wave * 64 + i * 8) * kCPR * 16);
     // one wait state between the M0 write and the LDS-DMA load that reads it
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :
-                 : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(src)
-                 : "memory", "m0");
-  };
-  // the first NS-1 K steps of a tile of nk steps (ring stages 0 .. NS-2)
-  auto prologue = [&](int nk) {
+    if (op == 0) {
+      const uint16_t* src = eb + aoff[i & 1] + (size_t)(i & 6) * 8 * (GATED ? H : F) + s * kBK;
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                   :
+                   : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(src)
+                   : "memory", "m0");
+    } else {
+      // the row's offset in VADDR, the K step's in SOFFSET: a row inside the
+      // buffer stays inside it at every K step of the row, a row past it stays
+      // past it
+      i32x4 rs;  // the resource is uniform; keep it in SGPRs
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
+      for (int c = 0; c < 4; ++c) rs[c] = __builtin_amdgcn_readfirstlane(brs[c]);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                   :
+                   : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(boff[GATED ? i : (i & 1)]), "s"(rs),
+                     "s"(__builtin_amdgcn_readfirstlane(s * (kBK * 2) + (GATED ? 0 : (i & 6) * 8 * F * 2)))
+                   : "memory", "m0");
+    }
+  };
+  // the first K steps of a tile of nk steps: tokens and weights of steps 0
+  // and 1, then the weights of step 2 (issued last: the first wait lets
+  // exactly those 8 loads stay in flight)
+  auto prologue = [&](int nk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
       if (s < nk) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma(s, 0, i);
+        for (int i = 0; i < 8; ++i) dma(s, 1, i, 3 + s);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dma(s, 1, i);
+        for (int i = 0; i < 8; ++i) dma(s, 0, i, s);
       }
+    if (nk > 2) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dma(2, 0, i, 2);
+    }
   };
 
   // The K loop of one tile for a wave that computes its first NJ token
@@ -331,73 +392,106 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
       brow[i] = (2 * i + wn) * 32 + (ln & 31);
     }
     const int kg = ln >> 5;
-    // fragments of one half step (16 k): lane group kg reads chunk 2 kg + h,
-    // a fixed permutation of the summation index applied to both operands
+    // fragments of one slice (16 k) of a K step: lane group kg reads chunk
+    // 4 kg + n in slice n, a fixed permutation of the summation index applied
+    // to both operands
     bf16x8 fa[2][4], fb[2][4];
-    // the 8 reads of half step (s, h) in the order of first use by the MFMAs
-    // (row block i of the weights, then token blocks 0..3, then weights 1..3)
-    auto rd = [&](int buf, int s, int h, int n) {
-      const int c = kg * 2 + h;
-      const u32x4* st = lds + (s % NS) * kStage;
-      if (n == 0) fa[buf][0] = as_bf16x8(st[lds_slot(arow[0], c)]);
-      else if (n < 5) {
-        if (n - 1 < NJ) fb[buf][n - 1] = as_bf16x8(st[256 * kCPR + lds_slot(brow[n - 1], c)]);
-      } else fa[buf][n - 4] = as_bf16x8(st[lds_slot(arow[n - 4], c)]);
+    // the 8 reads of slice n of the step in weight buffer wb and token buffer
+    // tb, in the order of first use by the MFMAs (row block 0 of the
+    // weights, then token blocks 0..3, then weights 1..3)
+    auto rd = [&](int buf, int wb, int tb, int n, int q) __attribute__((always_inline)) {
+      const int c = kg * 4 + n;
+      const u32x4* wst = lds + wb * kBuf;
+      const u32x4* tst = lds + (3 + tb) * kBuf;
+      if (q == 0) fa[buf][0] = as_bf16x8(wst[lds_slot(arow[0], c)]);
+      else if (q < 5) {
+        if (q - 1 < NJ) fb[buf][q - 1] = as_bf16x8(tst[lds_slot(brow[q - 1], c)]);
+      } else fa[buf][q - 4] = as_bf16x8(wst[lds_slot(arow[q - 4], c)]);
     };
-    // the MFMAs of fragment buffer buf, with the 8 reads of (rs, rh) into the
-    // other buffer and up to four 16-row loads of K step ls (half lh) woven in.
-    // RD / LD are std::bool_constant (fixed) or bool (decided at run time).
-    auto half_step = [&](int buf, auto RD, int rs, int rh, auto LD, int ls, int lh) {
+    // the 16 MFMAs of fragment buffer buf, with the 8 reads of slice rn of
+    // buffers (wb, tb) into the other fragment buffer and some loads woven
+    // in: the token loads of K step ts (8, into token buffer ts % 2) when LT,
+    // and the weight rows [wr0, wr0 + wn) of K step ws into weight buffer wsb
+    // when LW (4 rows: at every other MFMA of the second half; 2 rows: at
+    // MFMAs 4 and 12).
+    // RD / LT / LW are std::bool_constant (fixed) or bool (decided at run time).
+    auto slice = [&](int buf, auto RD, int wb, int tb, int rn, auto LT, int ts, auto LW, int ws,
+                     int wsb, auto WR0, auto WN) __attribute__((always_inline)) {
+      constexpr int wr0 = decltype(WR0)::value, wnum = decltype(WN)::value;
+      constexpr bool LT_SLICE = wr0 == 0;  // slice 3 (token loads at MFMAs 0-7)
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
         const int i = m >> 2, j = m & 3;
         if (j < NJ)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
-        if ((m & 1) == 0 && RD) rd(buf ^ 1, rs, rh, m >> 1);
-        if ((m & 3) == 1 && LD) dma(ls, lh, m >> 2);
+        if ((m & 1) == 0 && RD) rd(buf ^ 1, wb, tb, rn, m >> 1);
+        // (every token load of a step precedes every weight load issued in
+        // the same slice: the waits count the weight loads as the last ones)
+        if (m < 8 && LT) dma(ts, 1, m, 3 + (ts & 1));
+        if (wnum == 4 && m >= 8 && (m & 1) == 0 && LW) dma(ws, 0, wr0 + ((m - 8) >> 1), wsb);
+        if (wnum == 2 && m == (LT_SLICE ? 10 : 4) && LW) dma(ws, 0, wr0, wsb);
+        if (wnum == 2 && m == (LT_SLICE ? 14 : 12) && LW) dma(ws, 0, wr0 + 1, wsb);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
 #pragma unroll
-    for (int n = 0; n < 8; ++n) rd(0, 0, 0, n);
-    // K step k:  half 0 computes (k, 0) while reading (k, 1) and loading the
-    // token rows of step k+NS-2 into the stage of step k-2;  then every wave
-    // waits for its loads of step k+1 and a barrier publishes that stage and
-    // ends all reads of step k-1;  half 1 computes (k, 1) while reading
-    // (k+1, 0) and loading the weight rows of step k+NS-1 into the stage of
-    // step k-1.  Loads complete in issue order, so after half 0 of step k the
-    // loads still allowed in flight are those of steps k+2 .. k+NS-2.
-    // The steps 1 .. nk-NS run with every read and load present and take the
-    // branch-free body; the first and the last NS-1 steps decide at run time.
-    auto step = [&](int k) {
-      half_step(0, std::true_type(), k, 1, k >= 1 && k + NS - 2 < nk, k + NS - 2, 1);
-      if (k + NS - 2 < nk) WAIT_VMCNT((NS - 3) * 8); else WAIT_VMCNT(0);
+    for (int q = 0; q < 8; ++q) rd(0, 0, 0, 0, q);
+    using I0 = std::integral_constant<int, 0>;
+    using I2 = std::integral_constant<int, 2>;
+    using I4 = std::integral_constant<int, 4>;
+    using I6 = std::integral_constant<int, 6>;
+    // K step s in weight buffer w = s % 3 and token buffer t = s % 2:
+    // slices 0-2 compute while reading slices 1-3, and load part of the
+    // weight rows of step s+2 into the buffer freed one step earlier (gate/up:
+    // rows 4-7 in slices 0-1; down projection: rows 2-7 in slices 0-2); then
+    // every wave waits for its loads of step s+1 (the weights of step s+2,
+    // issued after every token load, may stay in flight) and a barrier
+    // publishes that step and ends all reads of step s (slice 3's fragments
+    // are already in registers); slice 3 computes while reading slice 0 of
+    // step s+1 and loading the tokens of step s+2 and the first weight rows
+    // of step s+3 (gate/up 0-3, down 0-1) into the buffers just freed.
+    // Spreading the loads over the slices keeps the matrix cores issuing
+    // (measured: one burst per step was slower).  Step 0 takes no weight rows
+    // in slices 0-2 (the prologue loaded all of step 2); the steps 1 .. nk-4
+    // take the branch-free body; the last three decide at run time.
+    auto step = [&](int s, int w, auto W2, auto NX, auto LT, auto LW, bool wait_all)
+        __attribute__((always_inline)) {
+      const int w1 = w == 2 ? 0 : w + 1, wp = w == 0 ? 2 : w - 1, t = s & 1;
+      if constexpr (GATED) {  // weight rows 0-3 | 4-5, 6-7
+        slice(0, std::true_type(), w, t, 1, std::false_type(), 0, W2, s + 2, wp, I4(), I2());
+        slice(1, std::true_type(), w, t, 2, std::false_type(), 0, W2, s + 2, wp, I6(), I2());
+        slice(0, std::true_type(), w, t, 3, std::false_type(), 0, std::false_type(), 0, 0, I0(), I0());
+      } else {  // weight rows 0-1 | 2-3, 4-5, 6-7
+        slice(0, std::true_type(), w, t, 1, std::false_type(), 0, W2, s + 2, wp, I2(), I2());
+        slice(1, std::true_type(), w, t, 2, std::false_type(), 0, W2, s + 2, wp, I4(), I2());
+        slice(0, std::true_type(), w, t, 3, std::false_type(), 0, W2, s + 2, wp, I6(), I2());
+      }
+      if (wait_all) WAIT_VMCNT(0); else WAIT_VMCNT(8);
       GG_BARRIER();
-      half_step(1, k + 1 < nk, k + 1, 0, k + NS - 1 < nk, k + NS - 1, 0);
+      slice(1, NX, w1, t ^ 1, 0, LT, s + 2, LW, s + 3, w, I0(),
+            std::integral_constant<int, GATED ? 4 : 2>());
+      return w1;
     };
-    int k = 0;
-    if (nk > 0) step(k++);
-    for (; k + NS - 1 < nk; ++k) {
-      half_step(0, std::true_type(), k, 1, std::true_type(), k + NS - 2, 1);
-      WAIT_VMCNT((NS - 3) * 8);
-      GG_BARRIER();
-      half_step(1, std::true_type(), k + 1, 0, std::true_type(), k + NS - 1, 0);
-    }
-    for (; k < nk; ++k) step(k);
+    int s = 0, w = 0;
+    if (nk > 3) w = step(s++, w, std::false_type(), std::true_type(), std::true_type(), std::true_type(), false);
+    for (; s + 3 < nk; ++s)
+      w = step(s, w, std::true_type(), std::true_type(), std::true_type(), std::true_type(), false);
+    for (; s < nk; ++s)
+      w = step(s, w, s >= 1 && s + 2 < nk, s + 1 < nk, s + 2 < nk, false, s + 2 >= nk);
   };
 
   int round = 0;
   Tile cur, nxt;
   if (!locate(round, cur)) return;
   {
-    int pv[4];
+    int pv[8];
     load_perm(cur, pv);
     set_tile(cur, pv);
   }
   prologue(cur.nk);
   // one tile for waves that compute NJ token blocks; returns whether a next
   // tile exists (then its first stages are in flight)
-  auto tile = [&](auto NJc) -> bool {
+  auto tile = [&](auto NJc) __attribute__((always_inline)) -> bool {
     f32x16 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -408,19 +502,21 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
     // the next tile, located and its token rows looked up while this one
     // computes (those loads precede the K loop's and only strengthen its waits)
     const bool more = locate(round + 1, nxt);
-    int pn[4] = {0, 0, 0, 0};
+    int pn[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (more) load_perm(nxt, pn);
     kloop(NJc, acc, cur.nk);
     // every load of the tile has landed; end every wave's reads of the ring,
-    // then start the next tile's first stages under this tile's epilogue
+    // then (gate/up) start the next tile's first K steps under this tile's
+    // epilogue; the down projection stages its output in the weight buffers
+    // and starts them after it
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (more) {
       set_tile(nxt, pn);
-      prologue(nxt.nk);
+      if (GATED) prologue(nxt.nk);
     }
     // read each accumulator where it is used: left to itself the compiler
     // copies all of them to VGPRs at once and spills
-    auto from_acc = [&](int i, int j, int q) -> f32x4 {
+    auto from_acc = [&](int i, int j, int q) __attribute__((always_inline)) -> f32x4 {
       f32x4 v;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -431,8 +527,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
       return v;
     };
     if (cur.np < 2) {
-      write_tile<GATED>(cur, [](int) {}, from_acc, out, F, H, plane, (uint8_t*)&lds[kStageOut],
-                        wave);
+      write_tile<GATED>(cur, [](int) {}, from_acc, out, F, H, plane, (uint8_t*)&lds[0], wave);
     } else {  // a piece: its partial sums, for the launch that finishes the tile
       f32x4* dst = part_base(ws, xcd * nw + jw, wave);
 #pragma unroll
@@ -442,22 +537,34 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
 #pragma unroll
           for (int q = 0; q < 4; ++q) dst[((i * 4 + j) * 4 + q) * 64] = from_acc(i, j, q);
     }
+    if (!GATED && more) {
+      // every wave is done with the output staging
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      prologue(nxt.nk);
+    }
     return more;
   };
   for (;;) {
-    // this tile's first NS-1 stages have landed (and the previous tile's
-    // output stores have completed, as vmcnt counts both); the barrier also
-    // ends every wave's reads of the previous tile's output staging
+    // this tile's first stages have landed (and the previous tile's output
+    // stores have completed, as vmcnt counts both); the barrier also ends
+    // every wave's reads of the previous tile's output staging
     WAIT_VMCNT(0);
     GG_BARRIER();
     const int nb = (cur.rows + 31) >> 5;        // 32-row token blocks in the tile
     const int nj = max((nb - wn + 1) >> 1, 1);  // this wave's (at least one)
     bool more;
-    switch (nj) {
-      case 1: more = tile(std::integral_constant<int, 1>()); break;
-      case 2: more = tile(std::integral_constant<int, 2>()); break;
-      case 3: more = tile(std::integral_constant<int, 3>()); break;
-      default: more = tile(std::integral_constant<int, 4>()); break;
+    if (GATED) {
+      switch (nj) {
+        case 1: more = tile(std::integral_constant<int, 1>()); break;
+        case 2: more = tile(std::integral_constant<int, 2>()); break;
+        case 3: more = tile(std::integral_constant<int, 3>()); break;
+        default: more = tile(std::integral_constant<int, 4>()); break;
+      }
+    } else {
+      // the down projection computes every token block: with several K loop
+      // variants in one kernel the compiler no longer keeps its accumulators
+      // in place (it copies all of them every K step)
+      more = tile(std::integral_constant<int, 4>());
     }
     if (!more) break;
     cur = nxt;
@@ -527,14 +634,14 @@ int grouped_down_ksplit(const ExpertArgs& a) {
 }
 
 int launch_grouped_gate_up(const ExpertArgs& a, hipStream_t st) {
-  grouped_gemm_kernel<true, kNS><<<persistent_grid(), 256, 0, st>>>(
+  grouped_gemm_kernel<true><<<persistent_grid(), 256, 0, st>>>(
       (const uint16_t*)a.experts, a.stride_elems, (const uint16_t*)a.x, a.perm, a.k, a.offsets,
       a.tile_off, a.E, a.H, a.F, a.T, 1, 0, a.act, nullptr);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_grouped_down(const ExpertArgs& a, int ksplit, hipStream_t st) {
-  grouped_gemm_kernel<false, kNS><<<persistent_grid(), 256, 0, st>>>(
+  grouped_gemm_kernel<false><<<persistent_grid(), 256, 0, st>>>(
       (const uint16_t*)a.experts, a.stride_elems, (const uint16_t*)a.act, a.perm, a.k,
       a.offsets, a.tile_off, a.E, a.H, a.F, a.T, ksplit, (size_t)a.S * a.H, a.yp, a.gws);
   if (a.gws)
