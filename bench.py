@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the 32-layer stacked decode (90 GB of experts)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the 64-expert and 128-expert layers")
     ap.add_argument("--decode-batches", default="1,4,16,64",
                     help="decode / stacked-decode batch sizes to run (comma-separated, "
                          "from 1,4,16,64; a subset isolates one batch size in a kernel trace)")
@@ -121,6 +123,115 @@ def stage_times(layer, x, y, T, steps, warm):
     torch.cuda.synchronize()
     return [sum(evs[i][s].elapsed_time(evs[i][s + 1]) for i in range(steps)) / steps
             for s in range(nst)]
+
+
+def routing_stats(shape, x_h, wr_h, b_h, counts):
+    """Per-config routing report: the experts' token loads (from the GPU's own
+    dispatch) and the near ties, tokens whose k-th and (k+1)-th largest logit
+    differ by less than 1e-3 (logits in float64 from the stored bf16 values;
+    a statistic of the inputs, not a step of the path)."""
+    import numpy as np
+
+    import gen
+    c = np.asarray(counts, dtype=np.int64)
+    out = {"experts_touched": int((c > 0).sum()), "load_min": int(c.min()),
+           "load_median": float(np.median(c)), "load_max": int(c.max())}
+    if shape.k < shape.E:
+        xs = gen.bf16_bits_to_f32(x_h).astype(np.float64)
+        ws = gen.bf16_bits_to_f32(wr_h).astype(np.float64)
+        lg = xs @ ws
+        if b_h is not None:
+            lg += b_h.astype(np.float64)[None, :]
+        srt = -np.sort(-lg, axis=1)
+        out["near_ties"] = int((srt[:, shape.k - 1] - srt[:, shape.k] < 1e-3).sum())
+    return out
+
+
+def time_layer(layer, x, y, T, steps, warm, stream):
+    """Wall time of `steps` forwards (after `warm`), and the mean per-stage and
+    whole-step device times (ms) from the library's per-stage HIP events."""
+    import torch
+
+    import mixture_experts_amd as moe
+    nst = moe.MOE_NUM_STAGES
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(steps)]
+    for row in evs:  # materialise the event handles
+        for e in row:
+            e.record(stream)
+    for _ in range(warm):
+        moe.moe_forward(layer.handle, x, T, y, stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        moe.moe_forward_ev(layer.handle, x, T, y, stream, [e.cuda_event for e in evs[i]])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = [sum(evs[i][s].elapsed_time(evs[i][s + 1]) for i in range(steps)) / steps
+                for s in range(nst)]
+    dev_ms = sum(evs[i][0].elapsed_time(evs[i][nst]) for i in range(steps)) / steps
+    return wall, stage_ms, dev_ms
+
+
+def gate_up_roofline(shape, T, touched, t_gu_s):
+    """Roofline of the gate/up launch: algorithmic flops 4*T*k*H*F and bytes
+    (touched experts' gate and up weights once, token rows in, activation
+    out); bound MFMA above the ridge (2.5 PF / 8 TB/s = 312.5 flop/B), else
+    HBM; the other fraction is reported beside it."""
+    S = T * shape.k
+    flops = 4.0 * S * shape.H * shape.F
+    byts = touched * 2.0 * shape.H * shape.F * 2 + T * shape.H * 2.0 + S * shape.F * 2.0
+    tf = flops / t_gu_s / 1e12
+    gbs = byts / t_gu_s / 1e9
+    if flops / byts >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        return {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
+def bench_workload(shape, T, K, W):
+    """One layer of another shape (the 64-expert and the Zipf-skewed
+    128-expert layers): tokens/s, stage times, the gate/up roofline and the
+    layer's fractions of both peaks over its algorithmic work."""
+    import numpy as np
+    import torch
+
+    import gen
+    import mixture_experts_amd as moe
+    st = torch.cuda.current_stream()
+    x_h, wr_h, b_h = gen.gen_x(shape, T), gen.gen_router(shape), gen.gen_bias(shape)
+    x = torch.from_numpy(x_h.view(np.int16)).cuda()
+    wr = torch.from_numpy(wr_h.view(np.int16)).cuda()
+    bias = None if b_h is None else torch.from_numpy(b_h).cuda()
+    ex = torch.empty(shape.E * shape.stride, dtype=torch.uint8, device="cuda")
+    gen.experts_device(shape, ex.data_ptr(), stream=st.cuda_stream)
+    layer = moe.MoELayer(shape.H, shape.F, shape.E, shape.k, T, moe.MOE_BF16, wr, ex,
+                         shape.stride, bias)
+    y = torch.empty((T, shape.H), dtype=torch.float32, device="cuda")
+    wall, stage_ms, dev_ms = time_layer(layer, x, y, T, K, W, st)
+    r = layer.route(x, T)
+    torch.cuda.synchronize()
+    counts = r["counts"].cpu().numpy()
+    touched = int((counts > 0).sum())
+    S = T * shape.k
+    flops = 6.0 * S * shape.H * shape.F + 2.0 * T * shape.H * shape.E
+    byts = touched * 3.0 * shape.H * shape.F * 2 + shape.H * shape.E * 2.0 + T * shape.H * (2 + 4)
+    dev_s = dev_ms * 1e-3
+    res = {"tokens": T, "hidden": shape.H, "ffn": shape.F, "experts": shape.E,
+           "top_k": shape.k, "router_bias": shape.bias,
+           "tokens_per_s": round(T * K / wall, 1), "ms_per_step": round(wall / K * 1e3, 4),
+           "step_device_ms": round(dev_ms, 4),
+           "stages_ms": {n: round(v, 4) for n, v in zip(moe.STAGE_NAMES, stage_ms)},
+           "roofline": gate_up_roofline(shape, T, touched,
+                                        stage_ms[moe.MOE_STAGE_GATE_UP] * 1e-3),
+           "layer_hbm_frac": round(byts / dev_s / 1e9 / PEAK_HBM_GBS, 4),
+           "layer_mfma_frac": round(flops / dev_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "routing": routing_stats(shape, x_h, wr_h, b_h, counts)}
+    layer.close()
+    del ex
+    torch.cuda.empty_cache()
+    return res
 
 
 DECODE_BATCHES = (1, 4, 16, 64)
@@ -306,49 +417,17 @@ def main():
     y = torch.empty((T, shape.H), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     K, W = args.steps, args.warmup
-    nst = moe.MOE_NUM_STAGES
-
-    def run(xx, yy, TT, steps, warm):
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(steps)]
-        for row in evs:  # materialise the event handles
-            for e in row:
-                e.record(stream)
-        for _ in range(warm):
-            moe.moe_forward(layer.handle, xx, TT, yy, stream)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(steps):
-            moe.moe_forward_ev(layer.handle, xx, TT, yy, stream, [e.cuda_event for e in evs[i]])
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        stage_ms = [sum(evs[i][s].elapsed_time(evs[i][s + 1]) for i in range(steps)) / steps
-                    for s in range(nst)]
-        dev_ms = sum(evs[i][0].elapsed_time(evs[i][nst]) for i in range(steps)) / steps
-        return wall, stage_ms, dev_ms
 
     print(f"[bench] prefill: {W} warmup + {K} timed steps", file=sys.stderr, flush=True)
-    wall, stage_ms, dev_ms = run(x, y, T, K, W)
+    wall, stage_ms, dev_ms = time_layer(layer, x, y, T, K, W, stream)
     tok_s = T * K / wall
     S = T * shape.k
-    gu_flops = 4.0 * S * shape.H * shape.F
-    dn_flops = 2.0 * S * shape.H * shape.F
-    t_gu = stage_ms[moe.MOE_STAGE_GATE_UP] * 1e-3
-    step_flops = gu_flops + dn_flops + 2.0 * T * shape.H * shape.E
-    # the gate/up launch's roofline: algorithmic bytes = the touched experts'
-    # gate and up weights once + the token rows in + the activation out; the
-    # bound is MFMA above the ridge (2.5 PF / 8 TB/s = 312.5 flop/B), else HBM
+    step_flops = 6.0 * S * shape.H * shape.F + 2.0 * T * shape.H * shape.E
     r = layer.route(x, T)
-    touched = int((r["counts"] > 0).sum().item())
-    gu_bytes = touched * 2.0 * shape.H * shape.F * 2 + T * shape.H * 2.0 + S * shape.F * 2.0
+    counts = r["counts"].cpu().numpy()
+    touched = int((counts > 0).sum())
     streaming = S <= 32 * shape.E  # the library's path choice
-    if gu_flops / gu_bytes >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
-        roof = {"bound": "mfma", "achieved": round(gu_flops / t_gu / 1e12, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(gu_flops / t_gu / 1e12 / PEAK_BF16_TFLOPS, 4)}
-    else:
-        roof = {"bound": "hbm", "achieved": round(gu_bytes / t_gu / 1e9, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(gu_bytes / t_gu / 1e9 / PEAK_HBM_GBS, 4)}
+    roof = gate_up_roofline(shape, T, touched, stage_ms[moe.MOE_STAGE_GATE_UP] * 1e-3)
     roof["kernel"] = ("streaming" if streaming else "grouped GEMM") + " gate/up + SiLU"
     out = {
         "metric": METRIC,
@@ -372,7 +451,14 @@ def main():
         "stages_ms": {n: round(v, 4) for n, v in zip(moe.STAGE_NAMES, stage_ms)},
         "step_device_ms": round(dev_ms, 4),
         "step_tflops": round(step_flops / (dev_ms * 1e-3) / 1e12, 2),
+        "step_mfma_frac": round(step_flops / (dev_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "routing": routing_stats(shape, x_h, wr_h, b_h, counts),
     }
+
+    if not args.no_workloads and args.workload == "mixtral_prefill":
+        print("[bench] 64-expert and 128-expert layers", file=sys.stderr, flush=True)
+        out["workloads"] = {"qwen2_moe_layer_T512": bench_workload(gen.QWEN, 512, K, W),
+                            "deepseek_moe_layer_T8192": bench_workload(gen.DEEPSEEK, 8192, K, W)}
 
     if not args.no_decode and args.workload == "mixtral_prefill":
         print("[bench] decode batches, bf16 and uint8 experts", file=sys.stderr, flush=True)
@@ -388,20 +474,40 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         orc = oracle.layer_from_gen(shape, wr_h, b_h, ex_h)
-        n, el = 2, 0.0
-        while True:
-            toks = np.arange(n, dtype=np.int32) * (T // n)
-            t0 = time.perf_counter()
-            orc.tokens(x_h, toks)
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds / 4 or n >= 1024:
-                break
-            n = min(1024, max(n * 2, int(n * args.cpu_seconds / 2 / max(el, 1e-3))))
+
+        def sample_rate(seconds):
+            """Tokens/s of the oracle over an evenly spread sample of tokens,
+            grown until it takes about `seconds` / 4 or more."""
+            n, el = 1, 0.0
+            while True:
+                toks = np.arange(n, dtype=np.int32) * (T // n)
+                t0 = time.perf_counter()
+                orc.tokens(x_h, toks)
+                el = time.perf_counter() - t0
+                if el >= seconds / 4 or n >= 1024:
+                    return n, el
+                n = min(1024, max(n * 2, int(n * seconds / 2 / max(el, 1e-3))))
+
+        threads = oracle.num_threads()
+        n, el = sample_rate(args.cpu_seconds)
+        oracle.set_num_threads(1)
+        n1, el1 = sample_rate(args.cpu_seconds / 2)
+        oracle.set_num_threads(threads)
+        model = ""
+        try:
+            with open("/proc/cpuinfo") as f:
+                model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+        except OSError:
+            pass
+        what = f"full layer per token (router, top-k, {shape.k} experts, combine), fp64"
         out["cpu_baseline"] = {"value": round(n / el, 3), "unit": "tokens/s",
-                               "cores": oracle.num_threads(), "kind": "oracle",
-                               "sample": f"{n} of the {T} tokens, full layer per token "
-                                         f"(router, top-k, {shape.k} experts, combine), fp64",
-                               "seconds": round(el, 2)}
+                               "cores": threads, "kind": "oracle",
+                               "sample": f"{n} of the {T} tokens, {what}",
+                               "seconds": round(el, 2), "cpu_model": model,
+                               "single_thread": {"value": round(n1 / el1, 3),
+                                                 "unit": "tokens/s", "cores": 1,
+                                                 "sample": f"{n1} of the {T} tokens, {what}",
+                                                 "seconds": round(el1, 2)}}
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)

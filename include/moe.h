@@ -38,6 +38,13 @@
  *   - One call in flight per layer (calls share the layer's workspace):
  *     create one layer per concurrent stream.  Results are bitwise
  *     reproducible for identical inputs (no floating-point atomics).
+ *   - bf16 batches of up to 64 tokens route and dispatch in one launch whose
+ *     workgroups count their completion in a counter in the workspace (for
+ *     moe_forward_noalloc, in its device array); every launch that runs to
+ *     completion leaves it at zero.  A launch that does not complete (a
+ *     device fault) leaves it wrong and later small-batch calls on that
+ *     workspace would skip their dispatch; as the device context has to be
+ *     re-created after a fault anyway, create the layer anew with it.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -71,9 +78,15 @@ enum {
    *   Wg [F][H], Wu [F][H], Wd [H][F]   uint8 (same orientation as above)
    *   at byte 3*H*F: moe_u8_params (64 bytes)
    * and expert_stride >= 3*H*F + 64 (a multiple of 256).  bf16 layers only;
-   * x, the router and the activation stay bf16, the expert FFN runs on the
-   * weight-streaming kernels for every batch size (MOE_FLAG_PATH_GROUPED is
-   * unsupported), which read one byte per weight. */
+   * x and the router stay bf16.  The expert FFN runs on the weight-streaming
+   * kernels for every batch size (MOE_FLAG_PATH_GROUPED is unsupported),
+   * which read one byte per weight and take their token operands in fp16:
+   * the layer input is converted once from bf16 to fp16, and the SwiGLU
+   * activation is rounded to bf16 and then stored as fp16, both conversions
+   * rounding toward zero.  For magnitudes in fp16's normal range
+   * [2^-14, 65504] they are exact (such bf16 values are fp16 values);
+   * smaller magnitudes keep an absolute error below 2^-24 (fp16 subnormals)
+   * and larger ones saturate to +-65504. */
   MOE_EXPERT_U8 = 1
 };
 
@@ -131,7 +144,14 @@ typedef struct {
                                Wu [F][H]  up_proj
                                Wd [H][F]  down_proj
                              so g_f = sum_h x_h Wg[f][h] and
-                             y_h = sum_f a_f Wd[h][f] */
+                             y_h = sum_f a_f Wd[h][f].  This output-major
+                             orientation is that of the pages' weight format
+                             (gate/up stored (intermediate, hidden), down
+                             (hidden, intermediate) [zskr.cn page sec. 3.1]),
+                             chosen deliberately over input-major
+                             [Wg H x F][Wu H x F][Wd F x H]: both GEMMs then
+                             read K-contiguous rows.  A caller holding
+                             input-major matrices transposes them once. */
   uint64_t expert_stride; /* bytes, >= 3*H*F*sizeof(dtype), multiple of 256 */
   int32_t expert_capacity;/* (token, slot) pairs an expert takes per call, 0 = no
                              limit.  Pairs beyond it are dropped: the pairs of

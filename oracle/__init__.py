@@ -60,6 +60,8 @@ def lib():
         L.orc_bf16_round.argtypes = [ctypes.c_double]
         L.orc_bf16_round.restype = ctypes.c_double
         L.orc_num_threads.argtypes = []
+        L.orc_set_num_threads.argtypes = [i32]
+        L.orc_set_num_threads.restype = None
         _LIB = L
     return _LIB
 
@@ -203,6 +205,11 @@ def bf16_round(v: float) -> float:
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's later parallel loops (timing only)."""
+    lib().orc_set_num_threads(n)
 
 
 def layer_from_gen(shape, router_w, router_b, experts, gate="softmax", capacity=0,

@@ -28,6 +28,14 @@ int orc_num_threads(void) {
 #endif
 }
 
+void orc_set_num_threads(int32_t n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* exact widening of one stored element to double */
 static double widen(const void* base, int32_t dtype, size_t i) {
   if (dtype == ORC_F32) return (double)((const float*)base)[i];

@@ -123,6 +123,8 @@ int orc_quantize_experts_u8(const void* src, uint64_t src_stride, int32_t E, int
                             int32_t F, void* dst, uint64_t dst_stride);
 double orc_bf16_round(double v);
 int orc_num_threads(void);
+/* Threads of later OpenMP regions (timing only; results do not depend on it). */
+void orc_set_num_threads(int32_t n);
 
 #ifdef __cplusplus
 }
