@@ -131,7 +131,8 @@ typedef struct {
   int32_t hidden;         /* H: model width */
   int32_t ffn;            /* F: expert FFN width */
   int32_t num_experts;    /* E: 1..256 */
-  int32_t top_k;          /* k: 1..min(E, 8) */
+  int32_t top_k;          /* k: 1..E (k = E: soft routing, every expert
+                             weighted by the softmax of all logits) */
   int32_t max_tokens;     /* largest T any call will pass: 1..65536 */
   int32_t dtype;          /* moe_dtype of x, router_w, the experts and the
                              stored SwiGLU activation */
@@ -169,8 +170,9 @@ typedef struct {
  * device and returns the layer, or NULL with *status (if non-NULL) set to the
  * error.  Shape limits of the kernels (else MOE_ERR_UNSUPPORTED): bf16 layers
  * need H % 256 == 0 and F % 128 == 0; fp32 layers H % 4 == 0 and F % 4 == 0;
- * E <= 256, k <= 8; max_tokens*k*max(H, F), max_tokens*H and 3*H*F below
- * 2^31.  Nothing is launched. */
+ * E <= 256; max_tokens*k*max(H, F), max_tokens*H and 3*H*F below 2^31.
+ * (k > 8 selects by ranks; bf16 batches of up to 64 tokens then route and
+ * dispatch in separate launches.)  Nothing is launched. */
 moe_layer_t* moe_layer_create(const moe_layer_desc* d, int* status);
 
 /* Steps 1-3 only, with their results copied out (for inspection and tests).

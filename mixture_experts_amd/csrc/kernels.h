@@ -5,6 +5,8 @@
 #include <stdint.h>
 
 #define MOE_MAX_EXPERTS 256
+// picks per token of the pick-by-pick top-k (the small-batch routes); beyond
+// it the top-k selects by ranks
 #define MOE_MAX_TOPK 8
 #define DISPATCH_RUN 512  // slots per histogram run
 

@@ -93,7 +93,7 @@ int validate_desc(const moe_layer_desc* d) {
   if (d->expert_stride < need || (d->expert_stride & 255u)) return MOE_ERR_INVALID_ARG;
   if (u8 && (d->dtype != MOE_BF16 || (d->flags & MOE_FLAG_PATH_GROUPED)))
     return MOE_ERR_UNSUPPORTED;
-  if (d->num_experts > MOE_MAX_EXPERTS || d->top_k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if (d->num_experts > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
   if (d->dtype == MOE_BF16 && (H % 256 || F % 128)) return MOE_ERR_UNSUPPORTED;
   if (d->dtype == MOE_F32 && (H % 4 || F % 4)) return MOE_ERR_UNSUPPORTED;
   if ((d->flags & MOE_FLAG_RESIDUAL_PRENORM) && (d->dtype != MOE_BF16 || H > 16384))
@@ -177,9 +177,10 @@ bool use_stream_path(const moe_layer* L, int T) {
   return (int64_t)T * L->d.top_k <= 32 * (int64_t)L->d.num_experts;
 }
 
-// Routing and dispatch in one launch (bf16 layers, one token tile).
+// Routing and dispatch in one launch (bf16 layers, one token tile, up to
+// MOE_MAX_TOPK picks per token).
 bool small_route(const moe_layer* L, int T, const float* logits_in) {
-  return L->d.dtype == MOE_BF16 && !logits_in && T <= 64;
+  return L->d.dtype == MOE_BF16 && !logits_in && T <= 64 && L->d.top_k <= MOE_MAX_TOPK;
 }
 
 // Steps 1-3 into the workspace.  x_route is the routing input (bf16 branch

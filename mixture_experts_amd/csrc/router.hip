@@ -62,14 +62,78 @@ __device__ __forceinline__ Cand wave_best(Cand c) {
 }
 #undef DPP_CAND
 
+// Top-k of one token by ranks, for k > MOE_MAX_TOPK (up to every expert:
+// soft routing): the rank of expert e is the number of experts that beat it
+// ((value desc, index asc), the same total order as the picks below), the k
+// best take the slots 0..k-1 by rank, and the softmax adds the exponentials
+// in slot order (lane 0, from ex_lds: [k] doubles of this wave).
+__device__ void topk_rank_row(const float* row, int t, int E, int k, int raw, int32_t* idx_out,
+                              float* w_out, double* ex_lds) {
+  const int lane = threadIdx.x & 63;
+  float v[4];
+  int rnk[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int e = lane + 64 * c;
+    v[c] = (e < E) ? row[e] : 0.0f;
+    rnk[c] = 0;
+  }
+  for (int e2 = 0; e2 < E; ++e2) {
+    const float v2 = row[e2];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) rnk[c] += (v2 > v[c]) | ((v2 == v[c]) & (e2 < lane + 64 * c));
+  }
+  // the largest logit (the pick of slot 0), for the softmax
+  float m = v[0];
+#pragma unroll
+  for (int c = 1; c < 4; ++c)
+    if (lane + 64 * c < E) m = fmaxf(m, v[c]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int e = lane + 64 * c;
+    if (e < E && rnk[c] < k) {
+      idx_out[(size_t)t * k + rnk[c]] = e;
+      if (!raw) ex_lds[rnk[c]] = exp((double)v[c] - (double)m);
+    }
+  }
+  if (raw) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (lane + 64 * c < E && rnk[c] < k) w_out[(size_t)t * k + rnk[c]] = v[c];
+    return;
+  }
+  __builtin_amdgcn_wave_barrier();
+  double z = 0.0;
+  if (lane == 0)
+    for (int j = 0; j < k; ++j) z += ex_lds[j];
+  z = __shfl(z, 0);
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    if (lane + 64 * c < E && rnk[c] < k) w_out[(size_t)t * k + rnk[c]] = (float)(ex_lds[rnk[c]] / z);
+  __builtin_amdgcn_wave_barrier();  // ex_lds is free for this wave's next token
+}
+
 // Top-k + softmax of tokens tile0 + wave, tile0 + wave + nwaves, ... below
 // tile0 + rows (interleaved so that small batches still spread over the
 // waves).  lg: LDS logits [rows][ldl].  idx_lds (optional): an LDS copy of the
-// picks of the tile, [RT_TOK][k].
+// picks of the tile, [RT_TOK][k].  k > MOE_MAX_TOPK takes topk_rank_row with
+// ex_lds: [nwaves][MOE_MAX_EXPERTS] doubles of LDS.
 __device__ void topk_rows(const float* lg, int ldl, int tile0, int T, int E, int k, int raw,
                           int32_t* idx_out, float* w_out, int nwaves = 4,
-                          int32_t* idx_lds = nullptr, int rows = RT_TOK) {
+                          int32_t* idx_lds = nullptr, int rows = RT_TOK,
+                          double* ex_lds = nullptr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (k > MOE_MAX_TOPK) {
+    for (int r = wave; r < rows; r += nwaves) {
+      const int t = tile0 + r;
+      if (t >= T) break;
+      topk_rank_row(lg + (size_t)r * ldl, t, E, k, raw, idx_out, w_out,
+                    ex_lds + wave * MOE_MAX_EXPERTS);
+    }
+    return;
+  }
   for (int r = wave; r < rows; r += nwaves) {
     const int t = tile0 + r;
     if (t >= T) break;
@@ -423,6 +487,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
                                                           int32_t* __restrict__ idx_out,
                                                           float* __restrict__ w_out) {
   __shared__ float lg[RK_TOK * (MOE_MAX_EXPERTS + 1)];
+  __shared__ double exs[4 * MOE_MAX_EXPERTS];  // (k > MOE_MAX_TOPK only)
   const int ldl = E + 1;
   const int tid = threadIdx.x;
   const int tile0 = blockIdx.x * RK_TOK;
@@ -441,7 +506,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     lg[r * ldl + e] = s;
   }
   __syncthreads();
-  topk_rows(lg, ldl, tile0, T, E, k, raw, idx_out, w_out, 4, nullptr, RK_TOK);
+  topk_rows(lg, ldl, tile0, T, E, k, raw, idx_out, w_out, 4, nullptr, RK_TOK, exs);
 }
 
 __global__ __launch_bounds__(256) void router_f32_kernel(
@@ -450,6 +515,7 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
     const float* __restrict__ logits_in, int32_t* __restrict__ idx_out,
     float* __restrict__ w_out) {
   __shared__ float lg[RT_TOK * 257];
+  __shared__ double exs[4 * MOE_MAX_EXPERTS];  // (k > MOE_MAX_TOPK only)
   const int ldl = E + 1;
   const int tid = threadIdx.x, wave = tid >> 6;
   const int tile0 = blockIdx.x * RT_TOK;
@@ -467,7 +533,7 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
     lg[r * ldl + e] = s;
   }
   __syncthreads();
-  topk_rows(lg, ldl, tile0, T, E, k, raw, idx_out, w_out);
+  topk_rows(lg, ldl, tile0, T, E, k, raw, idx_out, w_out, 4, nullptr, RT_TOK, exs);
 }
 
 // Branch input of a stacked layer: xt[t] = bf16(h[t] / sqrt(mean(h[t]^2) + 1e-6)),

@@ -66,7 +66,8 @@ def _desc(**kw):
     (dict(expert_capacity=-1), moe.MOE_ERR_INVALID_ARG),
     (dict(flags=moe.MOE_FLAG_PATH_GROUPED | moe.MOE_FLAG_PATH_STREAM), moe.MOE_ERR_INVALID_ARG),
     (dict(num_experts=300, top_k=2), moe.MOE_ERR_UNSUPPORTED),
-    (dict(top_k=9, num_experts=16), moe.MOE_ERR_UNSUPPORTED),
+    # soft routing (k = E) is supported, but its T*k rows must fit the workspace limits
+    (dict(top_k=256, num_experts=256, max_tokens=65536), moe.MOE_ERR_UNSUPPORTED),
     (dict(hidden=320, expert_stride=3 * 320 * 256 * 2), moe.MOE_ERR_UNSUPPORTED),
     (dict(ffn=192, expert_stride=3 * 256 * 192 * 2), moe.MOE_ERR_UNSUPPORTED),
     (dict(dtype=moe.MOE_F32, hidden=6, ffn=8, expert_stride=768), moe.MOE_ERR_UNSUPPORTED),

@@ -47,7 +47,10 @@ def f32_shape(E, k, H=8, F=8):
                                    (1, 1, 40), (256, 1, 3),
                                    # 8192 pairs: the one-workgroup dispatch at its largest;
                                    # 8194: the three dispatch kernels
-                                   (256, 8, 1024), (16, 2, 4097)])
+                                   (256, 8, 1024), (16, 2, 4097),
+                                   # k > 8: selection by ranks (soft routing at k = E)
+                                   (64, 64, 50), (128, 128, 20), (64, 12, 300), (200, 33, 40),
+                                   (256, 256, 3)])
 def test_route_given_logits_bit_exact(E, k, T):
     _log("route given logits", E, k, T)
     rng = np.random.default_rng(E * 1000 + T)
@@ -64,7 +67,8 @@ def test_route_given_logits_bit_exact(E, k, T):
     c.close()
 
 
-@pytest.mark.parametrize("E,k,T", [(8, 2, 1), (8, 2, 300), (64, 2, 97), (256, 8, 40)])
+@pytest.mark.parametrize("E,k,T", [(8, 2, 1), (8, 2, 300), (64, 2, 97), (256, 8, 40),
+                                   (64, 16, 97), (128, 128, 9)])
 def test_route_raw_gate_given_logits_bit_exact(E, k, T):
     """Raw gate: the same selection; the weights are the given fp32 logits."""
     rng = np.random.default_rng(7 * E + T)
@@ -137,6 +141,15 @@ SMALL = [
     ("bf16", 512, 256, 8, 8, 50, moe.MOE_FLAG_PATH_STREAM),
     ("bf16", 512, 256, 8, 8, 300, moe.MOE_FLAG_PATH_GROUPED),
     ("f32", 64, 128, 6, 6, 32, 0),
+    # soft routing over the 64- and 128-expert workloads' expert counts (k > 8:
+    # selection by ranks; small batches route in separate launches)
+    ("bf16", 256, 128, 64, 64, 20, 0),
+    ("bf16", 256, 128, 64, 64, 100, 0),
+    ("bf16", 256, 128, 128, 128, 8, 0),
+    ("bf16", 256, 128, 128, 128, 40, moe.MOE_FLAG_PATH_GROUPED),
+    ("bf16", 512, 256, 32, 12, 70, 0),
+    ("bf16", 256, 128, 64, 16, 33, moe.MOE_FLAG_GATE_RAW),
+    ("f32", 64, 128, 16, 16, 32, 0),
     # streaming down projection with 1 KB row runs and 9-16 token rows per
     # pass (F % 512 == 0), with the combine folded in and kept apart
     ("bf16", 512, 1024, 8, 2, 16, 0),
