@@ -31,26 +31,34 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s (decode T=1..64, prefill T=4096); % HBM / bf16-MFMA peak"
 PROFILE = os.path.join(ROOT, "profiles", "grouped_gemm_mixtral_prefill_T4096.md")
-KERNEL_SRC = os.path.join(ROOT, "mixture_experts_amd", "csrc", "expert_grouped.hip")
+LAYERS_PROFILE = os.path.join(ROOT, "profiles", "layers_qwen_deepseek_shapes.md")
+CSRC = os.path.join(ROOT, "mixture_experts_amd", "csrc")
 
 
-def measured_traffic():
-    """HBM bytes per gate/up launch from the committed rocprofv3 counter summary,
-    or None when the kernel source changed since the counters were taken."""
+def measured_traffic(profile=PROFILE, key="traffic_bytes_per_launch",
+                     src="expert_grouped.hip"):
+    """HBM bytes per launch of the kernel a committed rocprofv3 counter summary
+    covers (`key`), or None when that kernel's source (`src`) changed since the
+    counters were taken."""
     import hashlib
     try:
-        text = open(PROFILE).read()
-        src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+        text = open(profile).read()
+        digest = hashlib.sha256(open(os.path.join(CSRC, src), "rb").read()).hexdigest()
     except OSError:
         return None
-    fields = dict(l.split(":", 1) for l in text.splitlines()
-                  if l.startswith(("source_sha256:", "traffic_bytes_per_launch:")))
-    if fields.get("source_sha256", "").strip() != src:
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith(("source_sha256", "traffic_bytes_per_launch")) and ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get(f"source_sha256 {src}", fields.get("source_sha256")) != digest:
         return None
     try:
-        return float(fields["traffic_bytes_per_launch"])
+        return float(fields[key])
     except (KeyError, ValueError):
         return None
+
+
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
@@ -190,7 +198,7 @@ def gate_up_roofline(shape, T, touched, t_gu_s):
             "frac": round(gbs / PEAK_HBM_GBS, 4), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)}
 
 
-def bench_workload(shape, T, K, W):
+def bench_workload(name, shape, T, K, W):
     """One layer of another shape (the 64-expert and the Zipf-skewed
     128-expert layers): tokens/s, stage times, the gate/up roofline and the
     layer's fractions of both peaks over its algorithmic work."""
@@ -215,6 +223,8 @@ def bench_workload(shape, T, K, W):
     counts = r["counts"].cpu().numpy()
     touched = int((counts > 0).sum())
     S = T * shape.k
+    streaming = S <= 32 * shape.E  # the library's path choice
+    src = "expert_stream.hip" if streaming else "expert_grouped.hip"
     flops = 6.0 * S * shape.H * shape.F + 2.0 * T * shape.H * shape.E
     byts = touched * 3.0 * shape.H * shape.F * 2 + shape.H * shape.E * 2.0 + T * shape.H * (2 + 4)
     dev_s = dev_ms * 1e-3
@@ -223,8 +233,12 @@ def bench_workload(shape, T, K, W):
            "tokens_per_s": round(T * K / wall, 1), "ms_per_step": round(wall / K * 1e3, 4),
            "step_device_ms": round(dev_ms, 4),
            "stages_ms": {n: round(v, 4) for n, v in zip(moe.STAGE_NAMES, stage_ms)},
-           "roofline": gate_up_roofline(shape, T, touched,
-                                        stage_ms[moe.MOE_STAGE_GATE_UP] * 1e-3),
+           "roofline": dict(gate_up_roofline(shape, T, touched,
+                                             stage_ms[moe.MOE_STAGE_GATE_UP] * 1e-3),
+                            kernel=("streaming" if streaming else "grouped GEMM")
+                            + " gate/up + SiLU",
+                            traffic=measured_traffic(LAYERS_PROFILE,
+                                                     "traffic_bytes_per_launch_" + name, src)),
            "layer_hbm_frac": round(byts / dev_s / 1e9 / PEAK_HBM_GBS, 4),
            "layer_mfma_frac": round(flops / dev_s / 1e12 / PEAK_BF16_TFLOPS, 4),
            "routing": routing_stats(shape, x_h, wr_h, b_h, counts)}
@@ -405,12 +419,19 @@ def main():
                 "deepseek": (gen.DEEPSEEK, 8192)}[args.workload]
     print(f"[bench] generating inputs for {shape.name} T={T}", file=sys.stderr, flush=True)
     x_h = gen.gen_x(shape, T)
-    wr_h, b_h, ex_h = gen.gen_router(shape), gen.gen_bias(shape), gen.gen_experts(shape)
+    wr_h, b_h = gen.gen_router(shape), gen.gen_bias(shape)
 
     def dev(a):
         return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
 
-    x, wr, ex = dev(x_h), dev(wr_h), dev(ex_h)
+    x, wr = dev(x_h), dev(wr_h)
+    if args.no_cpu_baseline:  # the host copy of the experts only feeds the oracle
+        ex_h = None
+        ex = torch.empty(shape.E * shape.stride, dtype=torch.uint8, device="cuda")
+        gen.experts_device(shape, ex.data_ptr(), stream=torch.cuda.current_stream().cuda_stream)
+    else:
+        ex_h = gen.gen_experts(shape)
+        ex = dev(ex_h)
     bias = None if b_h is None else dev(b_h)
     layer = moe.MoELayer(shape.H, shape.F, shape.E, shape.k, T, moe.MOE_BF16, wr, ex,
                          shape.stride, bias)
@@ -457,8 +478,9 @@ def main():
 
     if not args.no_workloads and args.workload == "mixtral_prefill":
         print("[bench] 64-expert and 128-expert layers", file=sys.stderr, flush=True)
-        out["workloads"] = {"qwen2_moe_layer_T512": bench_workload(gen.QWEN, 512, K, W),
-                            "deepseek_moe_layer_T8192": bench_workload(gen.DEEPSEEK, 8192, K, W)}
+        out["workloads"] = {n: bench_workload(n, sh, t, K, W) for n, sh, t in
+                            (("qwen2_moe_layer_T512", gen.QWEN, 512),
+                             ("deepseek_moe_layer_T8192", gen.DEEPSEEK, 8192))}
 
     if not args.no_decode and args.workload == "mixtral_prefill":
         print("[bench] decode batches, bf16 and uint8 experts", file=sys.stderr, flush=True)
