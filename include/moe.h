@@ -106,8 +106,13 @@ enum {
   /* Kernel path for the expert FFN of bf16 layers.  By default a call with
    * T*k <= 32*E (few rows per expert: decode batches, many small experts)
    * streams each non-empty expert's weights once; otherwise the rows go
-   * through grouped GEMMs on 256x256 tiles.  These flags pin one path
-   * (results agree within rounding; both are deterministic). */
+   * through grouped GEMMs on 256x256 tiles.  A call with T == 1 whose widths
+   * suit it (H*w and F*w multiples of 1024 bytes, w the bytes per weight,
+   * with H*w/1024 in {2, 4, 6, 8}, F*w/1024 a multiple of 4 or 14, k <= 8 and
+   * k*F <= 40832) takes matrix-vector kernels instead, the combine folded
+   * into the down projection.  These flags pin one path (results agree
+   * within rounding; all are deterministic); MOE_FLAG_PATH_STREAM also keeps
+   * single tokens on the streaming kernels. */
   MOE_FLAG_PATH_GROUPED = 1u << 1,
   MOE_FLAG_PATH_STREAM = 1u << 2,
   /* Gate variant: the same top-k selection, and the gate weights are the k
@@ -119,10 +124,11 @@ enum {
   MOE_FLAG_GATE_RAW = 1u << 3,
   /* On the streaming path the down projection folds step 5 in when one
    * workgroup can own every expert's rows of a hidden slice (H/16 slices at
-   * least as many as compute units, T*k <= 256): it sums the k expert rows of
-   * each token in the same fixed slot order with the same fp32 operations as
-   * the separate combine, so the results are bit-identical.  This flag keeps
-   * the combine a kernel of its own (for profiling and testing). */
+   * least as many as compute units, T*k <= 256), and the single-token
+   * matrix-vector path always does: it sums the k expert rows of each token
+   * in the same fixed slot order with the same fp32 operations as the
+   * separate combine, so the results are bit-identical.  This flag keeps the
+   * combine a kernel of its own (for profiling and testing). */
   MOE_FLAG_COMBINE_SEPARATE = 1u << 4
 };
 

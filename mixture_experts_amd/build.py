@@ -13,7 +13,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
 SOURCES = ["moe_api.hip", "router.hip", "dispatch.hip", "expert_grouped.hip", "quantize.hip",
-           "expert_stream.hip", "expert_f32.hip", "combine.hip"]
+           "expert_stream.hip", "expert_gemv.hip", "expert_f32.hip", "combine.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -70,6 +70,19 @@ __device__ __forceinline__ h8_t dequant8(uint2 w, h2_t bias) {
   return h8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
+// Wait until a wave's loads of its oldest chunk in flight have landed: of
+// `ahead` chunks issued (at most A), the PER loads of each of the ahead - 1
+// younger ones may stay outstanding (loads complete in order).
+template <int PER, int A>
+__device__ __forceinline__ void wait_chunk(int ahead) {
+  if constexpr (A <= 1) {
+    WAIT_VMCNT(0);
+  } else {
+    if (ahead >= A) WAIT_VMCNT((A - 1) * PER);
+    else wait_chunk<PER, A - 1>(ahead);
+  }
+}
+
 // One LDS row run holds its chunks of 16 bytes with chunk c of run r at slot
 // c ^ (r % SPR) (SPR = chunks per run, at most 16), so the 16 lanes of an
 // MFMA operand read (16 runs, one chunk) spread over the bank groups.
@@ -102,16 +115,22 @@ __global__ __launch_bounds__(256) void stream_kernel(
   static_assert((CK == 128 || CK == 256 || CK == 512) && IT >= 1 && TR % (4 * RPIT) == 0 &&
                     IW >= 1 && WR % (4 * RPIW) == 0,
                 "chunk width and token rows per pass");
-  static_assert(NS >= 2 && NS <= 4, "ring depth");
-  __shared__ __attribute__((aligned(16))) uint8_t ring[NS][STAGE];
+  static_assert(NS >= 2 && NS <= 8 && (NS - 2) * (IW + IT) <= 63, "ring depth");
   // the waves' partial sums at the end of a pass, [4 waves][NA*NB][64 lanes],
   // in the ring stage just computed when it is large enough
   constexpr int RED = 4 * NA * NB * 64;
   constexpr bool RED_IN_RING = RED * 16 <= STAGE;
-  __shared__ f32x4 red_own[RED_IN_RING ? 1 : RED];
   static_assert(!FC || (!GATED && WR == 16), "combine folded into 16-row down items");
-  // FC: the down outputs of the slice, [pair t*k + j][16 rows], pairs < 256
-  __shared__ f32x4 comb[FC ? 256 * 16 / 4 : 1];
+  // one LDS block: the ring of NS stages, then the partial sums when a stage
+  // cannot hold them, then (FC) the down outputs of the slice, [pair t*k + j]
+  // [16 rows], pairs < 256; nothing else, so that the launch's occupancy
+  // arithmetic is exact
+  constexpr int LDS_BYTES = NS * STAGE + (RED_IN_RING ? 0 : RED * 16) + (FC ? 256 * 16 * 4 : 0);
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
+  uint8_t (*const ring)[STAGE] = reinterpret_cast<uint8_t (*)[STAGE]>(smem);
+  f32x4* const red_own = reinterpret_cast<f32x4*>(smem + NS * STAGE);
+  f32x4* const comb =
+      reinterpret_cast<f32x4*>(smem + NS * STAGE + (RED_IN_RING ? 0 : RED * 16));
 
   const int K = GATED ? H : F;
   const int NWT = GATED ? F / (16 * OB) : H / WR;
@@ -273,10 +292,7 @@ __global__ __launch_bounds__(256) void stream_kernel(
   while (c_ok) {
     // this wave's loads of the current chunk have landed once at most the
     // loads of the (ahead - 1) younger chunks are outstanding
-    constexpr int PER = IW + IT;
-    if (ahead >= 3) WAIT_VMCNT(2 * PER);
-    else if (ahead == 2) WAIT_VMCNT(PER);
-    else WAIT_VMCNT(0);
+    wait_chunk<IW + IT, NS - 1>(ahead);
     // publishes the chunk, and ends every wave's reads of the previous one
     asm volatile("s_barrier" ::: "memory");
     --ahead;
@@ -414,7 +430,7 @@ int launch_tr(const ExpertArgs& a, hipStream_t st, bool* combined = nullptr) {
   constexpr int NA = (Q8 || !GATED) ? QNA : 2, NB = (TR + 15) / 16;
   constexpr int OB = GATED ? NA / 2 : NA;
   constexpr int stage = (16 * NA * (Q8 ? 1 : 2) + TR * 2) * CK, red = 4 * NA * NB * 64 * 16;
-  constexpr int lds = NS * stage + (red <= stage ? 16 : red);
+  constexpr int lds = NS * stage + (red <= stage ? 0 : red);
   const int nwt = GATED ? a.F / (16 * OB) : a.H / (16 * NA);
   const int slots = a.E < a.S ? a.E : a.S;
   const uint16_t* tok = GATED ? (const uint16_t*)a.x : (const uint16_t*)a.act;

@@ -72,11 +72,11 @@ struct ExpertArgs {
   // grouped GEMMs: partial sums of split tail tiles, one 256 KB slot per
   // workgroup (grouped_grid() of them), or null (no split)
   float* gws = nullptr;
-  // step 5 inputs for a down projection that folds the combine in (cy null:
-  // it may not): gate weights [T][k], slot of each pair [T][k] (-1: dropped),
-  // residual [T][H] or null, output [T][H]
-  const float* cw = nullptr;
+  // slot of each pair [T][k] (-1: dropped by the capacity); step 5 inputs
+  // for a down projection that folds the combine in (cy null: it may not):
+  // gate weights [T][k], residual [T][H] or null, output [T][H]
   const int32_t* cinv = nullptr;
+  const float* cw = nullptr;
   const float* cres = nullptr;
   float* cy = nullptr;
 };
@@ -111,6 +111,12 @@ int launch_stream_gate_up(const ExpertArgs& a, hipStream_t st);
 // *combined: set when the launch also wrote y (step 5 folded in)
 int launch_stream_down(const ExpertArgs& a, bool* combined, hipStream_t st);
 // fp32 expert FFN (plain FMA)
+// single-token path (T == 1): the routed experts' weights streamed into
+// registers, matrix-vector products on the dot instructions, the combine
+// folded into the down projection when cy is set (then *combined = true)
+bool gemv_supported(int T, int H, int F, int k, bool u8);
+int launch_gemv_gate_up(const ExpertArgs& a, hipStream_t st);
+int launch_gemv_down(const ExpertArgs& a, bool* combined, hipStream_t st);
 int launch_f32_gate_up(const ExpertArgs& a, hipStream_t st);
 int launch_f32_down(const ExpertArgs& a, hipStream_t st);
 

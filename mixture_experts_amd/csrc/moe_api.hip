@@ -357,6 +357,11 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
   }
   const bool f32 = d.dtype == MOE_F32;
   const bool stream_path = !f32 && use_stream_path(L, T);
+  // a single token: matrix-vector kernels (unless the streaming kernels are
+  // asked for by flag)
+  const bool gemv_path = stream_path && !(d.flags & MOE_FLAG_PATH_STREAM) &&
+                         gemv_supported(T, d.hidden, d.ffn, d.top_k,
+                                        d.expert_format == MOE_EXPERT_U8);
   {
     const moe_layer_desc& dd = L->d;
     RouterArgs ra{xin, T, dd.hidden, dd.num_experts, dd.top_k, f32 ? 1 : 0, dd.router_w,
@@ -409,23 +414,26 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
       return MOE_ERR_DEVICE;
     ea.x = L->x16;
   }
-  int r1 = f32 ? launch_f32_gate_up(ea, st)
-               : stream_path ? launch_stream_gate_up(ea, st) : launch_grouped_gate_up(ea, st);
+  int r1 = f32           ? launch_f32_gate_up(ea, st)
+           : gemv_path   ? launch_gemv_gate_up(ea, st)
+           : stream_path ? launch_stream_gate_up(ea, st)
+                         : launch_grouped_gate_up(ea, st);
   if (r1 || !mark(MOE_STAGE_DOWN)) return MOE_ERR_DEVICE;
   const float* resid = prenorm ? (const float*)x : nullptr;
   const int planes = (f32 || stream_path) ? 1 : grouped_down_ksplit(ea);
   // the streaming down projection may take step 5 over (then the combine
   // stage below is empty)
   bool combined = false;
+  ea.cinv = L->inv;  // the single-token down projection finds its rows through it
   if (stream_path && !(d.flags & MOE_FLAG_COMBINE_SEPARATE)) {
     ea.cw = L->w;
-    ea.cinv = L->inv;
     ea.cres = resid;
     ea.cy = (float*)y;
   }
-  int r2 = f32 ? launch_f32_down(ea, st)
-               : stream_path ? launch_stream_down(ea, &combined, st)
-                             : launch_grouped_down(ea, planes, st);
+  int r2 = f32           ? launch_f32_down(ea, st)
+           : gemv_path   ? launch_gemv_down(ea, &combined, st)
+           : stream_path ? launch_stream_down(ea, &combined, st)
+                         : launch_grouped_down(ea, planes, st);
   if (r2 || !mark(MOE_STAGE_COMBINE)) return MOE_ERR_DEVICE;
   if (!combined &&
       launch_combine(L->yp, planes, L->w, L->inv, resid, T, d.hidden, d.top_k, y, st))

@@ -154,3 +154,48 @@ def check_rows(case: Case, x_np: np.ndarray, tokens, y_gpu_rows: np.ndarray,
     (see reference_rows and compare_rows)."""
     y_ref, stats = reference_rows(case, x_np, tokens, gpu_idx_rows, keep_rows, chunk, log)
     return compare_rows(case, y_gpu_rows, y_ref, stats, tol)
+
+
+def quantize_on_gpu(shape, d_src, E=None):
+    E = shape.E if E is None else E
+    st = moe.u8_stride(shape.H, shape.F)
+    dst = torch.zeros(E * st, dtype=torch.uint8, device="cuda")  # padding bytes defined
+    moe.moe_quantize_experts_u8(d_src, shape.stride, E, shape.H, shape.F, dst, st)
+    torch.cuda.synchronize()
+    return dst, st
+
+
+class U8Case:
+    """A uint8-expert layer on the GPU and the oracle's layer on the same codes."""
+
+    def __init__(self, shape, max_tokens, flags=0, layer=0):
+        self.shape = shape
+        self.router, self.bias = gen.gen_router(shape, layer), gen.gen_bias(shape)
+        d_src = torch.empty(shape.E * shape.stride, dtype=torch.uint8, device="cuda")
+        gen.experts_device(shape, d_src.data_ptr(), layer=layer,
+                           stream=torch.cuda.current_stream().cuda_stream)
+        self.d_u8, self.st = quantize_on_gpu(shape, d_src)
+        del d_src
+        self.u8 = self.d_u8.cpu().numpy()
+        self.d_router = to_dev(self.router)
+        self.d_bias = None if self.bias is None else to_dev(self.bias)
+        self.layer = moe.MoELayer(shape.H, shape.F, shape.E, shape.k, max_tokens, moe.MOE_BF16,
+                                  self.d_router, self.d_u8, self.st, self.d_bias, flags,
+                                  expert_format=moe.MOE_EXPERT_U8)
+        gate = "raw" if flags & moe.MOE_FLAG_GATE_RAW else "softmax"
+        self.orc = oracle.layer_from_gen(shape, self.router, self.bias, None, gate=gate,
+                                         u8_experts=self.u8, u8_stride=self.st)
+
+    def forward(self, x):
+        y = torch.empty((x.shape[0], self.shape.H), dtype=torch.float32, device="cuda")
+        self.layer.forward(to_dev(x), y)
+        torch.cuda.synchronize()
+        return y.cpu().numpy()
+
+    def route(self, x):
+        r = self.layer.route(to_dev(x), x.shape[0])
+        torch.cuda.synchronize()
+        return {k: v.cpu().numpy() for k, v in r.items()}
+
+    def close(self):
+        self.layer.close()
