@@ -517,7 +517,7 @@ __global__ __launch_bounds__(256) void router_f32_kernel(
   __shared__ float lg[RT_TOK * 257];
   __shared__ double exs[4 * MOE_MAX_EXPERTS];  // (k > MOE_MAX_TOPK only)
   const int ldl = E + 1;
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int tile0 = blockIdx.x * RT_TOK;
   for (int i = tid; i < RT_TOK * E; i += 256) {
     const int r = i / E, e = i % E, t = tile0 + r;

@@ -78,13 +78,14 @@ def test_gemv_many_calls(u8):
 
 
 @pytest.mark.parametrize("u8", [False, True])
-def test_gemv_and_stream_kernels_agree(u8):
+@pytest.mark.parametrize("E", [4, 8])
+def test_gemv_and_stream_kernels_agree(u8, E):
     """The streaming kernels at T = 1 (forced by flag) against the oracle, and
     within the bf16 tolerance of the matrix-vector kernels."""
-    _log("gemv vs stream", u8)
+    _log("gemv vs stream", u8, E)
     ys = []
     for fl in (0, moe.MOE_FLAG_PATH_STREAM):
-        shape, c = _case(u8, 4096, 14336 if u8 else 7168, 4, 2, fl)
+        shape, c = _case(u8, 4096, 14336 if u8 else 7168, E, 2, fl)
         x = gen.gen_x(shape, 1)
         y = c.forward(x)
         check_rows(c, x, np.arange(1), y, c.route(x)["idx"])

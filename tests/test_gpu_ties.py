@@ -120,6 +120,10 @@ FWD_CASES = [
     (1024, 256, 8, 2, 1, moe.MOE_FLAG_RESIDUAL_PRENORM),
     (1024, 256, 16, 4, 16, moe.MOE_FLAG_RESIDUAL_PRENORM),
     (1024, 256, 8, 2, 40, moe.MOE_FLAG_RESIDUAL_PRENORM),
+    # single tokens on the matrix-vector kernels
+    (1024, 2048, 8, 2, 1, 0),
+    (1024, 2048, 16, 4, 1, 0),
+    (1024, 2048, 8, 2, 1, moe.MOE_FLAG_RESIDUAL_PRENORM),
 ]
 
 
