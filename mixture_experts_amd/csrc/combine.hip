@@ -32,9 +32,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int pi = inv[(size_t)t * k + j];
     if (pi < 0) continue;  // a pair dropped by the expert capacity
     const int p = min(pi, S - 1);  // in range by construction
-    f32x4 v = *reinterpret_cast<const f32x4*>(yp + (size_t)p * H + c);
+    // each per-pair row is read once: non-temporal loads
+    f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(yp + (size_t)p * H + c));
     for (int pl = 1; pl < nplanes; ++pl)  // partial sums of a split K, in plane order
-      v += *reinterpret_cast<const f32x4*>(yp + ((size_t)pl * S + p) * H + c);
+      v += __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4*>(yp + ((size_t)pl * S + p) * H + c));
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = fmaf(wj, v[q], acc[q]);
   }

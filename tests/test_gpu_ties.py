@@ -54,6 +54,10 @@ ROUTE_CASES = [
     (1024, 64, 2, 33),
     (2048, 64, 8, 64),
     (256, 8, 2, 7),     # H not a multiple of 512: split-hidden route with 8 experts
+    # batches beyond 64 tokens: logits and top-k of 32-token tiles in one launch
+    (1024, 8, 2, 100),
+    (2048, 64, 4, 300),
+    (1024, 256, 16, 70),  # k beyond 8: selection by ranks
 ]
 
 
