@@ -196,6 +196,8 @@ __device__ __forceinline__ void write_tile(const Tile& t, Prep prep, Get get4,
           uint2 pk;
           pk.x = __builtin_bit_cast(uint32_t, lo);
           pk.y = __builtin_bit_cast(uint32_t, hi);
+          // (plain stores: as non-temporal 8-byte stores, partial lines, the
+          // Mixtral prefill gate/up took 1.75 -> 1.85 ms)
           *reinterpret_cast<uint2*>(row + 32 * i + 8 * q) = pk;
         }
     }
@@ -220,9 +222,11 @@ __device__ __forceinline__ void write_tile(const Tile& t, Prep prep, Get get4,
       for (int r0 = 0; r0 < 64; r0 += 4) {
         const int row = r0 + (tid >> 6);
         const int tl = (2 * j + (row >> 5)) * 32 + (row & 31);
-        if (tl < t.rows)
-          *reinterpret_cast<u32x4*>(yp + (size_t)(t.p0 + tl) * H + t.mt * 256 + ((c ^ (row & 15)) << 2)) =
-              *reinterpret_cast<const u32x4*>(ob + row * 1024 + (c << 4));
+        if (tl < t.rows)  // whole 1 KB row runs, written once: non-temporal
+          __builtin_nontemporal_store(
+              *reinterpret_cast<const u32x4*>(ob + row * 1024 + (c << 4)),
+              reinterpret_cast<u32x4*>(yp + (size_t)(t.p0 + tl) * H + t.mt * 256 +
+                                       ((c ^ (row & 15)) << 2)));
       }
     }
   }
@@ -236,7 +240,10 @@ __device__ __forceinline__ f32x4* part_base(float* ws, int slot, int wave) {
   return reinterpret_cast<f32x4*>(ws + (size_t)slot * kPartFloats + wave * 16384) + ln;
 }
 
-template <bool GATED>
+// NTW: the weight rows are loaded non-temporal (each weight tile meets one
+// token tile: the experts hold one tile of rows on average), so that they
+// do not push the token rows, which every weight tile reuses, out of L2.
+template <bool GATED, bool NTW>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
     const uint16_t* __restrict__ experts, uint64_t stride_elems,
     const uint16_t* __restrict__ tok, const int32_t* __restrict__ perm, int k_top,
@@ -337,10 +344,16 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
     // one wait state between the M0 write and the LDS-DMA load that reads it
     if (op == 0) {
       const uint16_t* src = eb + aoff[i & 1] + (size_t)(i & 6) * 8 * (GATED ? H : F) + s * kBK;
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                   :
-                   : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(src)
-                   : "memory", "m0");
+      if constexpr (NTW)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+                     :
+                     : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(src)
+                     : "memory", "m0");
+      else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :
+                     : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(src)
+                     : "memory", "m0");
     } else {
       // the row's offset in VADDR, the K step's in SOFFSET: a row inside the
       // buffer stays inside it at every K step of the row, a row past it stays
@@ -633,15 +646,21 @@ int grouped_down_ksplit(const ExpertArgs& a) {
   return (max_tiles * (a.H / 256) < 3 * 256 && a.F % (2 * kBK) == 0) ? 2 : 1;
 }
 
+// the experts hold at most one token tile of rows on average
+static bool weights_once(const ExpertArgs& a) { return a.S <= (int64_t)GG_BT * a.E; }
+
 int launch_grouped_gate_up(const ExpertArgs& a, hipStream_t st) {
-  grouped_gemm_kernel<true><<<persistent_grid(), 256, 0, st>>>(
+  auto kern = weights_once(a) ? grouped_gemm_kernel<true, true> : grouped_gemm_kernel<true, false>;
+  kern<<<persistent_grid(), 256, 0, st>>>(
       (const uint16_t*)a.experts, a.stride_elems, (const uint16_t*)a.x, a.perm, a.k, a.offsets,
       a.tile_off, a.E, a.H, a.F, a.T, 1, 0, a.act, nullptr);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_grouped_down(const ExpertArgs& a, int ksplit, hipStream_t st) {
-  grouped_gemm_kernel<false><<<persistent_grid(), 256, 0, st>>>(
+  auto kern =
+      weights_once(a) ? grouped_gemm_kernel<false, true> : grouped_gemm_kernel<false, false>;
+  kern<<<persistent_grid(), 256, 0, st>>>(
       (const uint16_t*)a.experts, a.stride_elems, (const uint16_t*)a.act, a.perm, a.k,
       a.offsets, a.tile_off, a.E, a.H, a.F, a.T, ksplit, (size_t)a.S * a.H, a.yp, a.gws);
   if (a.gws)
