@@ -244,7 +244,7 @@ constexpr int kDnActElems = (80 * 1024 - 256) / 2;
 // written here (step 5); else the per-slot rows yp[p][h].  (Tasks of two
 // or four hidden rows measured the same at the Mixtral width.)
 template <bool Q8, int CH, int WGW, bool FOLD>
-__global__ __launch_bounds__(64 * WGW, WGW / 2) void gemv_down_kernel(
+__global__ __launch_bounds__(64 * WGW, 4) void gemv_down_kernel(
     const uint8_t* __restrict__ experts, uint64_t stride_b, const uint16_t* __restrict__ act,
     const int32_t* __restrict__ active, int H, int F, int k, int nch,
     const float* __restrict__ cw, const int32_t* __restrict__ cinv, const float* cres, float* cy,
@@ -300,17 +300,42 @@ __global__ __launch_bounds__(64 * WGW, WGW / 2) void gemv_down_kernel(
     for (int i = 0; i < CH; ++i) ck.w[i] = ld_nt(src + i * 1024 + lane * 16);
   };
 
-  // the first chunk's loads go out before the activation rows are copied
+  // next chunk of the sequence (task t, chunk q of nseq) of this wave: tasks
+  // gw, gw + NW, ...
+  auto next = [&](int t, int q, int& t2, int& q2) __attribute__((always_inline)) {
+    q2 = q + 1;
+    t2 = t;
+    if (q2 == nseq) {
+      q2 = 0;
+      t2 = t + NW;
+    }
+  };
+  // The slots' activation rows go to LDS.  Their loads are issued first, then
+  // the wave's first two weight chunks: waiting for the activation (the
+  // oldest loads) leaves both chunks in flight.
+  constexpr int kStage = (kDnActElems / 8 + 64 * WGW - 1) / (64 * WGW);
+  const int per = F / 8, tot = nv * per;  // 16-byte pieces of one row, of all
+  u32x4 stage[kStage];
+#pragma unroll
+  for (int m = 0; m < kStage; ++m) {
+    const int i = threadIdx.x + m * 64 * WGW;
+    if (i < tot) {
+      const int v = i / per;
+      stage[m] = reinterpret_cast<const u32x4*>(act + (size_t)sl_p[v] * F)[i - v * per];
+    }
+  }
   Chunk A, B;
-  int tk = gw, q = 0;
-  if (tk < ntask) issue(tk, q, A);
-  for (int v = 0; v < nv; ++v) {  // the slots' activation rows -> LDS
-    const u32x4* src = reinterpret_cast<const u32x4*>(act + (size_t)sl_p[v] * F);
-    u32x4* dst = reinterpret_cast<u32x4*>(act_lds + (size_t)v * F);
-    for (int i = threadIdx.x; i < F / 8; i += 64 * WGW) dst[i] = src[i];
+  int ta = gw, qa = 0, tb, qb;
+  next(ta, qa, tb, qb);
+  issue(ta, qa, A);
+  issue(tb, qb, B);
+#pragma unroll
+  for (int m = 0; m < kStage; ++m) {
+    const int i = threadIdx.x + m * 64 * WGW;
+    if (i < tot) reinterpret_cast<u32x4*>(act_lds)[i] = stage[m];
   }
   __syncthreads();
-  if (tk >= ntask) return;
+  if (ta >= ntask) return;
 
   float a0 = 0.f, a1 = 0.f;  // the current slot's partial sums (even / odd pieces)
   float yacc = 0.f;          // step 5 for the task's row
@@ -342,25 +367,16 @@ __global__ __launch_bounds__(64 * WGW, WGW / 2) void gemv_down_kernel(
     }
   };
 
-  // chunk sequence of this wave: (task tk, chunk q of nseq), tk = gw, gw + NW, ...
+  // two chunks in flight: finish one, issue the one after the other
   for (;;) {
-    int tb = tk, qb = q + 1;
-    if (qb == nseq) {
-      qb = 0;
-      tb += NW;
-    }
-    issue(tb, qb, B);
-    finish(tk, A);
+    finish(ta, A);
     if (tb >= ntask) break;
-    tk = tb;
-    q = qb + 1;
-    if (q == nseq) {
-      q = 0;
-      tk += NW;
-    }
-    issue(tk, q, A);
+    next(tb, qb, ta, qa);
+    issue(ta, qa, A);
     finish(tb, B);
-    if (tk >= ntask) break;
+    if (ta >= ntask) break;
+    next(ta, qa, tb, qb);
+    issue(tb, qb, B);
   }
 }
 
@@ -381,8 +397,8 @@ int launch_gu(const ExpertArgs& a, hipStream_t st) {
 template <bool Q8, int CH, int WGW>
 int launch_dn(const ExpertArgs& a, bool fold, hipStream_t st) {
   const int nch = a.F * (Q8 ? 1 : 2) / 1024 / CH;
-  // two workgroups per CU (80 KB of LDS each)
-  int grid = cu_count() * 2;
+  // 16 waves per CU (80 KB of LDS per workgroup)
+  int grid = cu_count() * (16 / WGW);
   if (grid * WGW > a.H) grid = (a.H + WGW - 1) / WGW;
   auto* ex = (const uint8_t*)a.experts;
   const uint64_t sb = a.stride_elems * (Q8 ? 1 : 2);
@@ -410,7 +426,8 @@ int launch_gu_q(const ExpertArgs& a, hipStream_t st) {
 
 // Eight waves per workgroup (four per SIMD) and chunks of at most 8 KB:
 // 7-piece chunks and 8-wave workgroups measured 2 us faster at the Mixtral
-// width (both expert formats) than 14-piece chunks in 4-wave workgroups.
+// width (both expert formats) than 14-piece chunks in 4-wave workgroups; one
+// 16-wave workgroup per CU (half the activation copies) measured the same.
 template <bool Q8>
 int launch_dn_q(const ExpertArgs& a, bool fold, hipStream_t st) {
   const int lr = a.F * (Q8 ? 1 : 2) / 1024;

@@ -62,12 +62,50 @@ __device__ __forceinline__ Cand wave_best(Cand c) {
 }
 #undef DPP_CAND
 
+// DPP move of a 32-bit value; lanes without a source (row_shr past the row's
+// start) read 0.  CTRL: row_shr:n = 0x110 + n, row_ror:n = 0x120 + n.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)dpp_i<CTRL>((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)dpp_i<CTRL>((int)(uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// The best candidate of each 16-lane row, in every lane of the row: rotations
+// by 8, 4, 2 and 1 within the row ("better" is a total order, so the shape
+// of the reduction does not matter).
+__device__ __forceinline__ Cand row_best16(Cand c) {
+#define ROW_STEP(ctrl) \
+  c = dpp_best_step(c, Cand{__int_as_float(dpp_i<ctrl>(__float_as_int(c.v))), dpp_i<ctrl>(c.e)})
+  ROW_STEP(0x128);
+  ROW_STEP(0x124);
+  ROW_STEP(0x122);
+  ROW_STEP(0x121);
+#undef ROW_STEP
+  return c;
+}
+// Inclusive prefix sum of an integer over the 64 lanes: row-local steps
+// (row_shr 1, 2, 4, 8), then the rows' totals carried by row broadcasts.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp_i<0x111>(x);
+  x += dpp_i<0x112>(x);
+  x += dpp_i<0x114>(x);
+  x += dpp_i<0x118>(x);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+  return x;
+}
+
 // Top-k of one token by ranks, for k > MOE_MAX_TOPK (up to every expert:
 // soft routing): the rank of expert e is the number of experts that beat it
 // ((value desc, index asc), the same total order as the picks below), the k
 // best take the slots 0..k-1 by rank, and the softmax adds the exponentials
 // in slot order (lane 0, from ex_lds: [k] doubles of this wave).
-__device__ void topk_rank_row(const float* row, int t, int E, int k, int raw, int32_t* idx_out,
+__device__ __forceinline__ void topk_rank_row(const float* row, int t, int E, int k, int raw, int32_t* idx_out,
                               float* w_out, double* ex_lds) {
   const int lane = threadIdx.x & 63;
   float v[4];
@@ -120,7 +158,7 @@ __device__ void topk_rank_row(const float* row, int t, int E, int k, int raw, in
 // waves).  lg: LDS logits [rows][ldl].  idx_lds (optional): an LDS copy of the
 // picks of the tile, [RT_TOK][k].  k > MOE_MAX_TOPK takes topk_rank_row with
 // ex_lds: [nwaves][MOE_MAX_EXPERTS] doubles of LDS.
-__device__ void topk_rows(const float* lg, int ldl, int tile0, int T, int E, int k, int raw,
+__device__ __forceinline__ void topk_rows(const float* lg, int ldl, int tile0, int T, int E, int k, int raw,
                           int32_t* idx_out, float* w_out, int nwaves = 4,
                           int32_t* idx_lds = nullptr, int rows = RT_TOK,
                           double* ex_lds = nullptr) {
@@ -188,12 +226,13 @@ __device__ void topk_rows(const float* lg, int ldl, int tile0, int T, int E, int
   }
 }
 
-// Top-k + softmax (raw gate: the selected logits) for E <= 16: each 16-lane group of a wave takes one token
-// (lane = expert), so a wave handles 4 tokens at once: tokens
-// tile0 + 4 (wave + nwaves j) + g, g = lane / 16.  Same ordering (value desc,
-// index asc) and fp64 softmax as topk_rows; lane j of the group evaluates the
-// exponential of pick j.
-__device__ void topk_rows16(const float* lg, int ldl, int tile0, int T, int E, int k, int raw,
+// Top-k + softmax (raw gate: the selected logits) for E <= 16: each 16-lane
+// group (a DPP row) of a wave takes one token (lane = expert), so a wave
+// handles 4 tokens at once: tokens tile0 + 4 (wave + nwaves j) + g,
+// g = lane / 16.  Each pick is the row's best by DPP rotations; same ordering
+// (value desc, index asc) and fp64 softmax as topk_rows; lane j of the group
+// evaluates the exponential of pick j.
+__device__ __forceinline__ void topk_rows16(const float* lg, int ldl, int tile0, int T, int E, int k, int raw,
                             int32_t* idx_out, float* w_out, int nwaves, int32_t* idx_lds,
                             int rows) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -204,29 +243,37 @@ __device__ void topk_rows16(const float* lg, int ldl, int tile0, int T, int E, i
     const bool ok = r < rows && t < T;
     const float v = (ok && el < E) ? lg[(size_t)r * ldl + el] : 0.0f;
     bool avail = ok && el < E;
-    float my_v = 0.0f;
+    float my_v = 0.0f, m = 0.0f;
     int my_e = 0;
 #pragma unroll
     for (int j = 0; j < MOE_MAX_TOPK; ++j) {
       if (j >= k) break;
-      Cand best{v, avail ? el : INT32_MAX};
-#pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) {
-        Cand o{__shfl_xor(best.v, off), __shfl_xor(best.e, off)};
-        if (better(o, best)) best = o;
-      }
+      const Cand best = row_best16(Cand{v, avail ? el : INT32_MAX});
       if (best.e == el) avail = false;
-      if (el == j) { my_v = best.v; my_e = best.e; }
+      if (el == j) {
+        my_v = best.v;
+        my_e = best.e;
+      }
+      if (j == 0) m = best.v;  // the maximum, for the softmax
     }
-    // softmax over the picks: lane j < k holds pick j; the maximum is pick 0
-    const float m = __shfl(my_v, lane & ~15);
+    // softmax over the picks (lane j < k holds pick j): z adds the
+    // exponentials in pick order, as topk_rows does, so that every route
+    // kernel gives the same weights bit for bit -- a running sum passed along
+    // the row (lane j adds its term to lane j-1's sum), then lane k-1's total
+    // sent to the whole row by adding it to zeros (exact)
     const double ex = (el < k && !raw) ? exp((double)my_v - (double)m) : 0.0;
-    // z adds the exponentials in pick order, as topk_rows does, so that every
-    // route kernel gives the same weights bit for bit
-    double z = 0.0;
+    double s = ex;
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j)
-      if (j < k) z += __shfl(ex, (lane & ~15) + j);
+    for (int j = 1; j < MOE_MAX_TOPK; ++j) {
+      if (j >= k) break;
+      const double prev = dpp_d<0x111>(s);  // row_shr:1
+      if (el == j) s = prev + s;
+    }
+    double z = (el == k - 1) ? s : 0.0;
+    z += dpp_d<0x128>(z);
+    z += dpp_d<0x124>(z);
+    z += dpp_d<0x122>(z);
+    z += dpp_d<0x121>(z);
     if (ok && el < k) {
       idx_out[(size_t)t * k + el] = my_e;
       w_out[(size_t)t * k + el] = raw ? my_v : (float)(ex / z);
@@ -236,68 +283,83 @@ __device__ void topk_rows16(const float* lg, int ldl, int tile0, int T, int E, i
 }
 
 // Dispatch of S = T*k <= RT_TOK*8 slots whose expert ids are in LDS
-// (idx_lds[S]): wave 0 ranks the slots of each expert with ballot matches
-// in slot order, one thread scans the counts (capped at cap > 0), every
-// thread scatters (a slot ranked at or beyond cap is dropped: inv = -1).
-// Same stable counting sort as the dispatch kernels.  cnt, off_l, rank_l:
-// LDS.
-__device__ void dispatch_small(const int32_t* idx_lds, int S, int E, int tile_rows, int cap,
+// (idx_lds[S], published to wave 0), by wave 0 alone: it ranks the slots of
+// each expert with ballot matches in slot order, scans the counts (capped at
+// cap > 0) over the experts with lane-parallel prefix sums, and scatters (a
+// slot ranked at or beyond cap is dropped: inv = -1).  Same stable counting
+// sort as the dispatch kernels.  cnt, off_l, rank_l: LDS.  The other waves
+// return at once; nothing here waits for the workgroup.
+__device__ __forceinline__ void dispatch_small(const int32_t* idx_lds, int S, int E, int tile_rows, int cap,
                                int32_t* cnt, int32_t* off_l, int32_t* rank_l,
                                int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                int32_t* __restrict__ tile_off, int32_t* __restrict__ active,
                                int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (wave == 0) {
-    for (int e = lane; e < E; e += 64) cnt[e] = 0;
-    int nbits = 0;
-    while ((1 << nbits) < E) ++nbits;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int c = 0; c * 64 < S; ++c) {
-      const int sl = c * 64 + lane;
-      const bool valid = sl < S;
-      const int e = valid ? idx_lds[sl] : 0;
-      uint64_t match = __ballot(valid);
-      for (int b = 0; b < nbits; ++b) {
-        const bool bit = (e >> b) & 1;
-        const uint64_t m = __ballot(bit);
-        match &= bit ? m : ~m;
-      }
-      const uint64_t earlier = match & below;
-      const int c0 = valid ? cnt[e] : 0;
-      __builtin_amdgcn_wave_barrier();
-      if (valid) {
-        rank_l[sl] = c0 + __popcll(earlier);
-        if (earlier == 0) cnt[e] = c0 + __popcll(match);
-      }
-      __builtin_amdgcn_wave_barrier();
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid >= 64) return;
+  // (one wave: its LDS operations complete in order; the compiler fences keep
+  // them in program order)
+  for (int e = lane; e < E; e += 64) cnt[e] = 0;
+  asm volatile("" ::: "memory");
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c = 0; c * 64 < S; ++c) {
+    const int sl = c * 64 + lane;
+    const bool valid = sl < S;
+    const int e = valid ? idx_lds[sl] : 0;
+    uint64_t match = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      match &= bit ? m : ~m;
     }
+    const uint64_t earlier = match & below;
+    const int c0 = valid ? cnt[e] : 0;
+    asm volatile("" ::: "memory");
+    if (valid) {
+      rank_l[sl] = c0 + __popcll(earlier);
+      if (earlier == 0) cnt[e] = c0 + __popcll(match);
+    }
+    asm volatile("" ::: "memory");
   }
-  __syncthreads();
-  if (tid == 0) {
-    int o = 0, tt = 0, n = 0;
-    for (int e = 0; e < E; ++e) {
-      const int c = (cap > 0 && cnt[e] > cap) ? cap : cnt[e];  // pairs kept
-      off_l[e] = o;
-      offsets[e] = o;
+  // offsets / tile schedule / non-empty list: lane-parallel over 64 experts
+  // at a time, carried across the chunks
+  int o = 0, tt = 0, n = 0;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    const bool in = e < E;
+    int c = in ? cnt[e] : 0;
+    if (cap > 0 && c > cap) c = cap;  // pairs kept
+    const int tl = (c + tile_rows - 1) / tile_rows;
+    const int ic = wave_incl_scan(c), it = wave_incl_scan(tl);
+    const uint64_t nz = __ballot(c > 0);
+    if (in) {
+      const int oe = o + ic - c;
+      off_l[e] = oe;
+      offsets[e] = oe;
       counts[e] = c;
-      tile_off[e] = tt;
-      o += c;
-      tt += (c + tile_rows - 1) / tile_rows;
-      if (c > 0) active[n++] = e;
+      tile_off[e] = tt + it - tl;
+      if (c > 0) active[n + __popcll(nz & below)] = e;
     }
+    o += __builtin_amdgcn_readlane(ic, 63);
+    tt += __builtin_amdgcn_readlane(it, 63);
+    n += __popcll(nz);
+  }
+  if (lane == 0) {
     off_l[E] = o;
     offsets[E] = o;
     tile_off[E] = tt;
     active[E] = n;
   }
-  __syncthreads();
-  for (int sl = tid; sl < S; sl += blockDim.x) {
-    if (sl >= off_l[E]) perm[sl] = -1;  // beyond the kept pairs
-    if (cap > 0 && rank_l[sl] >= cap) {
+  asm volatile("" ::: "memory");
+  for (int sl = lane; sl < S; sl += 64) {
+    if (sl >= o) perm[sl] = -1;  // beyond the kept pairs
+    const int rk = rank_l[sl];
+    if (cap > 0 && rk >= cap) {
       inv[sl] = -1;  // dropped
       continue;
     }
-    const int p = off_l[idx_lds[sl]] + rank_l[sl];
+    const int p = off_l[idx_lds[sl]] + rk;
     perm[p] = sl;
     inv[sl] = p;
   }
