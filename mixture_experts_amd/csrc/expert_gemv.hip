@@ -25,7 +25,9 @@
 // the end), then the wave adds its lanes in a fixed DPP order: the result
 // is the same on every call.
 //
-// gate/up: one task = gate row f and up row f of one active expert; the
+// Both kernels read the routing itself (expert and activation row of each
+// slot: one step of dependent loads before the first weight load).
+// gate/up: one task = gate row f and up row f of one routed expert; the
 // token's operand for the lane's K positions sits in registers for the
 // whole kernel; the task ends with SiLU(g) * u rounded to bf16 (stored as
 // fp16 for uint8 layers, whose down projection takes fp16 operands).
@@ -132,19 +134,22 @@ __device__ __forceinline__ QParams qparams(const uint8_t* eb, int H, int F, int 
 // ---------------------------------------------------------------- gate/up
 // LR: 1 KB pieces per weight row (K = H); WPE: waves per SIMD the register
 // budget is cut for.  x: the token's expert input (fp16 for uint8 experts,
-// bf16 otherwise), act: [S][F] out.  (Tasks of two or four row pairs, and
+// bf16 otherwise); idx, inv: its routing (slot s: expert idx[s], activation
+// row inv[s]); act: [S][F] out.  (Tasks of two or four row pairs, and
 // two or five waves per SIMD, measured the same at the Mixtral width.)
 template <bool Q8, int LR, int WPE>
 __global__ __launch_bounds__(256, WPE) void gemv_gate_up_kernel(
     const uint8_t* __restrict__ experts, uint64_t stride_b, const uint16_t* __restrict__ x,
-    const int32_t* __restrict__ active, const int32_t* __restrict__ offsets, int E, int H, int F,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ inv, int ktop, int H, int F,
     uint16_t* __restrict__ act) {
   constexpr int WE = Q8 ? 1 : 2;  // bytes per weight
   constexpr int V = 16 / WE;      // weights per 16-byte piece
   const int lane = threadIdx.x & 63;
   const int gw = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
   const int NW = gridDim.x * 4;
-  const int ntask = active[E] * F;
+  // one token: its k slots reach k different experts, none beyond a capacity
+  // (an expert sees at most one pair); slot s writes activation row inv[s]
+  const int ntask = ktop * F;
   if (gw >= ntask) return;
   const size_t row_b = (size_t)H * WE;
 
@@ -171,8 +176,8 @@ __global__ __launch_bounds__(256, WPE) void gemv_gate_up_kernel(
     if (t < ntask) {
       const int s = t / F;
       k.f = t - s * F;
-      const int e = active[s];
-      k.p = offsets[e];
+      const int e = idx[s];
+      k.p = inv[s];
       k.eb = experts + stride_b * e;
       g = k.eb + (size_t)k.f * row_b;
       u = k.eb + (size_t)(F + k.f) * row_b;
@@ -246,7 +251,7 @@ constexpr int kDnActElems = (80 * 1024 - 256) / 2;
 template <bool Q8, int CH, int WGW, bool FOLD>
 __global__ __launch_bounds__(64 * WGW, 4) void gemv_down_kernel(
     const uint8_t* __restrict__ experts, uint64_t stride_b, const uint16_t* __restrict__ act,
-    const int32_t* __restrict__ active, int H, int F, int k, int nch,
+    const int32_t* __restrict__ idx, int H, int F, int k, int nch,
     const float* __restrict__ cw, const int32_t* __restrict__ cinv, const float* cres, float* cy,
     float* __restrict__ yp) {
   constexpr int WE = Q8 ? 1 : 2;
@@ -265,9 +270,9 @@ __global__ __launch_bounds__(64 * WGW, 4) void gemv_down_kernel(
   if (threadIdx.x == 0) {  // the token's slots that reach an expert, in slot order
     int v = 0;
     for (int j = 0; j < k; ++j) {
-      const int p = cinv[j];
+      const int p = cinv[j], e = idx[j];
       if (p < 0) continue;  // dropped by the expert capacity
-      sl_row[v] = experts + stride_b * active[p] + 2 * (size_t)F * H * WE;
+      sl_row[v] = experts + stride_b * e + 2 * (size_t)F * H * WE;
       sl_w[v] = FOLD ? cw[j] : 0.0f;
       sl_p[v] = p;
       ++v;
@@ -389,8 +394,8 @@ int launch_gu(const ExpertArgs& a, hipStream_t st) {
   int grid = cu_count() * WPE;
   if (grid * 4 > tasks) grid = (tasks + 3) / 4;
   gemv_gate_up_kernel<Q8, LR, WPE><<<grid, 256, 0, st>>>(
-      (const uint8_t*)a.experts, a.stride_elems * (Q8 ? 1 : 2), (const uint16_t*)a.x, a.active,
-      a.offsets, a.E, a.H, a.F, (uint16_t*)a.act);
+      (const uint8_t*)a.experts, a.stride_elems * (Q8 ? 1 : 2), (const uint16_t*)a.x, a.cidx,
+      a.cinv, a.k, a.H, a.F, (uint16_t*)a.act);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -404,11 +409,11 @@ int launch_dn(const ExpertArgs& a, bool fold, hipStream_t st) {
   const uint64_t sb = a.stride_elems * (Q8 ? 1 : 2);
   if (fold)
     gemv_down_kernel<Q8, CH, WGW, true><<<grid, 64 * WGW, 0, st>>>(
-        ex, sb, (const uint16_t*)a.act, a.active, a.H, a.F, a.k, nch, a.cw, a.cinv, a.cres, a.cy,
+        ex, sb, (const uint16_t*)a.act, a.cidx, a.H, a.F, a.k, nch, a.cw, a.cinv, a.cres, a.cy,
         a.yp);
   else
     gemv_down_kernel<Q8, CH, WGW, false><<<grid, 64 * WGW, 0, st>>>(
-        ex, sb, (const uint16_t*)a.act, a.active, a.H, a.F, a.k, nch, nullptr, a.cinv, nullptr,
+        ex, sb, (const uint16_t*)a.act, a.cidx, a.H, a.F, a.k, nch, nullptr, a.cinv, nullptr,
         nullptr, a.yp);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
@@ -452,13 +457,13 @@ bool gemv_supported(int T, int H, int F, int k, bool u8) {
 
 int launch_gemv_gate_up(const ExpertArgs& a, hipStream_t st) {
   if (!gemv_supported(a.T, a.H, a.F, a.k, a.u8)) return -1;
-  if (!a.experts || !a.x || !a.active || !a.offsets || !a.act) return -1;
+  if (!a.experts || !a.x || !a.cidx || !a.cinv || !a.act) return -1;
   return a.u8 ? launch_gu_q<true>(a, st) : launch_gu_q<false>(a, st);
 }
 
 int launch_gemv_down(const ExpertArgs& a, bool* combined, hipStream_t st) {
   if (!gemv_supported(a.T, a.H, a.F, a.k, a.u8)) return -1;
-  if (!a.experts || !a.act || !a.active || !a.cinv) return -1;
+  if (!a.experts || !a.act || !a.cidx || !a.cinv) return -1;
   const bool fold = combined && a.cy;
   if (fold ? !a.cw : !a.yp) return -1;
   if (combined) *combined = fold;

@@ -76,6 +76,9 @@ struct ExpertArgs {
   // for a down projection that folds the combine in (cy null: it may not):
   // gate weights [T][k], residual [T][H] or null, output [T][H]
   const int32_t* cinv = nullptr;
+  // the expert of each pair [T][k] (the single-token kernels read the
+  // routing directly: slot j's weights and activation row in one step)
+  const int32_t* cidx = nullptr;
   const float* cw = nullptr;
   const float* cres = nullptr;
   float* cy = nullptr;

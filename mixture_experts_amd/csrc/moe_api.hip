@@ -407,6 +407,9 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
     int hint = 2 * avg < 16 ? 16 : 2 * avg;
     ea.rows_hint = T < hint ? T : hint;
   }
+  // the single-token kernels find each slot's expert and rows through these
+  ea.cinv = L->inv;
+  ea.cidx = L->idx;
   if (!mark(MOE_STAGE_GATE_UP)) return MOE_ERR_DEVICE;
   if (ea.u8) {  // the uint8 kernels take fp16 token operands
     if (!fold_x16 &&
@@ -424,7 +427,6 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
   // the streaming down projection may take step 5 over (then the combine
   // stage below is empty)
   bool combined = false;
-  ea.cinv = L->inv;  // the single-token down projection finds its rows through it
   if (stream_path && !(d.flags & MOE_FLAG_COMBINE_SEPARATE)) {
     ea.cw = L->w;
     ea.cres = resid;
