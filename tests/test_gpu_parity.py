@@ -239,11 +239,12 @@ def test_mixtral_decode_every_row(T, flags):
 
 
 def grouped_down_plan(counts, H, F, E, S, cus):
-    """Host replica of the grouped down projection's persistent schedule:
-    (K split, pieces per XCD share), pieces > 1 where the tail split runs."""
+    """Host replica of the grouped down projection's persistent schedule for a
+    layer that holds the tail-split workspace (then the K range stays whole: one
+    plane): (K split, pieces per XCD share), pieces > 1 where the tail split
+    runs."""
     nw = max(cus // 8, 1)
-    max_tiles = -(-S // 256) + min(E, S)
-    ksplit = 2 if (max_tiles * (H // 256) < 3 * 256 and F % 64 == 0) else 1
+    ksplit = 1
     ntt = int(sum(-(-int(c) // 256) for c in counts))
     ntiles = ksplit * ntt * (H // 256)
     nk_slice = F // ksplit // 32
