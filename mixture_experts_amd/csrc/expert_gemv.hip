@@ -132,45 +132,48 @@ __device__ __forceinline__ QParams qparams(const uint8_t* eb, int H, int F, int 
 }
 
 // ---------------------------------------------------------------- gate/up
-// LR: 1 KB pieces per weight row (K = H); WPE: waves per SIMD the register
-// budget is cut for.  x: the token's expert input (fp16 for uint8 experts,
-// bf16 otherwise); idx, inv: its routing (slot s: expert idx[s], activation
-// row inv[s]); act: [S][F] out.  (Tasks of two or four row pairs, and
-// two or five waves per SIMD, measured the same at the Mixtral width.)
-template <bool Q8, int LR, int WPE>
-__global__ __launch_bounds__(256, WPE) void gemv_gate_up_kernel(
-    const uint8_t* __restrict__ experts, uint64_t stride_b, const uint16_t* __restrict__ x,
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ inv, int ktop, int H, int F,
-    uint16_t* __restrict__ act) {
-  constexpr int WE = Q8 ? 1 : 2;  // bytes per weight
-  constexpr int V = 16 / WE;      // weights per 16-byte piece
-  const int lane = threadIdx.x & 63;
-  const int gw = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
-  const int NW = gridDim.x * 4;
-  // one token: its k slots reach k different experts, none beyond a capacity
-  // (an expert sees at most one pair); slot s writes activation row inv[s]
-  const int ntask = ktop * F;
-  if (gw >= ntask) return;
-  const size_t row_b = (size_t)H * WE;
-
-  // the token's operand at this lane's K positions, all pieces
-  Opnd<Q8> xo[LR];
-#pragma unroll
-  for (int i = 0; i < LR; ++i) {
-    const uint16_t* xp = x + i * 64 * V + lane * V;
-    const u32x4 a = *reinterpret_cast<const u32x4*>(xp);
-    const u32x4 b = Q8 ? *reinterpret_cast<const u32x4*>(xp + 8) : a;
-    xo[i] = opnd_of(a, b, (Opnd<Q8>*)nullptr);
-  }
-
+// One wave's gate/up tasks.  LR: 1 KB pieces per weight row (K = H).  x: the
+// token's expert input (fp16 for uint8 experts, bf16 otherwise); idx, inv:
+// its routing (slot s: expert idx[s], activation row inv[s]); act: [S][F]
+// out.  One token: its k slots reach k different experts, none beyond a
+// capacity (an expert sees at most one pair), so there are k * F tasks.
+template <bool Q8, int LR>
+struct GuTasks {
+  static constexpr int WE = Q8 ? 1 : 2;  // bytes per weight
+  static constexpr int V = 16 / WE;      // weights per 16-byte piece
   struct Task {
     u32x4 w[2][LR];  // gate row, up row
     const uint8_t* eb;
     int p, f;
   };
+  const uint8_t* experts;
+  uint64_t stride_b;
+  const uint16_t* x;
+  const int32_t* idx;
+  const int32_t* inv;
+  uint16_t* act;
+  int H, F, ntask, lane;
+  size_t row_b;
+  Opnd<Q8> xo[LR];  // the token's operand at this lane's K positions
+
+  __device__ __forceinline__ GuTasks(const uint8_t* experts_, uint64_t stride_b_,
+                                     const uint16_t* x_, const int32_t* idx_, const int32_t* inv_,
+                                     int ktop, int H_, int F_, uint16_t* act_)
+      : experts(experts_), stride_b(stride_b_), x(x_), idx(idx_), inv(inv_), act(act_), H(H_),
+        F(F_), ntask(ktop * F_), lane((int)threadIdx.x & 63), row_b((size_t)H_ * WE) {}
+
+  __device__ __forceinline__ void load_x() {
+#pragma unroll
+    for (int i = 0; i < LR; ++i) {
+      const uint16_t* xp = x + i * 64 * V + lane * V;
+      const u32x4 a = *reinterpret_cast<const u32x4*>(xp);
+      const u32x4 b = Q8 ? *reinterpret_cast<const u32x4*>(xp + 8) : a;
+      xo[i] = opnd_of(a, b, (Opnd<Q8>*)nullptr);
+    }
+  }
   // issue the loads of task t (t >= ntask: loads of the token row instead,
   // in bounds and cached, never used)
-  auto issue = [&](int t, Task& k) __attribute__((always_inline)) {
+  __device__ __forceinline__ void issue(int t, Task& k) const {
     const uint8_t* g;
     const uint8_t* u;
     if (t < ntask) {
@@ -189,8 +192,8 @@ __global__ __launch_bounds__(256, WPE) void gemv_gate_up_kernel(
       k.w[0][i] = ld_nt(g + i * 1024 + lane * 16);
       k.w[1][i] = ld_nt(u + i * 1024 + lane * 16);
     }
-  };
-  auto finish = [&](const Task& k) __attribute__((always_inline)) {
+  }
+  __device__ __forceinline__ void finish(const Task& k) const {
     QParams qg{1.0f, h2_t{0, 0}}, qu{1.0f, h2_t{0, 0}};
     if (Q8) {
       qg = qparams(k.eb, H, F, 0);
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(256, WPE) void gemv_gate_up_kernel(
       g *= qg.scale;
       u *= qu.scale;
     }
-    if (lane == 0) {
+    if (lane == 0 && k.p >= 0) {
       const __bf16 a = (__bf16)(silu_f32(g) * u);
       uint16_t bits = __builtin_bit_cast(uint16_t, a);
       if (Q8) {  // the bf16-rounded value in fp16 (exact in fp16's normal range)
@@ -220,138 +223,140 @@ __global__ __launch_bounds__(256, WPE) void gemv_gate_up_kernel(
       }
       act[(size_t)k.p * F + k.f] = bits;
     }
-  };
-
-  Task A, B;
-  int t = gw;
-  issue(t, A);
-  for (;;) {
-    const int tb = t + NW;
-    issue(tb, B);
-    finish(A);
-    if (tb >= ntask) break;
-    t = tb + NW;
-    issue(t, A);
-    finish(B);
-    if (t >= ntask) break;
   }
+  // tasks gw, gw + NW, ... (gw < ntask), the next one's loads in flight while
+  // the current one computes
+  __device__ __forceinline__ void run(int gw, int NW) const {
+    Task A, B;
+    int t = gw;
+    issue(t, A);
+    for (;;) {
+      const int tb = t + NW;
+      issue(tb, B);
+      finish(A);
+      if (tb >= ntask) break;
+      t = tb + NW;
+      issue(t, A);
+      finish(B);
+      if (t >= ntask) break;
+    }
+  }
+};
+
+// WPE: waves per SIMD the register budget is cut for.  (Tasks of two or four
+// row pairs, and two or five waves per SIMD, measured the same at the Mixtral
+// width.)
+template <bool Q8, int LR, int WPE>
+__global__ __launch_bounds__(256, WPE) void gemv_gate_up_kernel(
+    const uint8_t* __restrict__ experts, uint64_t stride_b, const uint16_t* __restrict__ x,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ inv, int ktop, int H, int F,
+    uint16_t* __restrict__ act) {
+  const int gw = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
+  GuTasks<Q8, LR> gu(experts, stride_b, x, idx, inv, ktop, H, F, act);
+  if (gw >= gu.ntask) return;
+  gu.load_x();
+  gu.run(gw, gridDim.x * 4);
 }
 
 // ------------------------------------------------------------- down + combine
-// LDS of the down kernel: the activation rows of the token's routed slots
-// (F 16-bit values each) and the slot table, 80 KB in all, so that two
-// workgroups share a CU.
+// LDS of the down projection: the activation rows of the token's routed
+// slots (F 16-bit values each) and the slot table, 80 KB in all, so that two
+// workgroups share a CU.  The slot table holds byte offsets into the expert
+// blocks, not pointers: a weight address formed from the kernel's expert
+// pointer is a global load (a pointer read back from LDS would make every
+// weight load a flat one, which also counts as an LDS access and holds up
+// the waits for the activation reads).
 constexpr int kDnMaxSlots = 8;
 constexpr int kDnActElems = (80 * 1024 - 256) / 2;
+struct DnLds {
+  uint16_t act[kDnActElems];
+  uint64_t sl_off[kDnMaxSlots];  // byte offset of the slot's down matrix in the expert blocks
+  float sl_w[kDnMaxSlots];             // its gate weight
+  int sl_p[kDnMaxSlots];               // its activation row
+  int sl_n;
+};
+static_assert(sizeof(DnLds) <= 80 * 1024, "two workgroups per CU");
+// the block through an LDS pointer, so that every access is a ds_ operation
+typedef __attribute__((address_space(3))) DnLds* DnLdsP;
+typedef __attribute__((address_space(3))) const uint16_t lds_cu16;
+typedef __attribute__((address_space(3))) const u32x4 lds_cu32x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-// CH: 1 KB pieces per chunk of a down row (K = F); a row is nch chunks.
-// WGW: waves per workgroup (two workgroups per CU share its LDS).  FOLD: y
-// written here (step 5); else the per-slot rows yp[p][h].  (Tasks of two
-// or four hidden rows measured the same at the Mixtral width.)
-template <bool Q8, int CH, int WGW, bool FOLD>
-__global__ __launch_bounds__(64 * WGW, 4) void gemv_down_kernel(
-    const uint8_t* __restrict__ experts, uint64_t stride_b, const uint16_t* __restrict__ act,
-    const int32_t* __restrict__ idx, int H, int F, int k, int nch,
-    const float* __restrict__ cw, const int32_t* __restrict__ cinv, const float* cres, float* cy,
-    float* __restrict__ yp) {
+// The token's slots that reach an expert, in slot order (thread 0).
+template <bool Q8, bool FOLD>
+__device__ __forceinline__ void dn_slot_table(DnLdsP L, uint64_t stride_b,
+                                              const int32_t* idx, const int32_t* cinv,
+                                              const float* cw, int k, int H, int F) {
   constexpr int WE = Q8 ? 1 : 2;
-  constexpr int V = 16 / WE;
-  __shared__ __attribute__((aligned(16))) uint16_t act_lds[kDnActElems];
-  __shared__ const uint8_t* sl_row[kDnMaxSlots];  // down matrix of the slot's expert
-  __shared__ float sl_w[kDnMaxSlots];             // its gate weight
-  __shared__ int sl_p[kDnMaxSlots];               // its activation row
-  __shared__ int sl_n;
-  const int lane = threadIdx.x & 63;
-  const int gw = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * WGW + (threadIdx.x >> 6)));
-  const int NW = gridDim.x * WGW;
-  const int ntask = H;  // one hidden row per task
-  const size_t row_b = (size_t)F * WE;
-
-  if (threadIdx.x == 0) {  // the token's slots that reach an expert, in slot order
-    int v = 0;
-    for (int j = 0; j < k; ++j) {
-      const int p = cinv[j], e = idx[j];
-      if (p < 0) continue;  // dropped by the expert capacity
-      sl_row[v] = experts + stride_b * e + 2 * (size_t)F * H * WE;
-      sl_w[v] = FOLD ? cw[j] : 0.0f;
-      sl_p[v] = p;
-      ++v;
-    }
-    sl_n = v;
+  int v = 0;
+  for (int j = 0; j < k; ++j) {
+    const int p = cinv[j], e = idx[j];
+    if (p < 0) continue;  // dropped by the expert capacity
+    L->sl_off[v] = stride_b * e + 2 * (size_t)F * H * WE;
+    L->sl_w[v] = FOLD ? cw[j] : 0.0f;
+    L->sl_p[v] = p;
+    ++v;
   }
-  __syncthreads();
-  const int nv = sl_n;
-  const int nseq = nv * nch;  // chunks per task
-  if (nseq == 0) {  // no slot reached an expert: y = residual (+ nothing)
-    if (FOLD && lane == 0)
-      for (int h = gw; h < H; h += NW) cy[h] = cres ? cres[h] + 0.0f : 0.0f;
-    return;
-  }
+  L->sl_n = v;
+}
 
+// One wave's down tasks: task = hidden row h over every routed slot, in
+// chunks of CH pieces (nch chunks per row); FOLD: y[h] written here (step 5),
+// else the per-slot rows yp[p][h].
+template <bool Q8, int CH, bool FOLD>
+struct DnTasks {
+  static constexpr int WE = Q8 ? 1 : 2;
+  static constexpr int V = 16 / WE;
   struct Chunk {
     u32x4 w[CH];
     int v, c;  // slot (of the nv), chunk of the row
   };
-  // issue chunk q of task tk (tk >= ntask: loads of the first activation
-  // row instead, in bounds and cached, never used)
-  auto issue = [&](int tk, int q, Chunk& ck) __attribute__((always_inline)) {
-    const uint8_t* src = reinterpret_cast<const uint8_t*>(act);
-    if (tk < ntask) {
+  DnLdsP L;
+  const uint8_t* experts;  // (weight addresses from it: global loads)
+  const uint16_t* act;
+  const float* cres;
+  float* cy;
+  float* yp;
+  int H, F, nch, nv, nseq, NW, lane;
+  size_t row_b;
+  float a0 = 0.f, a1 = 0.f;  // the current slot's partial sums (even / odd pieces)
+  float yacc = 0.f;          // step 5 for the task's row
+
+  __device__ __forceinline__ DnTasks(DnLdsP L_, const uint8_t* experts_, const uint16_t* act_,
+                                     const float* cres_, float* cy_, float* yp_, int H_, int F_,
+                                     int nch_, int NW_)
+      : L(L_), experts(experts_), act(act_), cres(cres_), cy(cy_), yp(yp_), H(H_), F(F_), nch(nch_), nv(L_->sl_n),
+        nseq(L_->sl_n * nch_), NW(NW_), lane((int)threadIdx.x & 63), row_b((size_t)F_ * WE) {}
+
+  // issue chunk q of task tk (tk >= H: loads of the first weight bytes
+  // instead, in bounds, never used)
+  __device__ __forceinline__ void issue(int tk, int q, Chunk& ck) const {
+    const uint8_t* src = experts;
+    if (tk < H) {
       ck.v = q / nch;
       ck.c = q - ck.v * nch;
-      src = sl_row[ck.v] + (size_t)tk * row_b + (size_t)ck.c * CH * 1024;
+      src = experts + L->sl_off[ck.v] + (size_t)tk * row_b + (size_t)ck.c * CH * 1024;
     }
 #pragma unroll
     for (int i = 0; i < CH; ++i) ck.w[i] = ld_nt(src + i * 1024 + lane * 16);
-  };
-
-  // next chunk of the sequence (task t, chunk q of nseq) of this wave: tasks
-  // gw, gw + NW, ...
-  auto next = [&](int t, int q, int& t2, int& q2) __attribute__((always_inline)) {
+  }
+  // next chunk of the sequence (task t, chunk q of nseq): tasks gw, gw + NW, ...
+  __device__ __forceinline__ void next(int t, int q, int& t2, int& q2) const {
     q2 = q + 1;
     t2 = t;
     if (q2 == nseq) {
       q2 = 0;
       t2 = t + NW;
     }
-  };
-  // The slots' activation rows go to LDS.  Their loads are issued first, then
-  // the wave's first two weight chunks: waiting for the activation (the
-  // oldest loads) leaves both chunks in flight.
-  constexpr int kStage = (kDnActElems / 8 + 64 * WGW - 1) / (64 * WGW);
-  const int per = F / 8, tot = nv * per;  // 16-byte pieces of one row, of all
-  u32x4 stage[kStage];
-#pragma unroll
-  for (int m = 0; m < kStage; ++m) {
-    const int i = threadIdx.x + m * 64 * WGW;
-    if (i < tot) {
-      const int v = i / per;
-      stage[m] = reinterpret_cast<const u32x4*>(act + (size_t)sl_p[v] * F)[i - v * per];
-    }
   }
-  Chunk A, B;
-  int ta = gw, qa = 0, tb, qb;
-  next(ta, qa, tb, qb);
-  issue(ta, qa, A);
-  issue(tb, qb, B);
-#pragma unroll
-  for (int m = 0; m < kStage; ++m) {
-    const int i = threadIdx.x + m * 64 * WGW;
-    if (i < tot) reinterpret_cast<u32x4*>(act_lds)[i] = stage[m];
-  }
-  __syncthreads();
-  if (ta >= ntask) return;
-
-  float a0 = 0.f, a1 = 0.f;  // the current slot's partial sums (even / odd pieces)
-  float yacc = 0.f;          // step 5 for the task's row
-  auto finish = [&](int tk, const Chunk& ck) __attribute__((always_inline)) {
+  __device__ __forceinline__ void finish(int tk, const Chunk& ck) {
     QParams qd{1.0f, h2_t{0, 0}};
-    if (Q8) qd = qparams(sl_row[ck.v] - 2 * (size_t)F * H * WE, H, F, 2);
-    const uint16_t* arow = act_lds + (size_t)ck.v * F + (size_t)ck.c * CH * 64 * V + lane * V;
+    if (Q8) qd = qparams(experts + L->sl_off[ck.v] - 2 * (size_t)F * H * WE, H, F, 2);
+    lds_cu16* arow = L->act + (size_t)ck.v * F + (size_t)ck.c * CH * 64 * V + lane * V;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const u32x4 xa = *reinterpret_cast<const u32x4*>(arow + i * 64 * V);
-      const u32x4 xb = Q8 ? *reinterpret_cast<const u32x4*>(arow + i * 64 * V + 8) : xa;
+      const u32x4 xa = *(lds_cu32x4*)(arow + i * 64 * V);
+      const u32x4 xb = Q8 ? *(lds_cu32x4*)(arow + i * 64 * V + 8) : xa;
       const Opnd<Q8> xo = opnd_of(xa, xb, (Opnd<Q8>*)nullptr);
       if (i & 1) a1 = dot_piece(ck.w[i], xo, qd.bias, a1);
       else a0 = dot_piece(ck.w[i], xo, qd.bias, a0);
@@ -362,27 +367,97 @@ __global__ __launch_bounds__(64 * WGW, 4) void gemv_down_kernel(
     if (Q8) o *= qd.scale;
     const int h = tk;
     if (FOLD) {
-      yacc = fmaf(sl_w[ck.v], o, yacc);
+      yacc = fmaf(L->sl_w[ck.v], o, yacc);
       if (ck.v + 1 == nv) {  // the row's last slot
         if (lane == 0) cy[h] = cres ? cres[h] + yacc : yacc;
         yacc = 0.f;
       }
     } else if (lane == 0) {
-      yp[(size_t)sl_p[ck.v] * H + h] = o;
+      yp[(size_t)L->sl_p[ck.v] * H + h] = o;
     }
-  };
-
-  // two chunks in flight: finish one, issue the one after the other
-  for (;;) {
-    finish(ta, A);
-    if (tb >= ntask) break;
-    next(tb, qb, ta, qa);
-    issue(ta, qa, A);
-    finish(tb, B);
-    if (ta >= ntask) break;
-    next(ta, qa, tb, qb);
-    issue(tb, qb, B);
   }
+  // chunks A = (ta, qa) and B = (tb, qb) in flight (ta < H): finish one,
+  // issue the one after the other
+  __device__ __forceinline__ void run(int ta, int qa, int tb, int qb, Chunk& A, Chunk& B) {
+    for (;;) {
+      finish(ta, A);
+      if (tb >= H) break;
+      next(tb, qb, ta, qa);
+      issue(ta, qa, A);
+      finish(tb, B);
+      if (ta >= H) break;
+      next(ta, qa, tb, qb);
+      issue(tb, qb, B);
+    }
+  }
+  // no slot reached an expert: y = residual (+ nothing)
+  __device__ __forceinline__ void empty(int gw) const {
+    if (FOLD && lane == 0)
+      for (int h = gw; h < H; h += NW) cy[h] = cres ? cres[h] + 0.0f : 0.0f;
+  }
+};
+
+// The slots' activation rows to LDS, by the workgroup's 64 * WGW threads, in
+// two halves: load (into registers) and store, so that loads issued in
+// between stay in flight.
+template <int WGW>
+struct ActStage {
+  static constexpr int kN = (kDnActElems / 8 + 64 * WGW - 1) / (64 * WGW);
+  u32x4 r[kN];
+  __device__ __forceinline__ void load(DnLdsP L, const uint16_t* act, int F) {
+    const int per = F / 8, tot = L->sl_n * per;  // 16-byte pieces of one row, of all
+#pragma unroll
+    for (int m = 0; m < kN; ++m) {
+      const int i = threadIdx.x + m * 64 * WGW;
+      if (i < tot) {
+        const int v = i / per;
+        r[m] = reinterpret_cast<const u32x4*>(act + (size_t)L->sl_p[v] * F)[i - v * per];
+      }
+    }
+  }
+  __device__ __forceinline__ void store(DnLdsP L, int F) const {
+    const int tot = L->sl_n * (F / 8);
+#pragma unroll
+    for (int m = 0; m < kN; ++m) {
+      const int i = threadIdx.x + m * 64 * WGW;
+      if (i < tot) ((lds_u32x4*)L->act)[i] = r[m];
+    }
+  }
+};
+
+// CH: 1 KB pieces per chunk of a down row (K = F).  WGW: waves per workgroup
+// (two workgroups per CU share its LDS).  (Tasks of two or four hidden rows
+// measured the same at the Mixtral width.)
+template <bool Q8, int CH, int WGW, bool FOLD>
+__global__ __launch_bounds__(64 * WGW, 4) void gemv_down_kernel(
+    const uint8_t* __restrict__ experts, uint64_t stride_b, const uint16_t* __restrict__ act,
+    const int32_t* __restrict__ idx, int H, int F, int k, int nch,
+    const float* __restrict__ cw, const int32_t* __restrict__ cinv, const float* cres, float* cy,
+    float* __restrict__ yp) {
+  __shared__ __attribute__((aligned(16))) DnLds Ls;
+  const DnLdsP L = (DnLdsP)&Ls;
+  const int gw = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * WGW + (threadIdx.x >> 6)));
+  if (threadIdx.x == 0) dn_slot_table<Q8, FOLD>(L, stride_b, idx, cinv, cw, k, H, F);
+  __syncthreads();
+  DnTasks<Q8, CH, FOLD> dn(L, experts, act, cres, cy, yp, H, F, nch, gridDim.x * WGW);
+  if (dn.nseq == 0) {
+    dn.empty(gw);
+    return;
+  }
+  // The activation rows' loads are issued first, then the wave's first two
+  // weight chunks: waiting for the activation (the oldest loads) leaves both
+  // chunks in flight.
+  ActStage<WGW> stage;
+  stage.load(L, act, F);
+  typename DnTasks<Q8, CH, FOLD>::Chunk A, B;
+  int ta = gw, qa = 0, tb, qb;
+  dn.next(ta, qa, tb, qb);
+  dn.issue(ta, qa, A);
+  dn.issue(tb, qb, B);
+  stage.store(L, F);
+  __syncthreads();
+  if (ta >= H) return;
+  dn.run(ta, qa, tb, qb, A, B);
 }
 
 template <bool Q8, int LR, int WPE>

@@ -1,7 +1,8 @@
 """Forward calls captured in a HIP graph and replayed: every replay equals the
 eager result bit for bit, with eager work of the same layer (on other inputs)
 between the replays.  One case per launch sequence: the single-token route
-with the folded combine (plain, residual, uint8 experts), the router and
+with the folded combine (plain, residual, uint8 experts, rows of 4 and 8 KB),
+the router and
 dispatch kernels with the grouped GEMMs, and the LDS-staged router with the
 streaming kernels."""
 import numpy as np
@@ -24,6 +25,8 @@ CASES = [
     (4096, 256, 8, 2, 1, 0, False),
     (4096, 256, 8, 2, 1, moe.MOE_FLAG_RESIDUAL_PRENORM, False),
     (4096, 256, 8, 2, 1, 0, True),
+    (2048, 2048, 8, 2, 1, 0, False),
+    (4096, 4096, 8, 2, 1, moe.MOE_FLAG_RESIDUAL_PRENORM, True),
     (1024, 512, 8, 2, 700, moe.MOE_FLAG_PATH_GROUPED, False),
     (2048, 256, 64, 2, 200, 0, False),
 ]
