@@ -157,7 +157,7 @@ __device__ __forceinline__ void topk_rank_row(const float* row, int t, int E, in
 // tile0 + rows (interleaved so that small batches still spread over the
 // waves).  lg: LDS logits [rows][ldl].  idx_lds (optional): an LDS copy of the
 // picks of the tile, [RT_TOK][k].  k > MOE_MAX_TOPK takes topk_rank_row with
-// ex_lds: [nwaves][MOE_MAX_EXPERTS] doubles of LDS.
+// ex_lds: [nwaves][MOE_MAX_EXPERTS] doubles of LDS (required then).
 __device__ __forceinline__ void topk_rows(const float* lg, int ldl, int tile0, int T, int E, int k, int raw,
                           int32_t* idx_out, float* w_out, int nwaves = 4,
                           int32_t* idx_lds = nullptr, int rows = RT_TOK,
@@ -727,6 +727,8 @@ __global__ __launch_bounds__(256) void route_small_kernel(
     lg[t * ldl + e] = s;
   }
   __syncthreads();
+  // (no LDS for the top-k-by-ranks path: the small-batch routes are taken
+  // only with k <= MOE_MAX_TOPK)
   topk_rows(lg, ldl, 0, T, E, k, raw, idx_out, w_out, 4, idx_l);
   __syncthreads();
   if (tid == 0) *counter = 0;  // ready for the next launch
