@@ -11,10 +11,11 @@
 // of the hidden dimension (split so that the batch fills over a thousand
 // workgroups) with v_mfma_f32_16x16x32_bf16 (tokens as the A operand, the
 // transposed router as the B operand, read from L2 or, for many experts,
-// staged in LDS; fp32 accumulation); a second kernel adds the slices in a
-// fixed order (+ bias) and selects, one token per wave, with the experts
-// spread over the 64 lanes and a DPP max-reduction over (value desc, index
-// asc).  Batches of up to 64 tokens route and dispatch in one launch (the
+// staged in LDS; fp32 accumulation; the next hidden step's operands loaded
+// during this one's MFMAs); a second kernel adds the slices in a fixed order
+// (+ bias) and selects with a DPP max-reduction over (value desc, index asc):
+// one token per 16-lane row, each lane holding up to 16 experts' sums in
+// registers (k beyond 8: one token per wave, ranks).  Batches of up to 64 tokens route and dispatch in one launch (the
 // one-workgroup kernels below).  fp32 layers use one plain-FMA kernel.  The
 // softmax over the k picks is evaluated in fp64.
 #include "common.h"
@@ -282,6 +283,54 @@ __device__ __forceinline__ void topk_rows16(const float* lg, int ldl, int tile0,
   }
 }
 
+// The same top-k + softmax (k <= MOE_MAX_TOPK) for one token per 16-lane row
+// with C candidates per lane already in registers: lane el of the row holds
+// the logits of experts el, el + 16, ..., el + 16 (C - 1) (avail: which of
+// them exist).  Each pick is the lane's best candidate, then the row's best
+// by DPP rotations (the same total order, so the same picks as topk_rows);
+// the softmax as in topk_rows16.  Token t is written when ok.
+template <int C>
+__device__ __forceinline__ void topk_row16c(const float (&v)[C], uint32_t avail, bool ok, int t,
+                                            int k, int raw, int32_t* idx_out, float* w_out) {
+  const int el = threadIdx.x & 15;
+  float my_v = 0.0f, m = 0.0f;
+  int my_e = 0;
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    if (j >= k) break;
+    Cand best{0.0f, INT32_MAX};
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const Cand cand{v[c], (avail >> c & 1u) ? el + 16 * c : INT32_MAX};
+      if (better(cand, best)) best = cand;
+    }
+    best = row_best16(best);
+    if (best.e != INT32_MAX && (best.e & 15) == el) avail &= ~(1u << (best.e >> 4));
+    if (el == j) {
+      my_v = best.v;
+      my_e = best.e;
+    }
+    if (j == 0) m = best.v;
+  }
+  const double ex = (el < k && !raw) ? exp((double)my_v - (double)m) : 0.0;
+  double s = ex;
+#pragma unroll
+  for (int j = 1; j < MOE_MAX_TOPK; ++j) {
+    if (j >= k) break;
+    const double prev = dpp_d<0x111>(s);  // row_shr:1
+    if (el == j) s = prev + s;
+  }
+  double z = (el == k - 1) ? s : 0.0;
+  z += dpp_d<0x128>(z);
+  z += dpp_d<0x124>(z);
+  z += dpp_d<0x122>(z);
+  z += dpp_d<0x121>(z);
+  if (ok && el < k) {
+    idx_out[(size_t)t * k + el] = my_e;
+    w_out[(size_t)t * k + el] = raw ? my_v : (float)(ex / z);
+  }
+}
+
 // Dispatch of S = T*k <= RT_TOK*8 slots whose expert ids are in LDS
 // (idx_lds[S], published to wave 0), by wave 0 alone: it ranks the slots of
 // each expert with ballot matches in slot order, scans the counts (capped at
@@ -431,8 +480,10 @@ __global__ __launch_bounds__(256) void router_partial_kernel(
     const int e = n * 16 + (lane & 15);
     wrow[n] = wrt + (size_t)(e < E ? e : 0) * H + hb + kq;
   }
-  for (int h = 0; h < hslice; h += 4 * 32) {  // hslice is a multiple of RT_HC (64)
-    u32x4 av[4], bv[4][NT];
+  // operands of 128 hidden units per step, the next step's loads issued
+  // before this step's MFMAs
+  u32x4 av[4], bv[4][NT];
+  auto load = [&](int h) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       if (h + s * 32 < hslice) {
@@ -440,12 +491,23 @@ __global__ __launch_bounds__(256) void router_partial_kernel(
 #pragma unroll
         for (int n = 0; n < NT; ++n) bv[s][n] = ldg16(wrow[n] + h + s * 32);
       }
+  };
+  load(0);
+  for (int h = 0; h < hslice; h += 4 * 32) {  // hslice is a multiple of RT_HC (64)
+    u32x4 ca[4], cb[4][NT];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      ca[s] = av[s];
+#pragma unroll
+      for (int n = 0; n < NT; ++n) cb[s][n] = bv[s][n];
+    }
+    if (h + 4 * 32 < hslice) load(h + 4 * 32);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       if (h + s * 32 < hslice)
 #pragma unroll
         for (int n = 0; n < NT; ++n)
-          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[s]), as_bf16x8(bv[s][n]),
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ca[s]), as_bf16x8(cb[s][n]),
                                                            acc[n], 0, 0, 0);
   }
   // C layout: lane holds column (expert) lane%16, rows 4*(lane/16) + j;
@@ -501,17 +563,27 @@ __global__ __launch_bounds__(256) void router_partial_lds_kernel(
       *reinterpret_cast<u32x4*>(&wl[b][row * LW + c * 8]) = r[i];
     }
   };
+  // the token operands of a chunk are loaded a chunk ahead
+  u32x4 an[4];
+  auto tok_load = [&](int h) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      an[s] = (tok_ok && h + s * 32 < hslice) ? ldg16(xrow + h + s * 32) : u32x4{0u, 0u, 0u, 0u};
+  };
   stage_load(0);
+  tok_load(0);
   stage_store(0);
   __syncthreads();
   int b = 0;
   for (int h = 0; h < hslice; h += CH) {
     const bool more = h + CH < hslice;
-    if (more) stage_load(h + CH);
     u32x4 av[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      av[s] = (tok_ok && h + s * 32 < hslice) ? ldg16(xrow + h + s * 32) : u32x4{0u, 0u, 0u, 0u};
+    for (int s = 0; s < 4; ++s) av[s] = an[s];
+    if (more) {
+      stage_load(h + CH);
+      tok_load(h + CH);
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       if (h + s * 32 < hslice)
@@ -538,10 +610,55 @@ __global__ __launch_bounds__(256) void router_partial_lds_kernel(
   }
 }
 
-// Sum of the partial logits in split order (+ bias), then top-k and softmax.
+// Sum of the partial logits in split order (+ bias), then top-k and softmax,
+// for k <= MOE_MAX_TOPK and E <= 16 C: 16 tokens per workgroup, one per
+// 16-lane row (lane el sums and ranks experts el + 16 c in registers, no LDS).
+// The splits are read four at a time, all loads of a group in flight.
 // nsplit == 0: `part` holds caller-given logits [T][E], used as they are.
-// RK_TOK tokens per workgroup, one per wave: the selection is a chain of
-// cross-lane steps, so many waves in flight, not many tokens per wave, hide it.
+constexpr int RK16_TOK = 16;
+template <int C>
+__global__ __launch_bounds__(256) void router_topk16_kernel(const float* __restrict__ part,
+                                                            int nsplit, int T, int E, int k,
+                                                            int raw, const float* __restrict__ bias,
+                                                            int32_t* __restrict__ idx_out,
+                                                            float* __restrict__ w_out) {
+  const int el = threadIdx.x & 15;
+  const int t = blockIdx.x * RK16_TOK + (threadIdx.x >> 4);
+  const bool ok = t < T;
+  uint32_t avail = 0;
+  float v[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const bool in = ok && el + 16 * c < E;
+    avail |= (uint32_t)in << c;
+    v[c] = 0.0f;
+  }
+  const int np = nsplit > 0 ? nsplit : 1;
+  for (int p0 = 0; p0 < np; p0 += 4) {
+    float q[4][C];
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+        q[d][c] = (p0 + d < np && (avail >> c & 1u))
+                      ? part[((size_t)(p0 + d) * T + t) * E + el + 16 * c]
+                      : 0.0f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+        if (p0 + d < np) v[c] = (p0 + d == 0) ? q[d][c] : v[c] + q[d][c];
+  }
+  if (nsplit > 0 && bias) {
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+      if (avail >> c & 1u) v[c] += bias[el + 16 * c];
+  }
+  topk_row16c<C>(v, avail, ok, t, k, raw, idx_out, w_out);
+}
+
+// The same for k > MOE_MAX_TOPK (top-k by ranks): RK_TOK tokens per
+// workgroup, one per wave, the sums staged in LDS.
 constexpr int RK_TOK = 4;
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ part,
                                                           int nsplit, int T, int E, int k, int raw,
@@ -1108,9 +1225,27 @@ int router_splits(int T, int H, int E) {
   return ns;
 }
 
+// Step 2 over the logits (nsplit partial planes, or given logits with 0).
+static void launch_topk(const float* part, int nsplit, const RouterArgs& a, const float* bias,
+                 hipStream_t st) {
+  if (a.k > MOE_MAX_TOPK) {
+    const int kgrid = (a.T + RK_TOK - 1) / RK_TOK;
+    router_topk_kernel<<<kgrid, 256, 0, st>>>(part, nsplit, a.T, a.E, a.k, a.raw_gate, bias,
+                                              a.idx, a.w);
+    return;
+  }
+  const int grid = (a.T + RK16_TOK - 1) / RK16_TOK;
+#define RK16_ARGS part, nsplit, a.T, a.E, a.k, a.raw_gate, bias, a.idx, a.w
+  if (a.E <= 16) router_topk16_kernel<1><<<grid, 256, 0, st>>>(RK16_ARGS);
+  else if (a.E <= 32) router_topk16_kernel<2><<<grid, 256, 0, st>>>(RK16_ARGS);
+  else if (a.E <= 64) router_topk16_kernel<4><<<grid, 256, 0, st>>>(RK16_ARGS);
+  else if (a.E <= 128) router_topk16_kernel<8><<<grid, 256, 0, st>>>(RK16_ARGS);
+  else router_topk16_kernel<16><<<grid, 256, 0, st>>>(RK16_ARGS);
+#undef RK16_ARGS
+}
+
 int launch_router(const RouterArgs& a, hipStream_t st) {
   const int grid = (a.T + RT_TOK - 1) / RT_TOK;
-  const int kgrid = (a.T + RK_TOK - 1) / RK_TOK;
   if (a.dtype_f32) {
     router_f32_kernel<<<grid, 256, 0, st>>>((const float*)a.x, a.T, a.H, a.E, a.k, a.raw_gate,
                                             (const float*)a.wr, a.bias, a.logits_in, a.idx,
@@ -1118,8 +1253,7 @@ int launch_router(const RouterArgs& a, hipStream_t st) {
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
   if (a.logits_in) {
-    router_topk_kernel<<<kgrid, 256, 0, st>>>(a.logits_in, 0, a.T, a.E, a.k, a.raw_gate, nullptr, a.idx,
-                                              a.w);
+    launch_topk(a.logits_in, 0, a, nullptr, st);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
   const int ns = router_splits(a.T, a.H, a.E);
@@ -1140,8 +1274,7 @@ int launch_router(const RouterArgs& a, hipStream_t st) {
     router_partial_lds_kernel<8><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, wt, hs, a.part);
   else
     router_partial_lds_kernel<16><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, wt, hs, a.part);
-  router_topk_kernel<<<kgrid, 256, 0, st>>>(a.part, ns, a.T, a.E, a.k, a.raw_gate, a.bias, a.idx,
-                                            a.w);
+  launch_topk(a.part, ns, a, a.bias, st);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
