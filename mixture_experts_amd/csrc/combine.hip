@@ -9,12 +9,16 @@
 // each output element is owned by one thread, which fixes the order.  The
 // residual is taken inside the forward call as on www.pnsm.cn page sec. 2.1.
 // HBM-bound: 16-byte loads and stores, consecutive threads on consecutive
-// columns.
+// columns; for k <= 8 a thread's k row loads are in flight together.
 #include "common.h"
 #include "kernels.h"
 
 namespace {
 
+// KT > 0: k == KT and nplanes == NP fixed at compile time, so that a
+// thread's KT (x NP) row loads are issued together, then summed in slot
+// order; KT == 0: any k and nplanes, slot by slot.
+template <int KT, int NP>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ yp,
                                                       int nplanes,
                                                       const float* __restrict__ w,
@@ -27,18 +31,47 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int t = (int)(i / h4n), c = (int)(i % h4n) * 4;
   const int S = T * k;
   f32x4 acc{0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const float wj = w[(size_t)t * k + j];
-    const int pi = inv[(size_t)t * k + j];
-    if (pi < 0) continue;  // a pair dropped by the expert capacity
-    const int p = min(pi, S - 1);  // in range by construction
-    // each per-pair row is read once: non-temporal loads
-    f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(yp + (size_t)p * H + c));
-    for (int pl = 1; pl < nplanes; ++pl)  // partial sums of a split K, in plane order
-      v += __builtin_nontemporal_load(
-          reinterpret_cast<const f32x4*>(yp + ((size_t)pl * S + p) * H + c));
+  if constexpr (KT > 0) {
+    float wj[KT];
+    int pj[KT];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[q] = fmaf(wj, v[q], acc[q]);
+    for (int j = 0; j < KT; ++j) {
+      wj[j] = w[(size_t)t * KT + j];
+      pj[j] = inv[(size_t)t * KT + j];
+    }
+    // each per-pair row is read once: non-temporal loads; a pair dropped by
+    // the expert capacity (inv < 0) reads row 0 and adds nothing
+    f32x4 v[KT][NP];
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      const int p = min(max(pj[j], 0), S - 1);  // in range by construction
+#pragma unroll
+      for (int pl = 0; pl < NP; ++pl)
+        v[j][pl] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(yp + ((size_t)pl * S + p) * H + c));
+    }
+#pragma unroll
+    for (int j = 0; j < KT; ++j) {
+      f32x4 u = v[j][0];
+#pragma unroll
+      for (int pl = 1; pl < NP; ++pl) u += v[j][pl];  // split-K partial sums, in plane order
+      const bool kept = pj[j] >= 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = kept ? fmaf(wj[j], u[q], acc[q]) : acc[q];
+    }
+  } else {
+    for (int j = 0; j < k; ++j) {
+      const float wj = w[(size_t)t * k + j];
+      const int pi = inv[(size_t)t * k + j];
+      if (pi < 0) continue;  // a pair dropped by the expert capacity
+      const int p = min(pi, S - 1);  // in range by construction
+      f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(yp + (size_t)p * H + c));
+      for (int pl = 1; pl < nplanes; ++pl)  // partial sums of a split K, in plane order
+        v += __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(yp + ((size_t)pl * S + p) * H + c));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = fmaf(wj, v[q], acc[q]);
+    }
   }
   if (resid) {
     const f32x4 r = *reinterpret_cast<const f32x4*>(resid + (size_t)t * H + c);
@@ -53,7 +86,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 int launch_combine(const float* yp, int nplanes, const float* w, const int32_t* inv,
                    const float* resid, int T, int H, int k, float* y, hipStream_t st) {
   const int64_t n = (int64_t)T * (H / 4);
-  combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(yp, nplanes, w, inv, resid, T, H,
-                                                              k, y);
+  const unsigned grid = (unsigned)((n + 255) / 256);
+#define COMBINE(KT, NP) combine_kernel<KT, NP><<<grid, 256, 0, st>>>(yp, nplanes, w, inv, resid, T, H, k, y)
+#define COMBINE_K(KT) \
+  case KT:            \
+    if (nplanes == 1) \
+      COMBINE(KT, 1); \
+    else              \
+      COMBINE(KT, 2); \
+    break
+  if (nplanes < 1 || nplanes > 2) {
+    COMBINE(0, 0);
+  } else {
+    switch (k) {
+      COMBINE_K(1);
+      COMBINE_K(2);
+      COMBINE_K(3);
+      COMBINE_K(4);
+      COMBINE_K(5);
+      COMBINE_K(6);
+      COMBINE_K(7);
+      COMBINE_K(8);
+      default: COMBINE(0, 0);
+    }
+  }
+#undef COMBINE_K
+#undef COMBINE
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

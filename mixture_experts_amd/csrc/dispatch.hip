@@ -98,10 +98,18 @@ __global__ __launch_bounds__(64) void dispatch_hist_kernel(const int32_t* __rest
   __syncthreads();
   const int base = blockIdx.x * DISPATCH_RUN;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // the run's expert ids, all loads in flight together
+  int ev[DISPATCH_RUN / 64];
+#pragma unroll
+  for (int c = 0; c < DISPATCH_RUN / 64; ++c) {
+    const int s = base + c * 64 + lane;
+    ev[c] = s < S ? idx[s] : 0;
+  }
+#pragma unroll
   for (int c = 0; c < DISPATCH_RUN / 64; ++c) {
     const int s = base + c * 64 + lane;
     const bool valid = s < S;
-    const int e = valid ? idx[s] : 0;
+    const int e = ev[c];
     uint64_t match = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (e >> b) & 1;
@@ -138,18 +146,30 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
   const int rq = (nrun + 3) / 4;  // runs per quarter
   const int r_beg = q * rq, r_end = min(nrun, r_beg + rq);
   int sum = 0;
+  int h0[16] = {};  // a quarter of at most 16 runs: its counts, kept for the second pass
   if (e < E) {
     for (int r0 = r_beg; r0 < r_end; r0 += 16) {
       int h[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) h[j] = r0 + j < r_end ? hist[(size_t)(r0 + j) * E + e] : 0;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) sum += h[j];
+      for (int j = 0; j < 16; ++j) {
+        sum += h[j];
+        h0[j] = h[j];
+      }
     }
   }
   qs[q][e] = sum;
   __syncthreads();
-  if (e < E) {
+  if (e < E && rq <= 16) {
+    int run = 0;
+    for (int p = 0; p < q; ++p) run += qs[p][e];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (r_beg + j < r_end) base[(size_t)(r_beg + j) * E + e] = run;
+      run += h0[j];
+    }
+  } else if (e < E) {
     int run = 0;
     for (int p = 0; p < q; ++p) run += qs[p][e];
     for (int r0 = r_beg; r0 < r_end; r0 += 16) {
@@ -162,12 +182,12 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
         run += h[j];
       }
     }
-    if (q == 0) {
-      int tot = qs[0][e] + qs[1][e] + qs[2][e] + qs[3][e];
-      if (cap > 0 && tot > cap) tot = cap;
-      counts[e] = tot;
-      sc[e] = tot;
-    }
+  }
+  if (e < E && q == 0) {
+    int tot = qs[0][e] + qs[1][e] + qs[2][e] + qs[3][e];
+    if (cap > 0 && tot > cap) tot = cap;
+    counts[e] = tot;
+    sc[e] = tot;
   }
   __syncthreads();
   expert_prefix(sc, E, tile_rows, offsets, tile_off, active, off_l);
@@ -212,7 +232,14 @@ __global__ __launch_bounds__(1024) void dispatch_one_kernel(
   __shared__ int32_t tot[MOE_MAX_EXPERTS];
   __shared__ int32_t off_l[MOE_MAX_EXPERTS + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < S; i += 1024) idx_l[i] = idx[i];
+  {  // the expert ids, all loads in flight together
+    int v[D1_MAX / 1024];
+#pragma unroll
+    for (int j = 0; j < D1_MAX / 1024; ++j) v[j] = tid + 1024 * j < S ? idx[tid + 1024 * j] : 0;
+#pragma unroll
+    for (int j = 0; j < D1_MAX / 1024; ++j)
+      if (tid + 1024 * j < S) idx_l[tid + 1024 * j] = v[j];
+  }
   for (int i = tid; i < 16 * MOE_MAX_EXPERTS; i += 1024) wh[i / MOE_MAX_EXPERTS][i % MOE_MAX_EXPERTS] = 0;
   __syncthreads();
   const int SW = ((S + 1023) / 1024) * 64;  // slots per wave
