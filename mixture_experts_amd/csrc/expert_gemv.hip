@@ -134,7 +134,8 @@ __device__ __forceinline__ QParams qparams(const uint8_t* eb, int H, int F, int 
 // ---------------------------------------------------------------- gate/up
 // One wave's gate/up tasks.  LR: 1 KB pieces per weight row (K = H).  x: the
 // token's expert input (fp16 for uint8 experts, bf16 otherwise); idx, inv:
-// its routing (slot s: expert idx[s], activation row inv[s]); act: [S][F]
+// its routing (slot s: expert idx[s], activation row inv[s], or row s when
+// inv is null); act: [S][F]
 // out.  One token: its k slots reach k different experts, none beyond a
 // capacity (an expert sees at most one pair), so there are k * F tasks.
 template <bool Q8, int LR>
@@ -180,7 +181,7 @@ struct GuTasks {
       const int s = t / F;
       k.f = t - s * F;
       const int e = idx[s];
-      k.p = inv[s];
+      k.p = inv ? inv[s] : s;
       k.eb = experts + stride_b * e;
       g = k.eb + (size_t)k.f * row_b;
       u = k.eb + (size_t)(F + k.f) * row_b;
@@ -290,7 +291,7 @@ __device__ __forceinline__ void dn_slot_table(DnLdsP L, uint64_t stride_b,
   constexpr int WE = Q8 ? 1 : 2;
   int v = 0;
   for (int j = 0; j < k; ++j) {
-    const int p = cinv[j], e = idx[j];
+    const int p = cinv ? cinv[j] : j, e = idx[j];
     if (p < 0) continue;  // dropped by the expert capacity
     L->sl_off[v] = stride_b * e + 2 * (size_t)F * H * WE;
     L->sl_w[v] = FOLD ? cw[j] : 0.0f;
@@ -532,13 +533,13 @@ bool gemv_supported(int T, int H, int F, int k, bool u8) {
 
 int launch_gemv_gate_up(const ExpertArgs& a, hipStream_t st) {
   if (!gemv_supported(a.T, a.H, a.F, a.k, a.u8)) return -1;
-  if (!a.experts || !a.x || !a.cidx || !a.cinv || !a.act) return -1;
+  if (!a.experts || !a.x || !a.cidx || !a.act) return -1;
   return a.u8 ? launch_gu_q<true>(a, st) : launch_gu_q<false>(a, st);
 }
 
 int launch_gemv_down(const ExpertArgs& a, bool* combined, hipStream_t st) {
   if (!gemv_supported(a.T, a.H, a.F, a.k, a.u8)) return -1;
-  if (!a.experts || !a.act || !a.cidx || !a.cinv) return -1;
+  if (!a.experts || !a.act || !a.cidx) return -1;
   const bool fold = combined && a.cy;
   if (fold ? !a.cw : !a.yp) return -1;
   if (combined) *combined = fold;

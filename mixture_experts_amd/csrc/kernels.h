@@ -53,6 +53,9 @@ struct DispatchArgs {
   int32_t* perm;       // [S]
   int32_t* inv;        // [S]
   int capacity;        // pairs an expert keeps, 0 = all
+  // the single-token route may leave the dispatch out (its outputs are then
+  // not written): the expert kernels that follow take the slots in order
+  bool none = false;
 };
 
 struct ExpertArgs {
@@ -72,9 +75,10 @@ struct ExpertArgs {
   // grouped GEMMs: partial sums of split tail tiles, one 256 KB slot per
   // workgroup (grouped_grid() of them), or null (no split)
   float* gws = nullptr;
-  // slot of each pair [T][k] (-1: dropped by the capacity); step 5 inputs
-  // for a down projection that folds the combine in (cy null: it may not):
-  // gate weights [T][k], residual [T][H] or null, output [T][H]
+  // slot of each pair [T][k] (-1: dropped by the capacity; the
+  // single-token kernels take null as slot j = row j, none dropped); step 5
+  // inputs for a down projection that folds the combine in (cy null: it may
+  // not): gate weights [T][k], residual [T][H] or null, output [T][H]
   const int32_t* cinv = nullptr;
   // the expert of each pair [T][k] (the single-token kernels read the
   // routing directly: slot j's weights and activation row in one step)

@@ -362,6 +362,7 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
   const bool gemv_path = stream_path && !(d.flags & MOE_FLAG_PATH_STREAM) &&
                          gemv_supported(T, d.hidden, d.ffn, d.top_k,
                                         d.expert_format == MOE_EXPERT_U8);
+  const bool slot_order = gemv_path && !(d.flags & MOE_FLAG_COMBINE_SEPARATE);
   {
     const moe_layer_desc& dd = L->d;
     RouterArgs ra{xin, T, dd.hidden, dd.num_experts, dd.top_k, f32 ? 1 : 0, dd.router_w,
@@ -369,6 +370,10 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
                   (dd.flags & MOE_FLAG_GATE_RAW) ? 1 : 0};
     DispatchArgs da{L->idx, S, dd.num_experts, GG_BT, L->hist, L->rank, L->base, L->counts,
                     L->offsets, L->tile_off, L->active, L->perm, L->inv, dd.expert_capacity};
+    // a single token on the matrix-vector kernels with the combine folded
+    // in: its activation rows in slot order, no dispatch (no pair of one
+    // token is ever dropped)
+    da.none = slot_order;
     if (fold_pn) {
       ra.hres = (const float*)x;
       ra.xt_out = L->xt;
@@ -408,7 +413,7 @@ int moe_forward_ev(moe_layer_t* L, const void* x, int32_t T, float* y, void* str
     ea.rows_hint = T < hint ? T : hint;
   }
   // the single-token kernels find each slot's expert and rows through these
-  ea.cinv = L->inv;
+  ea.cinv = slot_order ? nullptr : L->inv;
   ea.cidx = L->idx;
   if (!mark(MOE_STAGE_GATE_UP)) return MOE_ERR_DEVICE;
   if (ea.u8) {  // the uint8 kernels take fp16 token operands

@@ -1091,7 +1091,9 @@ __global__ __launch_bounds__(1024) void route_one_kernel(
 // order.  With hres (residual layers) the workgroup first forms the branch
 // input bf16(h / sqrt(mean h^2 + 1e-6)) the same way (squares, then the same
 // reductions) and writes it for the expert kernels; with x16_out it writes
-// the fp16 copy of the expert input.  Top-k and dispatch as in route_one.
+// the fp16 copy of the expert input.  Top-k and dispatch as in route_one;
+// with nodisp the dispatch is left out (the matrix-vector expert kernels
+// that follow take the slots in order).
 __device__ __forceinline__ float wave_sum_dpp(float v) {
 #define DPP_ADD(ctrl, rmask) \
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, rmask, 0xF, false))
@@ -1112,7 +1114,7 @@ __global__ __launch_bounds__(1024) void route_tiny_kernel(
     int cap, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off,
     int32_t* __restrict__ active, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
-    uint16_t* __restrict__ xt_out, uint16_t* __restrict__ x16_out) {
+    uint16_t* __restrict__ xt_out, uint16_t* __restrict__ x16_out, int nodisp) {
   constexpr int HPT = R1_HMAX / 1024;  // hidden units per thread, at most
   __shared__ float red[16][TT * 16];  // per-wave partial logits
   __shared__ float ssq[16][TT];
@@ -1204,6 +1206,7 @@ __global__ __launch_bounds__(1024) void route_tiny_kernel(
   }
   __syncthreads();
   topk_rows16(lg, 17, 0, T, E, k, raw, idx_out, w_out, 16, idx_l, 16);
+  if (nodisp) return;  // the expert kernels take the slots in order
   __syncthreads();
   dispatch_small(idx_l, T * k, E, tile_rows, cap, cnt, off_l, rank_l, counts, offsets,
                  tile_off, active, perm, inv);
@@ -1298,7 +1301,8 @@ int launch_route_small(const RouterArgs& a, const DispatchArgs& d, int32_t* coun
     auto* xx = (const uint16_t*)a.x;
     auto* ww = (const uint16_t*)a.wr;
 #define RT_ARGS xx, a.hres, a.T, a.H, a.E, a.k, a.raw_gate, ww, a.bias, d.tile_rows, d.capacity, \
-                a.idx, a.w, d.counts, d.offsets, d.tile_off, d.active, d.perm, d.inv, a.xt_out, a.x16_out
+                a.idx, a.w, d.counts, d.offsets, d.tile_off, d.active, d.perm, d.inv, a.xt_out, a.x16_out, \
+                d.none ? 1 : 0
     // a router row is one (E = 8) or two (E = 16) 16-byte loads
     if (a.E == 8) route_tiny_kernel<1, 8><<<1, 1024, 0, st>>>(RT_ARGS);
     else route_tiny_kernel<1, 16><<<1, 1024, 0, st>>>(RT_ARGS);
