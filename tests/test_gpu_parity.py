@@ -161,6 +161,10 @@ SMALL = [
     ("f32", 64, 128, 1, 1, 32, 0),
     # grouped down projection whose last tiles are split along K
     ("bf16", 256, 2048, 8, 2, 600, moe.MOE_FLAG_PATH_GROUPED),
+    # the separate combine at k = 3, 5 and 7 (its loads unrolled per k)
+    ("bf16", 256, 128, 8, 3, 200, moe.MOE_FLAG_PATH_GROUPED),
+    ("bf16", 256, 128, 16, 5, 150, 0),
+    ("bf16", 256, 128, 8, 7, 40, moe.MOE_FLAG_PATH_STREAM),
 ]
 
 
@@ -378,6 +382,7 @@ CAP_CASES = [
     ("bf16", 512, 384, 4, 2, 700, 200, moe.MOE_FLAG_PATH_STREAM),    # dispatch kernels, stream
     ("bf16", 1024, 256, 8, 2, 4, 1, 0),                              # one-workgroup route, T = 4
     ("f32", 64, 128, 8, 2, 32, 4, 0),
+    ("bf16", 256, 128, 16, 5, 150, 30, 0),                           # dropped pairs, k = 5
 ]
 
 
