@@ -250,7 +250,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_off, int E, int H,
     int F, int T, int ksplit, size_t plane, void* __restrict__ out, float* __restrict__ ws) {
   // weight buffers 0-2, token buffers 3-4 (the down projection's output is
-  // staged in the first 64 KB after the K loop)
+  // staged in weight buffers 1-2 after the K loop)
   __shared__ u32x4 lds[5 * kBuf];
 
   // ksplit > 1 (down projection only): the K range is cut into ksplit
@@ -385,6 +385,32 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
       for (int i = 0; i < 8; ++i) dma(2, 0, i, 2);
     }
   };
+  // The down projection's prologue in two parts around its epilogue, which
+  // stages the output in weight buffers 1-2: the token rows of steps 0 and 1
+  // and the weights of step 0 before it, the weights of steps 1 and 2 after
+  // it (the same issue order of the step-1 and step-2 weights as above, so
+  // the K loop's counted waits still hold).
+  auto prologue_a = [&](int nk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      if (s < nk) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dma(s, 1, i, 3 + s);
+      }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dma(0, 0, i, 0);
+  };
+  auto prologue_b = [&](int nk) __attribute__((always_inline)) -> int {
+    if (nk > 1) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dma(1, 0, i, 1);
+    }
+    if (nk > 2) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dma(2, 0, i, 2);
+    }
+    return (nk > 1 ? 8 : 0) + (nk > 2 ? 8 : 0);  // loads issued
+  };
 
   // The K loop of one tile for a wave that computes its first NJ token
   // blocks (the others lie beyond the tile's rows).  Loads never depend on
@@ -494,6 +520,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
   };
 
   int round = 0;
+  int st_groups = 0;  // gate/up: token-block groups the wave stored after the current tile's first loads
+  int tail_loads = 0;  // down: the current tile's first loads issued after the previous epilogue
   Tile cur, nxt;
   if (!locate(round, cur)) return;
   {
@@ -519,13 +547,14 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
     if (more) load_perm(nxt, pn);
     kloop(NJc, acc, cur.nk);
     // every load of the tile has landed; end every wave's reads of the ring,
-    // then (gate/up) start the next tile's first K steps under this tile's
-    // epilogue; the down projection stages its output in the weight buffers
-    // and starts them after it
+    // then start the next tile's first K steps under this tile's epilogue
+    // (the down projection stages its output in weight buffers 1-2 and
+    // loads their weights after it)
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (more) {
       set_tile(nxt, pn);
       if (GATED) prologue(nxt.nk);
+      else prologue_a(nxt.nk);
     }
     // read each accumulator where it is used: left to itself the compiler
     // copies all of them to VGPRs at once and spills
@@ -540,7 +569,12 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
       return v;
     };
     if (cur.np < 2) {
-      write_tile<GATED>(cur, [](int) {}, from_acc, out, F, H, plane, (uint8_t*)&lds[0], wave);
+      write_tile<GATED>(cur, [](int) {}, from_acc, out, F, H, plane, (uint8_t*)&lds[kBuf], wave);
+      if (GATED) {  // groups j with a row of this wave's token block 2 j + wn
+        st_groups = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) st_groups += (2 * j + wn) * 32 < cur.rows ? 1 : 0;
+      }
     } else {  // a piece: its partial sums, for the launch that finishes the tile
       f32x4* dst = part_base(ws, xcd * nw + jw, wave);
 #pragma unroll
@@ -553,15 +587,32 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
     if (!GATED && more) {
       // every wave is done with the output staging
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      prologue(nxt.nk);
+      tail_loads = prologue_b(nxt.nk);
     }
     return more;
   };
   for (;;) {
-    // this tile's first stages have landed (and the previous tile's output
-    // stores have completed, as vmcnt counts both); the barrier also ends
-    // every wave's reads of the previous tile's output staging
-    WAIT_VMCNT(0);
+    // this tile's first stages have landed; the barrier also ends every
+    // wave's reads of the previous tile's output staging.  Gate/up issued its
+    // previous output stores (8 per token-block group the wave wrote) after
+    // this tile's first loads, and vmcnt counts loads and stores in issue
+    // order: those stores may stay in flight here (the K loop's first wait
+    // takes them in); the down projection waits for everything.
+    if (GATED) {
+      switch (st_groups) {
+        case 1: WAIT_VMCNT(8); break;
+        case 2: WAIT_VMCNT(16); break;
+        case 3: WAIT_VMCNT(24); break;
+        case 4: WAIT_VMCNT(32); break;
+        default: WAIT_VMCNT(0); break;
+      }
+    } else {
+      // the down projection: its step-1 and step-2 weights, issued after
+      // the epilogue, may stay in flight
+      if (tail_loads == 16) WAIT_VMCNT(16);
+      else if (tail_loads == 8) WAIT_VMCNT(8);
+      else WAIT_VMCNT(0);
+    }
     GG_BARRIER();
     const int nb = (cur.rows + 31) >> 5;        // 32-row token blocks in the tile
     const int nj = max((nb - wn + 1) >> 1, 1);  // this wave's (at least one)
