@@ -44,8 +44,9 @@
 // along K into pieces run by the workgroups that would otherwise idle; the
 // pieces store fp32 partial sums and a second, short launch adds them in
 // piece order and writes those tiles (no cross-workgroup waiting, and the
-// same result on every call).  Gate/up tiles are shorter (K = H) and gain
-// nothing from it.
+// same result on every call).  Gate/up tiles are shorter (K = H) and gained
+// nothing from K pieces; their last round's tiles are cut into pieces of
+// token rows instead, which need no second pass.
 #include "common.h"
 #include "kernels.h"
 
@@ -110,9 +111,13 @@ struct Tile {
 // contiguous eighth of the numbering and its nw workgroups take those tiles
 // in turn, so tiles running together on an XCD share data in its L2, and
 // each XCD sees every expert, whatever the routing skew.  With split set,
-// the nleft tiles of a last, partial round are cut into np K pieces each
-// (np * nleft <= nw); each piece stores its fp32 partial sums and a second
-// launch adds the np partials in piece order and writes the tile.
+// the nleft tiles of a last, partial round are cut into np pieces each
+// (np * nleft <= nw).  Down projection: K pieces; each stores its fp32
+// partial sums and a second launch adds the np partials in piece order and
+// writes the tile.  Gate/up: pieces of the tile's 32-row token blocks, each
+// a tile of its own (disjoint output rows, nothing to add): a piece of at
+// most two blocks per wave column keeps the MFMAs and the token loads of
+// the blocks it leaves out.
 struct Plan {
   int MW, ngpe, ntt, per_ks, nk_slice, q_beg, q_end, nfull, nleft, np;
 };
@@ -132,7 +137,8 @@ __device__ Plan make_plan(bool gated, const int32_t* tile_off, int E, int H, int
   p.nleft = p.q_end - p.q_beg - p.nfull * nw;
   p.np = 1;
   if (split && p.nleft > 0)
-    p.np = max(1, min(min(nw / p.nleft, kMaxPieces), p.nk_slice / kMinPiece));
+    p.np = gated ? min(nw / p.nleft, kMaxPieces)
+                 : max(1, min(min(nw / p.nleft, kMaxPieces), p.nk_slice / kMinPiece));
   return p;
 }
 
@@ -259,7 +265,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
   const int xcd = blockIdx.x & 7;
   const int nw = gridDim.x >> 3;   // workgroups per XCD
   const int jw = blockIdx.x >> 3;  // this workgroup's place on its XCD
-  const Plan pl = make_plan(GATED, tile_off, E, H, F, ksplit, xcd, nw, !GATED && ws != nullptr);
+  const Plan pl = make_plan(GATED, tile_off, E, H, F, ksplit, xcd, nw, GATED || ws != nullptr);
   // work item w of this workgroup (rounds 0, 1, ...)
   auto locate = [&](int w, Tile& t) __attribute__((always_inline)) -> bool {
     if (pl.np < 2 || w < pl.nfull) {
@@ -271,6 +277,14 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(
     if (w > pl.nfull || jw >= pl.nleft * pl.np) return false;
     const int l = jw % pl.nleft, piece = jw / pl.nleft;
     tile_at(pl, pl.q_beg + pl.nfull * nw + l, tile_off, offsets, E, t);
+    if (GATED) {  // token blocks [b0, b1) of the tile's nb
+      const int nb = (t.rows + 31) >> 5;
+      const int b0 = piece * nb / pl.np, b1 = (piece + 1) * nb / pl.np;
+      if (b1 <= b0) return false;
+      t.p0 += 32 * b0;
+      t.rows = min(t.rows - 32 * b0, 32 * (b1 - b0));
+      return true;
+    }
     t.l = l;
     t.piece = piece;
     t.np = pl.np;

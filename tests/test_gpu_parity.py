@@ -260,10 +260,24 @@ def grouped_down_plan(counts, H, F, E, S, cus):
     return ksplit, pieces
 
 
+def grouped_gate_up_pieces(counts, F, cus):
+    """Host replica of the grouped gate/up schedule's last round: per XCD
+    share, the number of token-row pieces each leftover tile is cut into."""
+    nw = max(cus // 8, 1)
+    ntiles = int(sum(-(-int(c) // 256) for c in counts)) * (F // 128)
+    pieces = []
+    for xcd in range(8):
+        q0, q1 = (xcd * ntiles) >> 3, ((xcd + 1) * ntiles) >> 3
+        nleft = (q1 - q0) % nw
+        pieces.append(min(nw // nleft, 4) if nleft else 1)
+    return pieces
+
+
 def test_grouped_down_tail_split_every_row():
     """A grouped layer whose down projection runs the tail split (tiles of the
-    last, partial round cut along K, finished by the fix-up launch): the plan
-    is replayed on the host to show the split happens, then every row is
+    last, partial round cut along K, finished by the fix-up launch) and whose
+    gate/up cuts its last round's tiles into token-row pieces: both plans are
+    replayed on the host to show the splits happen, then every row is
     compared with the oracle."""
     shape = gen.LayerShape("tail", H=256, F=2048, E=8, k=2, dtype="bf16")
     T = 600
@@ -272,8 +286,11 @@ def test_grouped_down_tail_split_every_row():
     r = c.route(x)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     ksplit, pieces = grouped_down_plan(r["counts"], shape.H, shape.F, shape.E, T * shape.k, cus)
-    _log(f"  CUs {cus}, K split {ksplit}, pieces per XCD share {pieces}")
+    gu_pieces = grouped_gate_up_pieces(r["counts"], shape.F, cus)
+    _log(f"  CUs {cus}, K split {ksplit}, pieces per XCD share {pieces}, "
+         f"gate/up token pieces {gu_pieces}")
     assert max(pieces) >= 2
+    assert max(gu_pieces) >= 2
     y = c.forward(x)
     st = check_rows(c, x, np.arange(T), y, r["idx"])
     _log("  ", st)
