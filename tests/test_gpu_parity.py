@@ -126,6 +126,10 @@ SMALL = [
     ("bf16", 256, 640, 16, 4, 300, moe.MOE_FLAG_PATH_GROUPED),
     ("bf16", 768, 256, 3, 1, 1100, 0),
     ("bf16", 256, 128, 64, 8, 97, 0),
+    # batches beyond 64 tokens with 33-64 experts: the router staged from its
+    # [H][E] layout in the partial-logit kernel (E = 45: element by element)
+    ("bf16", 768, 128, 45, 3, 200, 0),
+    ("bf16", 512, 256, 40, 2, 1500, 0),
     # the single-token route (T = 1, E = 8 or 16, H % 1024 == 0)
     ("bf16", 1024, 256, 16, 4, 1, 0),
     ("bf16", 4096, 128, 8, 2, 1, 0),
