@@ -176,8 +176,28 @@ def time_layer(layer, x, y, T, steps, warm, stream):
     wall = time.perf_counter() - t0
     stage_ms = [sum(evs[i][s].elapsed_time(evs[i][s + 1]) for i in range(steps)) / steps
                 for s in range(nst)]
-    dev_ms = sum(evs[i][0].elapsed_time(evs[i][nst]) for i in range(steps)) / steps
-    return wall, stage_ms, dev_ms
+    per_step = [evs[i][0].elapsed_time(evs[i][nst]) for i in range(steps)]
+    return wall, stage_ms, sum(per_step) / steps, per_step
+
+
+def percentiles(ms):
+    """p10 / p50 / p90 of per-step times (ms)."""
+    import numpy as np
+    return [round(float(np.percentile(np.asarray(ms), q)), 4) for q in (10, 50, 90)]
+
+
+def replay_times(g, K, stream, scale=1.0):
+    """Device times (ms, times `scale`) of K single replays of graph g, each
+    bracketed by HIP events on the launch stream (a pass of its own, after the
+    timed one)."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    evs[0].record(stream)
+    for i in range(K):
+        g.replay()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [evs[i].elapsed_time(evs[i + 1]) * scale for i in range(K)]
 
 
 def gate_up_roofline(shape, T, touched, t_gu_s):
@@ -217,7 +237,7 @@ def bench_workload(name, shape, T, K, W):
     layer = moe.MoELayer(shape.H, shape.F, shape.E, shape.k, T, moe.MOE_BF16, wr, ex,
                          shape.stride, bias)
     y = torch.empty((T, shape.H), dtype=torch.float32, device="cuda")
-    wall, stage_ms, dev_ms = time_layer(layer, x, y, T, K, W, st)
+    wall, stage_ms, dev_ms, per_step = time_layer(layer, x, y, T, K, W, st)
     r = layer.route(x, T)
     torch.cuda.synchronize()
     counts = r["counts"].cpu().numpy()
@@ -232,6 +252,7 @@ def bench_workload(name, shape, T, K, W):
            "top_k": shape.k, "router_bias": shape.bias,
            "tokens_per_s": round(T * K / wall, 1), "ms_per_step": round(wall / K * 1e3, 4),
            "step_device_ms": round(dev_ms, 4),
+           "step_device_ms_p10_p50_p90": percentiles(per_step),
            "stages_ms": {n: round(v, 4) for n, v in zip(moe.STAGE_NAMES, stage_ms)},
            "roofline": dict(gate_up_roofline(shape, T, touched,
                                              stage_ms[moe.MOE_STAGE_GATE_UP] * 1e-3),
@@ -305,12 +326,14 @@ def bench_decode(shape, x, y, K, W, u8=False, batches=DECODE_BATCHES):
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / (K * NCOPY)
         dev_s = e0.elapsed_time(e1) * 1e-3 / (K * NCOPY)
+        pct = percentiles(replay_times(g, K, st, 1.0 / NCOPY))
         bytes_step = touched * eb + shape.H * shape.E * 2 + Td * shape.H * (2 + 4)
         gu_bytes = touched * 2 * shape.H * shape.F * wbytes
         res[f"T{Td}"] = {
             "tokens_per_s": round(Td / wall, 1),
             "ms_per_step": round(wall * 1e3, 4),
             "device_ms": round(dev_s * 1e3, 4),
+            "device_ms_p10_p50_p90": pct,
             "experts_touched": touched,
             "hbm_frac_step": round(bytes_step / dev_s / 1e9 / PEAK_HBM_GBS, 4),
             "gate_up_GBs": round(gu_bytes / (st_d[moe.MOE_STAGE_GATE_UP] * 1e-3) / 1e9, 1),
@@ -385,9 +408,11 @@ def bench_stack(K, W, u8=False, batches=DECODE_BATCHES):
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / K
         dev_s = e0.elapsed_time(e1) / K * 1e-3
+        pct = percentiles(replay_times(g, K, st))
         byts = touched * eb
         res[f"T{T}"] = {"tokens_per_s": round(T / wall, 1), "ms_per_step": round(wall * 1e3, 4),
                         "device_ms": round(dev_s * 1e3, 4),
+                        "device_ms_p10_p50_p90": pct,
                         "experts_touched_per_layer": round(touched / NL, 3),
                         "hbm_frac": round(byts / dev_s / 1e9 / PEAK_HBM_GBS, 4)}
         del g
@@ -440,7 +465,7 @@ def main():
     K, W = args.steps, args.warmup
 
     print(f"[bench] prefill: {W} warmup + {K} timed steps", file=sys.stderr, flush=True)
-    wall, stage_ms, dev_ms = time_layer(layer, x, y, T, K, W, stream)
+    wall, stage_ms, dev_ms, per_step = time_layer(layer, x, y, T, K, W, stream)
     tok_s = T * K / wall
     S = T * shape.k
     step_flops = 6.0 * S * shape.H * shape.F + 2.0 * T * shape.H * shape.E
@@ -471,6 +496,7 @@ def main():
                          if args.workload == "mixtral_prefill" else None),
         "stages_ms": {n: round(v, 4) for n, v in zip(moe.STAGE_NAMES, stage_ms)},
         "step_device_ms": round(dev_ms, 4),
+        "step_device_ms_p10_p50_p90": percentiles(per_step),
         "step_tflops": round(step_flops / (dev_ms * 1e-3) / 1e12, 2),
         "step_mfma_frac": round(step_flops / (dev_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "routing": routing_stats(shape, x_h, wr_h, b_h, counts),
