@@ -42,6 +42,27 @@ __device__ __forceinline__ float silu_f32(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
 }
 
+// Completion count of a launch whose last workgroup to finish does the rest
+// of its work.  The workgroup barrier orders every wave's stores before it
+// (they are in this CU's L2); then one wave releases them at device scope
+// (one L2 write-back per workgroup, not one per wave) and counts.  The last
+// workgroup acquires every other's stores the same way (one wave's
+// invalidate, then the barrier) and resets the counter for the next launch.
+// True in every thread of the last workgroup.  *flag: a __shared__ int.
+__device__ __forceinline__ bool last_workgroup(int32_t* counter, int* flag) {
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    __threadfence();  // release, at device scope
+    if (threadIdx.x == 0) *flag = (atomicAdd(counter, 1) == (int)gridDim.x - 1);
+  }
+  __syncthreads();
+  if (!*flag) return false;
+  if (threadIdx.x < 64) __threadfence();  // acquire, at device scope
+  if (threadIdx.x == 0) *counter = 0;     // every workgroup has counted
+  __syncthreads();
+  return true;
+}
+
 // The chip has 8 XCDs, each with its own L2; consecutive workgroup ids are
 // dealt round-robin over them.  Renumber so that blocks sharing data (same
 // logical neighbourhood) land on the same XCD: physical id i -> logical id

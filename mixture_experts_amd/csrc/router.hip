@@ -867,12 +867,7 @@ __global__ __launch_bounds__(256) void route_small_kernel(
       }
     }
   }
-  __threadfence();  // release this block's partials
-  __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(counter, 1) == (int)gridDim.x - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();  // acquire every block's partials
+  if (!last_workgroup(counter, &s_last)) return;  // then every block's partials are seen
 
   const int ns = gridDim.x;
   const int ldl = E + 1;
@@ -888,7 +883,6 @@ __global__ __launch_bounds__(256) void route_small_kernel(
   // only with k <= MOE_MAX_TOPK)
   topk_rows(lg, ldl, 0, T, E, k, raw, idx_out, w_out, 4, idx_l);
   __syncthreads();
-  if (tid == 0) *counter = 0;  // ready for the next launch
   dispatch_small(idx_l, T * k, E, tile_rows, cap, cnt, off_l, rank_l, counts, offsets, tile_off,
                  active, perm, inv);
 }
@@ -1104,15 +1098,9 @@ __global__ __launch_bounds__(1024) void route_one_kernel(
     topk_rows16(lg, 17, 0, T, E, k, raw, idx_out + (size_t)tok0 * k, w_out + (size_t)tok0 * k,
                 16, nullptr, RT_TOK);
     __shared__ int s_last;
-    __threadfence();  // release this block's experts and weights
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(counter, 1) == (int)gridDim.x - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();  // acquire every block's
+    if (!last_workgroup(counter, &s_last)) return;  // then every block's experts are seen
     for (int i = tid; i < T_all * k; i += 1024) idx_l[i] = idx_out[i];
     __syncthreads();
-    if (tid == 0) *counter = 0;  // ready for the next launch
   } else {
     topk_rows16(lg, 17, 0, T, E, k, raw, idx_out, w_out, 16, idx_l, RT_TOK);
     __syncthreads();
