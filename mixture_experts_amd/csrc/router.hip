@@ -6,13 +6,14 @@
 // (equal logits: lower expert index first) and a softmax over those k
 // [www.lmnt.cn/news/246575 sec. 2.2, route_tokens].
 //
-// bf16 layers, batches beyond 64 tokens: the router is transposed once per
-// call; a first kernel computes partial logits of 64-token tiles over slices
-// of the hidden dimension (split so that the batch fills over a thousand
-// workgroups) with v_mfma_f32_16x16x32_bf16 (tokens as the A operand, the
-// transposed router as the B operand, read from L2 or, for many experts,
-// staged in LDS; fp32 accumulation; the next hidden step's operands loaded
-// during this one's MFMAs); a second kernel adds the slices in a fixed order
+// bf16 layers, batches beyond 64 tokens: a first kernel computes partial
+// logits of 64-token tiles over slices of the hidden dimension (split so
+// that the batch fills hundreds of workgroups) with v_mfma_f32_16x16x32_bf16
+// (tokens as the A operand, the router as the B operand, staged in LDS
+// chunk by chunk: up to 64 experts transposed on the way from its [H][E]
+// layout, beyond that from a copy transposed by a kernel of its own; fp32
+// accumulation; the next hidden step's operands loaded during this one's
+// MFMAs); a second kernel adds the slices in a fixed order
 // (+ bias) and selects with a DPP max-reduction over (value desc, index asc):
 // one token per 16-lane row, each lane holding up to 16 experts' sums in
 // registers (k beyond 8: one token per wave, ranks).  Batches of up to 64 tokens route and dispatch in one launch (the
@@ -414,15 +415,10 @@ __device__ __forceinline__ void dispatch_small(const int32_t* idx_lds, int S, in
   }
 }
 
-// Partial logits of a 64-token tile over one slice of the hidden dimension:
-// part[split][t][e] = sum over h in the slice of x[t][h] * Wr[h][e].  The
-// slice is walked in chunks (the whole slice when its router rows fit in
-// 32 KB); each chunk of the router is staged in LDS transposed ([e][h]) so
-// that the MFMA B operand is a 16-byte read, and all token loads of a chunk
-// are issued before the staging, so their latency overlaps it.
 // Wr [H][E] -> WrT [E][H] (64 x 64 tiles through LDS), so that the router
-// operand of the logits GEMM is K-contiguous like the tokens.  Rows move as
-// 16-byte runs of 8 values (E a multiple of 8; else element by element).
+// operand of the logits GEMM is K-contiguous like the tokens (routers of more
+// than 64 experts).  Rows move as 16-byte runs of 8 values (E a multiple of
+// 8; else element by element).
 __global__ __launch_bounds__(256) void router_transpose_kernel(const uint16_t* __restrict__ wr,
                                                                int H, int E,
                                                                uint16_t* __restrict__ wrt) {
@@ -456,87 +452,23 @@ __global__ __launch_bounds__(256) void router_transpose_kernel(const uint16_t* _
   }
 }
 
-// Partial logits of one hidden slice for 64 tokens: tokens as the A operand
-// and the transposed router as the B operand of v_mfma_f32_16x16x32_bf16,
-// both read straight from global memory (the router is L2-resident).
-template <int NT>
-__global__ __launch_bounds__(256) void router_partial_kernel(
-    const uint16_t* __restrict__ x, int T, int H, int E, const uint16_t* __restrict__ wrt,
-    int hslice, float* __restrict__ part) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tile0 = blockIdx.x * RT_TOK;
-  const int split = blockIdx.y;
-  const int hb = split * hslice;
-  f32x4 acc[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int my_tok = tile0 + wave * 16 + (lane & 15);
-  const bool tok_ok = my_tok < T;
-  const int kq = (lane >> 4) * 8;
-  const uint16_t* xrow = x + (size_t)(tok_ok ? my_tok : 0) * H + hb + kq;
-  const uint16_t* wrow[NT];  // this lane's expert row of WrT per column block
-#pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const int e = n * 16 + (lane & 15);
-    wrow[n] = wrt + (size_t)(e < E ? e : 0) * H + hb + kq;
-  }
-  // operands of 128 hidden units per step, the next step's loads issued
-  // before this step's MFMAs
-  u32x4 av[4], bv[4][NT];
-  auto load = [&](int h) __attribute__((always_inline)) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      if (h + s * 32 < hslice) {
-        av[s] = tok_ok ? ldg16(xrow + h + s * 32) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int n = 0; n < NT; ++n) bv[s][n] = ldg16(wrow[n] + h + s * 32);
-      }
-  };
-  load(0);
-  for (int h = 0; h < hslice; h += 4 * 32) {  // hslice is a multiple of RT_HC (64)
-    u32x4 ca[4], cb[4][NT];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      ca[s] = av[s];
-#pragma unroll
-      for (int n = 0; n < NT; ++n) cb[s][n] = bv[s][n];
-    }
-    if (h + 4 * 32 < hslice) load(h + 4 * 32);
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      if (h + s * 32 < hslice)
-#pragma unroll
-        for (int n = 0; n < NT; ++n)
-          acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ca[s]), as_bf16x8(cb[s][n]),
-                                                           acc[n], 0, 0, 0);
-  }
-  // C layout: lane holds column (expert) lane%16, rows 4*(lane/16) + j;
-  // experts beyond E (rows of WrT clamped to 0) are not stored
-  float* out = part + (size_t)split * T * E;
-#pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const int e = n * 16 + (lane & 15);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = tile0 + wave * 16 + (lane >> 4) * 4 + j;
-      if (e < E && t < T) out[(size_t)t * E + e] = acc[n][j];
-    }
-  }
-}
-
-// The same partial logits for many experts (E > 32): each 128-wide hidden
+// Partial logits of one hidden slice for 64 tokens: part[split][t][e] = sum
+// over h in the slice of x[t][h] * Wr[h][e], tokens as the A operand and the
+// router as the B operand of v_mfma_f32_16x16x32_bf16, the token operands
+// read straight from global memory a chunk ahead.  Each 128-wide hidden
 // chunk of the router is staged in LDS once per workgroup and shared by its
 // 4 waves (read straight from L2 every wave would fetch it four times), as
 // [e][h] rows so that the MFMA B operand is a 16-byte read, double-buffered
-// with the next chunk's loads in flight during the MFMAs.  DIRECT: the router
-// is read in its [H][E] layout and transposed on the way: a piece of the
-// staging is 8 experts of one hidden row (16 bytes; element by element when
-// E is not a multiple of 8), the 64 lanes of a wave taking 64 consecutive
-// hidden rows, so that its 2-byte LDS writes fall on consecutive addresses.
-// Else the router comes transposed ([E][H], router_transpose_kernel) and a
-// piece is 8 hidden units of one expert.  (Direct staging saves the
-// transpose launch: 64-expert route 16.5 -> 13.3 us; at 128 experts its
-// loads touch 64 lines per instruction and the route took 1 us longer.)
+// with the next chunk's loads in flight during the MFMAs.  DIRECT (E <= 64):
+// the router is read in its [H][E] layout and transposed on the way: a piece
+// of the staging is 8 experts of one hidden row (16 bytes; element by
+// element when E is not a multiple of 8), the 64 lanes of a wave taking 64
+// consecutive hidden rows, so that its 2-byte LDS writes fall on
+// consecutive addresses.  Else the router comes transposed ([E][H],
+// router_transpose_kernel) and a piece is 8 hidden units of one expert.
+// (Direct staging saves the transpose launch: Mixtral-shaped prefill route
+// 27 -> 19 us, 64-expert route 16.5 -> 13.3 us; at 128 experts its loads
+// touch 64 lines per instruction and the route took 1 us longer.)
 template <int NT, bool DIRECT>
 __global__ __launch_bounds__(256) void router_partial_lds_kernel(
     const uint16_t* __restrict__ x, int T, int H, int E, const uint16_t* __restrict__ wr,
@@ -1293,19 +1225,20 @@ int launch_router(const RouterArgs& a, hipStream_t st) {
   const int nt = (a.E + 15) / 16;
   auto* xx = (const uint16_t*)a.x;
   auto* ww = (const uint16_t*)a.wr;
-  if (nt > 2 && nt <= 4) {  // the router staged from its own layout (no transpose launch)
-    router_partial_lds_kernel<4, true><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, ww, hs, a.part);
+  if (nt <= 4) {  // the router staged from its own layout (no transpose launch)
+    if (nt <= 1)
+      router_partial_lds_kernel<1, true><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, ww, hs, a.part);
+    else if (nt <= 2)
+      router_partial_lds_kernel<2, true><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, ww, hs, a.part);
+    else
+      router_partial_lds_kernel<4, true><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, ww, hs, a.part);
     launch_topk(a.part, ns, a, a.bias, st);
     return hipGetLastError() == hipSuccess ? 0 : -1;
   }
   const dim3 gt((a.H + 63) / 64, (a.E + 63) / 64);
   router_transpose_kernel<<<gt, 256, 0, st>>>(ww, a.H, a.E, a.wrt);
   const uint16_t* wt = a.wrt;
-  if (nt <= 1)
-    router_partial_kernel<1><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, wt, hs, a.part);
-  else if (nt <= 2)
-    router_partial_kernel<2><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, wt, hs, a.part);
-  else if (nt <= 8)
+  if (nt <= 8)
     router_partial_lds_kernel<8, false><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, wt, hs, a.part);
   else
     router_partial_lds_kernel<16, false><<<g2, 256, 0, st>>>(xx, a.T, a.H, a.E, wt, hs, a.part);
