@@ -200,6 +200,37 @@ def replay_times(g, K, stream, scale=1.0):
     return [evs[i].elapsed_time(evs[i + 1]) * scale for i in range(K)]
 
 
+def graph_step(layer, x, y, T, K, W, stream):
+    """One forward captured in a HIP graph (after one eager call on the
+    capture stream) and replayed W times untimed, then K times between two
+    HIP events: mean device ms per replay, and p10/p50/p90 of single replays.
+    The replay has no host launch gaps between the layer's kernels."""
+    import torch
+
+    import mixture_experts_amd as moe
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        moe.moe_forward(layer.handle, x, T, y, side)
+    stream.wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.moe_forward(layer.handle, x, T, y, torch.cuda.current_stream())
+    for _ in range(W):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    mean = e0.elapsed_time(e1) / K
+    pct = percentiles(replay_times(g, K, stream))
+    del g
+    return mean, pct
+
+
 def gate_up_roofline(shape, T, touched, t_gu_s):
     """Roofline of the gate/up launch: algorithmic flops 4*T*k*H*F and bytes
     (touched experts' gate and up weights once, token rows in, activation
@@ -263,6 +294,12 @@ def bench_workload(name, shape, T, K, W):
            "layer_hbm_frac": round(byts / dev_s / 1e9 / PEAK_HBM_GBS, 4),
            "layer_mfma_frac": round(flops / dev_s / 1e12 / PEAK_BF16_TFLOPS, 4),
            "routing": routing_stats(shape, x_h, wr_h, b_h, counts)}
+    g_ms, g_pct = graph_step(layer, x, y, T, K, W, st)
+    g_s = g_ms * 1e-3
+    res["graph_replay"] = {"device_ms": round(g_ms, 4), "device_ms_p10_p50_p90": g_pct,
+                           "tokens_per_s": round(T / g_s, 1),
+                           "layer_hbm_frac": round(byts / g_s / 1e9 / PEAK_HBM_GBS, 4),
+                           "layer_mfma_frac": round(flops / g_s / 1e12 / PEAK_BF16_TFLOPS, 4)}
     layer.close()
     del ex
     torch.cuda.empty_cache()
@@ -501,6 +538,9 @@ def main():
         "step_mfma_frac": round(step_flops / (dev_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "routing": routing_stats(shape, x_h, wr_h, b_h, counts),
     }
+    g_ms, g_pct = graph_step(layer, x, y, T, K, W, stream)
+    out["graph_replay"] = {"device_ms": round(g_ms, 4), "device_ms_p10_p50_p90": g_pct,
+                           "tokens_per_s": round(T / (g_ms * 1e-3), 1)}
 
     if not args.no_workloads and args.workload == "mixtral_prefill":
         print("[bench] 64-expert and 128-expert layers", file=sys.stderr, flush=True)

@@ -3,8 +3,9 @@ eager result bit for bit, with eager work of the same layer (on other inputs)
 between the replays.  One case per launch sequence: the single-token route
 with the folded combine (plain, residual, uint8 experts, rows of 4 and 8 KB),
 the router and
-dispatch kernels with the grouped GEMMs, and the LDS-staged router with the
-streaming kernels."""
+dispatch kernels with the grouped GEMMs (one-workgroup dispatch, and the
+histogram / scan / scatter dispatch of 16384 pairs), and the LDS-staged router
+with the streaming kernels."""
 import numpy as np
 import pytest
 import torch
@@ -29,6 +30,7 @@ CASES = [
     (4096, 4096, 8, 2, 1, moe.MOE_FLAG_RESIDUAL_PRENORM, True),
     (1024, 512, 8, 2, 700, moe.MOE_FLAG_PATH_GROUPED, False),
     (2048, 256, 64, 2, 200, 0, False),
+    (2048, 1408, 128, 4, 4096, 0, False),
 ]
 
 
