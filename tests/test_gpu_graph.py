@@ -4,8 +4,9 @@ between the replays.  One case per launch sequence: the single-token route
 with the folded combine (plain, residual, uint8 experts, rows of 4 and 8 KB),
 the router and
 dispatch kernels with the grouped GEMMs (one-workgroup dispatch, and the
-histogram / scan / scatter dispatch of 16384 pairs), and the LDS-staged router
-with the streaming kernels."""
+histogram / scan / scatter dispatch of 16384 pairs), the LDS-staged router
+with the streaming kernels, and the route of several workgroups (17 to 64
+tokens) with the streaming kernels, bf16 and uint8."""
 import numpy as np
 import pytest
 import torch
@@ -31,6 +32,10 @@ CASES = [
     (1024, 512, 8, 2, 700, moe.MOE_FLAG_PATH_GROUPED, False),
     (2048, 256, 64, 2, 200, 0, False),
     (2048, 1408, 128, 4, 4096, 0, False),
+    # T = 17..64: the route of several workgroups whose last one dispatches
+    # and resets the completion counter (every replay must find it at zero)
+    (2048, 512, 8, 2, 48, 0, False),
+    (2048, 512, 8, 2, 64, 0, True),
 ]
 
 
