@@ -63,9 +63,9 @@ class Stack:
             L.close()
 
 
-def test_stack_graph_replay_matches_eager():
+@pytest.mark.parametrize("T", [12, 64])  # 64: separate branch normalisation, several-workgroup route
+def test_stack_graph_replay_matches_eager(T):
     shape = gen.LayerShape("gstack", H=512, F=256, E=8, k=2, dtype="bf16")
-    T = 12
     s = Stack(shape, 4, T)
     x0 = torch.from_numpy(gen.normal(0, 0, gen.T_X, T * shape.H, 1.0, "f32")).cuda().view(T, shape.H)
     h = torch.empty_like(x0)
