@@ -104,12 +104,18 @@ def test_u8_mixtral_decode(T, nsample):
     c.close()
 
 
-def test_u8_residual_stack_teacher_forced():
+# T = 1: the single-token route forms the normalisation itself and the
+# matrix-vector kernels run (H and F multiples of 1 KB of codes); T = 4: the
+# normalisation folded into a one-workgroup route; T = 24, 64: a separate
+# normalisation launch and the route of several workgroups
+@pytest.mark.parametrize("H,F,T", [(512, 512, 24), (1024, 1024, 1), (1024, 1024, 4),
+                                   (1024, 1024, 64)])
+def test_u8_residual_stack_teacher_forced(H, F, T):
     """Three stacked uint8 layers in place (RESIDUAL_PRENORM: the normalised
     bf16 branch input is what the uint8 kernels read in fp16), each checked
     against the oracle fed with the GPU's residual stream at that layer."""
-    shape = gen.LayerShape("u8stack", H=512, F=512, E=8, k=2, dtype="bf16")
-    T = 24
+    _log("u8 residual stack", H, F, T)
+    shape = gen.LayerShape("u8stack", H=H, F=F, E=8, k=2, dtype="bf16")
     cases = [U8Case(shape, T, moe.MOE_FLAG_RESIDUAL_PRENORM, layer=l) for l in range(3)]
     h = torch.from_numpy(gen.normal(0, 0, gen.T_X, T * shape.H, 1.0, "f32").reshape(T, shape.H)).cuda()
     for c in cases:
