@@ -229,6 +229,28 @@ def test_forward_config(name, shape, T, chunk):
     c.close()
 
 
+@pytest.mark.parametrize("H,F,E,k", [(512, 512, 8, 2), (256, 256, 128, 8)])
+def test_forward_at_max_tokens(H, F, E, k):
+    """T = 65536, the largest batch a layer takes: the grouped GEMMs over many
+    rounds of tiles and the histogram / scan / scatter dispatch of T*k pairs
+    (131072 and 524288); sampled rows (both ends and random ones) against the
+    oracle, the whole output bitwise reproducible."""
+    T = 65536
+    _log("max tokens", H, F, E, k, T)
+    shape = gen.LayerShape(f"max{H}_{F}_{E}_{k}", H=H, F=F, E=E, k=k, dtype="bf16")
+    c = Case(shape, T)
+    x = gen.gen_x(shape, T)
+    y = c.forward(x)
+    r = c.route(x)
+    idx = r["idx"].reshape(T, k)
+    rng = np.random.default_rng(7)
+    toks = np.unique(np.concatenate([[0, 1, T - 2, T - 1], rng.choice(T, 60, False)]))
+    st = check_rows(c, x, toks, y[toks], idx[toks])
+    _log("  ", st)
+    assert np.array_equal(y, c.forward(x))
+    c.close()
+
+
 @pytest.mark.parametrize("flags", [0, moe.MOE_FLAG_COMBINE_SEPARATE])
 @pytest.mark.parametrize("T", [4, 16, 64])
 def test_mixtral_decode_every_row(T, flags):
